@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of split-KV attention on one MI355X.
+
+A step is one pass of the whole path over one batch: da_micro_attention
+(MicroAttention partials for every request, query head and split) followed by
+da_merge (aggregation into the attention output), on inputs already resident
+in HBM.  The headline workload is the single 1M-token request (LLaMA-2-7B /
+LWM shape, 32 heads, D=128, bf16 K/V, 64-token pages, 32 splits); the
+batched GQA + block-sparse workload (8 x 512K, 32/8 heads) is reported beside
+it.  Prints ONE JSON line on stdout.
+
+Metric: effective KV-read GB/s = algorithmic bytes / step time, where the
+algorithmic bytes are 2 * D * sizeof(elem) per kept token per KV head (every
+kept K and V row read once).  roofline.achieved uses the same bytes over the
+average duration of the MicroAttention kernel alone, timed with HIP events on
+the stream the kernels run on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "split-KV decode attention: effective KV-read GB/s vs HBM peak; µs/step"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C4", help="headline workload (C2, C3, C4, C5)")
+    ap.add_argument("--secondary", default="C5", help="comma list reported beside it, or ''")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    return ap.parse_args()
+
+
+def time_workload(key, steps, warmup, dev):
+    import torch
+
+    from long_context_decode_microattention_amd import _lib
+    from long_context_decode_microattention_amd import workloads as wl
+
+    spec = wl.CONFIGS[key]
+    t0 = time.time()
+    b = wl.build(spec, 0, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] built {key} in {time.time() - t0:.1f}s: NP={b.k_pages.shape[0]}")
+    kv_bytes = b.kv_bytes()
+    S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
+    MA = torch.empty((S, Hq, B, D), dtype=torch.float32, device=dev)
+    m = torch.empty((S, Hq, B), dtype=torch.float32, device=dev)
+    e = torch.empty((S, Hq, B), dtype=torch.float32, device=dev)
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    args = (b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
+
+    # a plain copy of known size (1 GiB): the yardstick for the HBM byte counters
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del src, dst
+
+    for _ in range(warmup):
+        _lib.micro_attention(*args, scale=b.scale, out=(MA, m, e))
+        _lib.merge(MA, m, e, out=out)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[3 * i].record()
+        _lib.micro_attention(*args, scale=b.scale, out=(MA, m, e))
+        ev[3 * i + 1].record()
+        _lib.merge(MA, m, e, out=out)
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    micro_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)]
+    merge_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_step = total_ms / steps
+    avg_micro = sum(micro_ms) / steps
+    avg_merge = sum(merge_ms) / steps
+    assert torch.isfinite(out).all(), "non-finite output"
+    res = dict(
+        workload=spec.name, key=key, kv_bytes=kv_bytes, ms_per_step=ms_step,
+        us_per_step=ms_step * 1e3, us_micro=avg_micro * 1e3, us_merge=avg_merge * 1e3,
+        us_micro_min=min(micro_ms) * 1e3, merge_share=avg_merge / (avg_micro + avg_merge),
+        GBps=kv_bytes / (ms_step * 1e-3) / 1e9, micro_GBps=kv_bytes / (avg_micro * 1e-3) / 1e9,
+        shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B, kv_dtype=spec.dtype,
+                   max_len=spec.max_len, block_mask=spec.mask is not None),
+    )
+    res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
+    return b, res
+
+
+def read_ceiling(b):
+    """Streaming-read rate over the workload's own K and V pools."""
+    import torch
+
+    from long_context_decode_microattention_amd import _lib
+
+    sink = None
+    bufs = (b.k_pages, b.v_pages)
+    for buf in bufs:  # warm
+        sink = _lib.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    s.record()
+    for _ in range(reps):
+        for buf in bufs:
+            _lib.stream_read(buf, sink)
+    t.record()
+    torch.cuda.synchronize()
+    nbytes = sum(x.numel() * x.element_size() for x in bufs) * reps
+    return nbytes / (s.elapsed_time(t) * 1e-3) / 1e9
+
+
+def cpu_baseline(b, budget_s):
+    """The fp64 oracle on a bounded sample of the same workload, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from long_context_decode_microattention_amd import workloads as wl
+
+    sp = b.spec
+    G = sp.G
+    lens = b.seq_lens.cpu().numpy()
+    kept = b.kept_tokens()
+    units = [(s, kvh) for s in range(sp.S) for kvh in range(sp.Hkv)]
+    done_bytes, secs, n = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for s, kvh in units:
+            L = int(lens[s])
+            npg = -(-L // sp.P)
+            pages = b.block_table[s, :npg].long()
+            h = wl.host
+            k = h(b.k_pages[:, kvh:kvh + 1].index_select(0, pages).contiguous())
+            v = h(b.v_pages[:, kvh:kvh + 1].index_select(0, pages).contiguous())
+            q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
+            mask = None
+            if b.block_mask is not None:
+                mask = h(b.block_mask[s:s + 1, kvh:kvh + 1, :npg].contiguous())
+            table = np.arange(npg, dtype=np.int32)[None, :]
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, table, np.array([L], dtype=np.int32), block_mask=mask, scale=b.scale)
+            secs += time.perf_counter() - t0
+            done_bytes += int(kept[s, kvh]) * 2 * sp.D * sp.esize
+            n += 1
+            if secs >= budget_s:
+                break
+    return dict(value=done_bytes / secs / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{sp.name}: {n} (request, KV head) unit(s), {done_bytes / 2**30:.2f} GiB of "
+                       f"K+V, fp64 numpy oracle.attention, BLAS limited to 1 thread, {secs:.1f} s")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the path is single-GPU; multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    from long_context_decode_microattention_amd import _lib
+
+    _lib.load()
+
+    b, head = time_workload(a.workload, a.steps, a.warmup, dev)
+    ceiling = None if a.no_ceiling else read_ceiling(b)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(b, a.cpu_budget)
+    del b
+    torch.cuda.empty_cache()
+    secondary = {}
+    for key in [k for k in a.secondary.split(",") if k and k != a.workload]:
+        b2, r2 = time_workload(key, a.steps, a.warmup, dev)
+        r2["roofline_frac"] = r2["micro_GBps"] / HBM_PEAK_GBPS
+        secondary[key] = r2
+        del b2
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], **head["shape"], "seed": 0,
+                   "kv_bytes_per_step": head["kv_bytes"]},
+        "us_per_step": round(head["us_per_step"], 2),
+        "frac_of_hbm_peak": round(head["frac_of_peak"], 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["micro_GBps"], 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(head["micro_GBps"] / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "micro_kernel (da_micro_attention)",
+            "us_per_launch": round(head["us_micro"], 2),
+        },
+        "us_merge": round(head["us_merge"], 2),
+        "merge_share_of_step": round(head["merge_share"], 5),
+        "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "frac_of_read_ceiling": None if ceiling is None else round(head["GBps"] / ceiling, 4),
+        "cpu_baseline": cpu,
+        "secondary": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                      for k, r in secondary.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * da.h -- C ABI of the split-KV decode attention library (libda.so, gfx950).
+ *
+ * The library computes decode-phase attention of one query token per
+ * (request, query head) over a paged KV cache in two steps:
+ *
+ *   da_micro_attention  MicroAttention per (request, query head, split):
+ *                         m_j  = max_i s_i
+ *                         e_j  = sum_i exp(s_i - m_j)
+ *                         MA_j = sum_i exp(s_i - m_j) * v_i
+ *                       with s_i = scale * (q . k_i).
+ *                       (Infinite-LLM page, section 方法细节, the MicroAttention
+ *                       equations of the equivalent transform.)
+ *   da_merge            aggregation of the b partials of each (request, head):
+ *                         m_g = max_j m_j
+ *                         e_g = sum_j e_j * exp(m_j - m_g)
+ *                         out = sum_j MA_j * exp(m_j - m_g) / e_g
+ *                       (Infinite-LLM page, section 方法细节, the aggregation
+ *                       equations.)
+ *
+ * Whole KV pages can be skipped with a block mask (LServe blog page, section
+ * 2.1.1: only the selected blocks are loaded and computed).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is DEVICE memory owned by the caller.  The library
+ *   keeps no pointer after a call returns and allocates nothing.
+ * - Calls only enqueue work on `stream` (0 = the null stream) and return; the
+ *   caller synchronises.  Calls are re-entrant and may run concurrently on
+ *   different streams when their output buffers do not overlap.
+ * - A call that returns anything but DA_OK has enqueued nothing (argument
+ *   errors are found on the host before any launch), except DA_ERR_HIP, which
+ *   reports a failed launch.  da_last_error() then describes the failure.
+ * - Array CONTENTS are trusted: block-table entries must index pages of the
+ *   pool and values must be finite on every token that a split reads.  Slots
+ *   that no split reads (tail of a partial last page, masked pages, pages the
+ *   table does not name) are never loaded and may hold anything.
+ *   da_check_inputs() validates the contents on the device.
+ */
+#ifndef DA_H
+#define DA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum da_status {
+  DA_OK = 0,
+  DA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape     */
+  DA_ERR_UNSUPPORTED = 2, /* valid but not built: D, P, dtype or group size  */
+  DA_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed      */
+} da_status;
+
+typedef enum da_dtype {
+  DA_F32 = 0,  /* IEEE binary32                                     */
+  DA_BF16 = 1  /* bfloat16: the upper 16 bits of an IEEE binary32  */
+} da_dtype;
+
+/* Problem shape.  Notation: S requests, Hq query heads, Hkv KV heads
+ * (G = Hq / Hkv query heads share one KV head: query head h reads KV head
+ * h / G), D head dimension, P tokens per page, NP pages in the pool. */
+typedef struct da_shape {
+  int32_t S;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t D;               /* 64 or 128                                        */
+  int32_t P;               /* 16, 32, 64, 128 or 256                           */
+  int32_t max_pages;       /* row length of block_table and block_mask         */
+  int32_t max_splits;      /* b: splits per (request[, KV head]), >= 1          */
+  int32_t bounds_per_head; /* 0: split_bounds is [S, 1, b+1]; 1: [S, Hkv, b+1]  */
+  int32_t dtype;           /* da_dtype of q, k_pages and v_pages               */
+  float scale;             /* score scale, > 0 and finite (usually 1/sqrt(D))  */
+  int64_t NP;              /* pages in k_pages / v_pages, >= 1                 */
+} da_shape;
+
+/*
+ * MicroAttention partials for every (request s, query head h, split j).
+ *
+ * Inputs (device, caller-owned):
+ *   q            [S, Hq, D] of sh->dtype, 16-byte aligned.
+ *   k_pages      [NP, Hkv, P, D] of sh->dtype, 16-byte aligned: the key of
+ *                logical token t of request s for KV head g is
+ *                k_pages[block_table[s, t / P], g, t % P, :].
+ *   v_pages      same layout as k_pages, for values.
+ *   block_table  [S, max_pages] int32: logical page -> physical page.  Only
+ *                entries of pages that hold tokens of some split are read.
+ *   seq_lens     [S] int32: context length L_s, 0 <= L_s <= max_pages * P.
+ *   split_bounds [S, 1, b+1] or [S, Hkv, b+1] int32 token offsets.  Split j
+ *                of request s (and KV head g when bounds are per head) is the
+ *                token range [sb_j, sb_{j+1}) intersected with [0, L_s).  The
+ *                usual choice is 0 = sb_0 <= ... <= sb_b = L_s, padded by
+ *                repeating L_s, but any values are accepted: an inverted or
+ *                out-of-range split is empty.  Ranges from different calls may
+ *                cover different parts of a request; their partials merge.
+ *   block_mask   NULL, or [S, Hkv, max_pages] uint8: page lp of request s is
+ *                skipped for KV head g (and its G query heads) when
+ *                block_mask[s, g, lp] == 0.
+ * Outputs (device, caller-owned, fully written):
+ *   MA           [S, Hq, b, D] float32, 16-byte aligned.
+ *   m, e         [S, Hq, b] float32.  m is in the natural-log domain of the
+ *                scaled score.  An empty split (no kept token) is written as
+ *                MA = 0, m = -inf, e = 0.
+ * Errors: DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED (D, P, dtype or G = Hq/Hkv
+ * outside the built set {1, 2, 4, 8}), DA_ERR_HIP.
+ */
+da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* split_bounds,
+                             const uint8_t* block_mask, float* MA, float* m, float* e,
+                             hipStream_t stream);
+
+/*
+ * Aggregate b partials per (request, query head) into attention output.
+ *
+ *   MA [S, Hq, b, D], m [S, Hq, b], e [S, Hq, b] float32 as written by
+ *   da_micro_attention (or gathered from several calls: the merge accepts any
+ *   partials that follow the same convention, in any order).
+ *   out [S, Hq, D] float32.  A (request, head) whose partials are all empty
+ *   gets out = 0.
+ * Only sh->S, sh->Hq, sh->D and sh->max_splits (= b) are read.
+ * Errors: DA_ERR_INVALID_ARG, DA_ERR_HIP.
+ */
+da_status da_merge(const da_shape* sh, const float* MA, const float* m, const float* e,
+                   float* out, hipStream_t stream);
+
+/*
+ * Device-side validation of the array contents that da_micro_attention
+ * trusts: 0 <= seq_lens[s] <= max_pages * P for every request, and
+ * 0 <= block_table[s, lp] < NP for every logical page lp < ceil(L_s / P)
+ * (stricter than needed: it also covers pages that no split reads or the
+ * mask skips).  Adds the number of violations found to err[0] (device int32,
+ * caller-owned; set it to 0 first).  Reads sh->S, P, max_pages and NP only.
+ */
+da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t* err, hipStream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local; never NULL; empty if none). */
+const char* da_last_error(void);
+
+/*
+ * Measurement helper, not part of the attention path: reads `bytes` bytes of
+ * device memory at `src` (16-byte aligned, bytes a multiple of 16) with
+ * coalesced 16-byte loads and writes one 32-bit word per workgroup into
+ * `sink` (device, >= da_stream_read_sink_words() words) so the reads cannot be
+ * elided.  Gives the achievable HBM read rate on this device.
+ */
+da_status da_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+size_t da_stream_read_sink_words(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DA_H */

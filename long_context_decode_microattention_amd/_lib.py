@@ -1,0 +1,209 @@
+"""ctypes binding of libda.so (C ABI in include/da.h).
+
+Argument marshalling only: shapes are read off the tensors, outputs are
+allocated with torch (device memory is plumbing here), and every step of the
+computation runs in the library's HIP kernels on the current torch stream.
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libda.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "da.h")
+
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
+DA_F32, DA_BF16 = 0, 1
+STATUS_NAMES = {0: "DA_OK", 1: "DA_ERR_INVALID_ARG", 2: "DA_ERR_UNSUPPORTED", 3: "DA_ERR_HIP"}
+
+
+class DaShape(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("P", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("bounds_per_head", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("NP", ctypes.c_int64),
+    ]
+
+
+class DaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+
+
+def load() -> ctypes.CDLL:
+    """Load libda.so (once) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    sp = ctypes.POINTER(DaShape)
+    lib.da_micro_attention.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.da_micro_attention.restype = ctypes.c_int
+    lib.da_merge.argtypes = [sp, _VP, _VP, _VP, _VP, _VP]
+    lib.da_merge.restype = ctypes.c_int
+    lib.da_check_inputs.argtypes = [sp, _VP, _VP, _VP, _VP]
+    lib.da_check_inputs.restype = ctypes.c_int
+    lib.da_last_error.argtypes = []
+    lib.da_last_error.restype = ctypes.c_char_p
+    lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
+    lib.da_stream_read.restype = ctypes.c_int
+    lib.da_stream_read_sink_words.argtypes = []
+    lib.da_stream_read_sink_words.restype = ctypes.c_size_t
+    _LIB = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions that include/da.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(da_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != DA_OK:
+        raise DaError(status, load().da_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, has shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None) -> DaShape:
+    S, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_pages.shape
+    if D2 != D:
+        raise ValueError(f"head dim of q ({D}) and k_pages ({D2}) differ")
+    nbh = split_bounds.shape[1]
+    if nbh not in (1, Hkv):
+        raise ValueError(f"split_bounds has {nbh} rows per request; expected 1 or Hkv={Hkv}")
+    if q.dtype == torch.float32:
+        dt = DA_F32
+    elif q.dtype == torch.bfloat16:
+        dt = DA_BF16
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=block_table.shape[1],
+                   max_splits=split_bounds.shape[2] - 1, bounds_per_head=int(nbh == Hkv and Hkv > 1),
+                   dtype=dt, scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), NP=NP)
+
+
+def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
+                    *, scale: Optional[float] = None, out=None):
+    """MicroAttention partials (MA [S,Hq,b,D], m [S,Hq,b], e [S,Hq,b]) via da_micro_attention."""
+    dev = q.device
+    _need(q, "q", None, dev, 3)
+    _need(k_pages, "k_pages", q.dtype, dev, 4)
+    _need(v_pages, "v_pages", q.dtype, dev, 4)
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages differ in shape")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+    sh = shape_of(q, k_pages, block_table, split_bounds, scale)
+    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
+        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
+    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
+        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
+    if out is None:
+        MA = torch.empty((sh.S, sh.Hq, sh.max_splits, sh.D), dtype=torch.float32, device=dev)
+        m = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
+        e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
+    else:
+        MA, m, e = out
+    _check(load().da_micro_attention(
+        ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+        _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m), _ptr(e), _stream(dev)))
+    return MA, m, e
+
+
+def merge(MA, m, e, *, out=None):
+    """Aggregate partials into out [S, Hq, D] float32 via da_merge."""
+    dev = MA.device
+    _need(MA, "MA", torch.float32, dev, 4)
+    _need(m, "m", torch.float32, dev, 3)
+    _need(e, "e", torch.float32, dev, 3)
+    S, Hq, B, D = MA.shape
+    if tuple(m.shape) != (S, Hq, B) or tuple(e.shape) != (S, Hq, B):
+        raise ValueError("m and e must be [S, Hq, b]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    sh = DaShape(S=S, Hq=Hq, Hkv=1, D=D, P=1, max_pages=1, max_splits=B, bounds_per_head=0,
+                 dtype=DA_F32, scale=1.0, NP=1)
+    _check(load().da_merge(ctypes.byref(sh), _ptr(MA), _ptr(m), _ptr(e), _ptr(out), _stream(dev)))
+    return out
+
+
+def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
+              *, scale: Optional[float] = None):
+    """One decode step: micro_attention then merge."""
+    MA, m, e = micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds,
+                               block_mask, scale=scale)
+    return merge(MA, m, e)
+
+
+def check_inputs(block_table, seq_lens, NP: int, P: int) -> int:
+    """Number of invalid seq_lens / block-table entries (synchronises)."""
+    dev = block_table.device
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    sh = DaShape(S=block_table.shape[0], Hq=1, Hkv=1, D=1, P=P, max_pages=block_table.shape[1],
+                 max_splits=1, bounds_per_head=0, dtype=DA_F32, scale=1.0, NP=NP)
+    _check(load().da_check_inputs(ctypes.byref(sh), _ptr(block_table), _ptr(seq_lens), _ptr(err),
+                                  _stream(dev)))
+    return int(err.item())
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of ``buf`` once (HBM read-rate measurement)."""
+    if sink is None:
+        sink = torch.zeros(int(load().da_stream_read_sink_words()), dtype=torch.int32, device=buf.device)
+    _check(load().da_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(buf.device)))
+    return sink

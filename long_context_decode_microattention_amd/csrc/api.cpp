@@ -1,0 +1,152 @@
+// Public C ABI of libda.so (include/da.h): argument validation on the host,
+// status codes with a thread-local message, and dispatch to the kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <climits>
+#include <string>
+
+#include "da.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+da_status fail(da_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Shape checks shared by the entry points that read the paged cache.
+da_status check_shape(const da_shape* sh) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 ||
+      sh->max_splits < 1 || sh->NP < 1)
+    return fail(DA_ERR_INVALID_ARG,
+                "sizes must be >= 1 (S=%d Hq=%d Hkv=%d D=%d P=%d max_pages=%d max_splits=%d NP=%lld)",
+                sh->S, sh->Hq, sh->Hkv, sh->D, sh->P, sh->max_pages, sh->max_splits,
+                (long long)sh->NP);
+  if (sh->Hq % sh->Hkv != 0)
+    return fail(DA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", sh->Hq, sh->Hkv);
+  if (sh->bounds_per_head != 0 && sh->bounds_per_head != 1)
+    return fail(DA_ERR_INVALID_ARG, "bounds_per_head must be 0 or 1 (got %d)", sh->bounds_per_head);
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
+    return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if (!(sh->scale > 0.f) || !isfinite(sh->scale))
+    return fail(DA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->S * sh->Hkv * sh->max_splits > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits exceeds the launch range");
+  if (sh->NP > (long long)INT_MAX + 1)
+    return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* split_bounds,
+                             const uint8_t* block_mask, float* MA, float* m, float* e,
+                             hipStream_t stream) {
+  da_status st = check_shape(sh);
+  if (st != DA_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds || !MA || !m || !e)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(MA, 16))
+    return fail(DA_ERR_INVALID_ARG, "q, k_pages, v_pages and MA must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(split_bounds, 4) ||
+      !aligned(m, 4) || !aligned(e, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
+  if (sh->D != 64 && sh->D != 128)
+    return fail(DA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", sh->D);
+  if (sh->P != 16 && sh->P != 32 && sh->P != 64 && sh->P != 128 && sh->P != 256)
+    return fail(DA_ERR_UNSUPPORTED, "page size %d not built (16, 32, 64, 128, 256)", sh->P);
+  const int G = sh->Hq / sh->Hkv;
+  if (!da::micro_supported(sh->dtype, sh->D, G))
+    return fail(DA_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", G);
+
+  da::MicroParams p{};
+  p.q = q;
+  p.k = k_pages;
+  p.v = v_pages;
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.bounds = split_bounds;
+  p.mask = block_mask;
+  p.MA = MA;
+  p.m = m;
+  p.e = e;
+  p.S = sh->S;
+  p.Hq = sh->Hq;
+  p.Hkv = sh->Hkv;
+  p.P = sh->P;
+  p.max_pages = sh->max_pages;
+  p.max_splits = sh->max_splits;
+  p.bounds_per_head = sh->bounds_per_head;
+  p.scale = sh->scale;
+  const hipError_t err = da::launch_micro(sh->dtype, sh->D, G, p, stream);
+  if (err != hipSuccess)
+    return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_merge(const da_shape* sh, const float* MA, const float* m, const float* e,
+                   float* out, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hq < 1 || sh->D < 1 || sh->max_splits < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hq=%d D=%d max_splits=%d)", sh->S,
+                sh->Hq, sh->D, sh->max_splits);
+  if ((long long)sh->S * sh->Hq > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hq exceeds the launch range");
+  if (!MA || !m || !e || !out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(MA, 4) || !aligned(m, 4) || !aligned(e, 4) || !aligned(out, 4))
+    return fail(DA_ERR_INVALID_ARG, "float arrays must be 4-byte aligned");
+  const hipError_t err =
+      da::launch_merge(MA, m, e, out, sh->S, sh->Hq, sh->D, sh->max_splits, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t* err, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!block_table || !seq_lens || !err) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(err, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  if ((long long)sh->S * sh->max_pages > (long long)UINT_MAX * 256)
+    return fail(DA_ERR_INVALID_ARG, "table too large");
+  const hipError_t e2 = da::launch_check_inputs(block_table, seq_lens, sh->S, sh->P, sh->max_pages,
+                                                sh->NP, err, stream);
+  if (e2 != hipSuccess) return fail(DA_ERR_HIP, "check launch failed: %s", hipGetErrorString(e2));
+  return DA_OK;
+}
+
+const char* da_last_error(void) { return g_last_error.c_str(); }
+
+da_status da_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(src, 16) || bytes % 16 != 0 || bytes == 0)
+    return fail(DA_ERR_INVALID_ARG, "src must be 16-byte aligned and bytes a positive multiple of 16");
+  const hipError_t err = da::launch_stream_read(src, bytes, sink, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "stream-read launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+size_t da_stream_read_sink_words(void) { return (size_t)da::stream_read_grid(); }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Device helpers shared by the gfx950 kernels: wave64 cross-lane reductions
+// and bf16 handling.  Internal to libda.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// DPP control words (GCN/CDNA data-parallel primitives on 16-lane rows).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8-lane half row
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i inside each 16-lane row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 8, 16 or 32); every
+// lane of the group receives the group total.  After the two quad steps each
+// lane holds its quad's sum; the half-row mirror pairs every lane with a lane
+// of the other quad of its 8-lane half, the row mirror with a lane of the
+// other half of its 16-lane row; a 32-lane group finishes with an exchange
+// across rows.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N == 32) x += __shfl_xor(x, 16, kWave);
+  return x;
+}
+
+// bf16 pair packed in a 32-bit word -> the two float values (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// a.x*b.x + a.y*b.y + c for bf16 pairs, accumulated in fp32 (v_dot2 on gfx950).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace da

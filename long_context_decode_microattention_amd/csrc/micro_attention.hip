@@ -1,0 +1,369 @@
+// MicroAttention kernel for gfx950: per (request, KV head, split) work item,
+// the partial softmax statistics and unnormalised value sum of every query
+// head of the KV head's group over the split's kept tokens:
+//   m_j = max_i s_i,  e_j = sum_i exp(s_i - m_j),  MA_j = sum_i exp(s_i - m_j) v_i
+// (Infinite-LLM page, section 方法细节, MicroAttention equations), with
+// s_i = scale * (q . k_i).  Whole pages with a zero block-mask entry are
+// neither loaded nor computed (LServe blog page, section 2.1.1).
+//
+// Work decomposition.  One 256-lane workgroup (4 waves) per work item.  The
+// item's kept logical pages are compacted into an LDS list (wave ballots, no
+// per-token branches), then cut into 16-token slabs that the 4 waves take
+// round-robin.  A slab of one KV head is contiguous in the pool
+// ([page, head, slot, D] layout), so every wave-wide 16-byte load reads 1 KiB
+// of consecutive bytes.  Each lane holds 16 bytes of one token row: a row of
+// LPT = D*sizeof(elem)/16 consecutive lanes covers one token, so a wave load
+// covers 64/LPT tokens ("rows").  Dot products are reduced inside each row
+// with DPP; every row keeps its own online (m, e, MA) state -- the triple is
+// closed under the aggregation rule, so rows never exchange maxima in the
+// loop -- and rows and waves are combined once at the end of the item.
+//
+// Arithmetic: fp32 accumulation.  bf16 scores use v_dot2 (bf16 pairs, fp32
+// accumulate); bf16 values are widened exactly by bit shifts.  Exponentials
+// run in base 2 on raw dot products: exp(scale*(d - d_max)) =
+// exp2((d - d_max) * scale*log2(e)); the reported m_j is scale * d_max.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace da {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPageCap = 1024;  // kept pages staged in LDS per batch
+constexpr int kSlab = 16;       // tokens per slab
+
+template <int DT, int D>
+struct Layout {
+  static constexpr int ES = DT == 0 ? 4 : 2;  // bytes per element
+  static constexpr int TOKB = D * ES;          // bytes per token row
+  static constexpr int LPT = TOKB / 16;        // lanes per token row
+  static constexpr int TPI = kWave / LPT;      // token rows per wave load
+  static constexpr int EPL = 16 / ES;          // elements per lane
+  static constexpr int NI = kSlab / TPI;       // wave loads per slab per tensor
+  static_assert(TPI * TOKB == kWave * 16, "wave load covers whole rows");
+  static_assert(NI >= 1 && kSlab % TPI == 0, "slab covers whole wave loads");
+};
+
+template <int DT, int D>
+struct Frag {
+  uint4 k[Layout<DT, D>::NI];
+  uint4 v[Layout<DT, D>::NI];
+};
+
+template <bool B>
+using Bool = std::integral_constant<bool, B>;
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
+  using L = Layout<DT, D>;
+  __shared__ int s_phys[kPageCap];
+  __shared__ int s_lp[kPageCap];
+  __shared__ int s_cnt[kWaves];
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_e[kWaves][G];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int row = lane / L::LPT;
+  const int chunk = lane % L::LPT;
+
+  const int item = blockIdx.x;
+  const int j = item % p.max_splits;
+  const int sk = item / p.max_splits;
+  const int kvh = sk % p.Hkv;
+  const int s = sk / p.Hkv;
+  const int h0 = kvh * G;
+  const int P = p.P;
+
+  int Ls = p.lens[s];
+  Ls = max(0, min(Ls, p.max_pages * P));
+  const int32_t* sb =
+      p.bounds + ((size_t)s * (p.bounds_per_head ? p.Hkv : 1) + (p.bounds_per_head ? kvh : 0)) *
+                     (size_t)(p.max_splits + 1);
+  const int t0 = max(sb[j], 0);
+  const int t1 = min(sb[j + 1], Ls);
+  const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
+
+  // Query fragment of every head in the group: the lane's 16-byte column.
+  uint4 qv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const char* qp = static_cast<const char*>(p.q) +
+                     ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
+    qv[g] = *reinterpret_cast<const uint4*>(qp);
+  }
+
+  float m_[G], e_[G], acc[G][L::EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_[g] = neg_inf();
+    e_[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < L::EPL; ++k) acc[g][k] = 0.f;
+  }
+
+  if (t0 < t1) {
+    const int lp0 = t0 / P;
+    const int lp1 = (t1 + P - 1) / P;
+    const uint8_t* mrow = p.mask ? p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages : nullptr;
+    const int32_t* trow = p.table + (size_t)s * p.max_pages;
+    const int spp = P / kSlab;  // slabs per page
+    const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+    const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
+    const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+
+    for (int base = lp0; base < lp1; base += kPageCap) {
+      // ---- compact the kept pages of [base, base + kPageCap) into LDS ----
+      int nk = 0;
+      const int span = min(kPageCap, lp1 - base);
+      for (int r = 0; r < span; r += kThreads) {
+        const int lp = base + r + tid;
+        const bool keep = lp < lp1 && (mrow == nullptr || mrow[lp] != 0);
+        const uint64_t bal = __ballot(keep);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) s_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = nk;
+        for (int w = 0; w < wave; ++w) off += s_cnt[w];
+        if (keep) {
+          s_phys[off + pre] = trow[lp];
+          s_lp[off + pre] = lp;
+        }
+        nk += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+        __syncthreads();
+      }
+
+      // ---- stream the slabs: wave w takes slabs w, w+4, ... ----
+      const int nslab = nk * spp;
+
+      auto load = [&](int sl, Frag<DT, D>& f) {
+        const int kp = sl / spp;
+        const int sub = sl - kp * spp;
+        const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
+        const int tb = s_lp[kp] * P + sub * kSlab;
+        if (tb >= t0 && tb + kSlab <= t1) {
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            f.k[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
+            f.v[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            const int t = tb + i * L::TPI + row;
+            if (t >= t0 && t < t1) {
+              f.k[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
+              f.v[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+            } else {
+              f.k[i] = make_uint4(0, 0, 0, 0);
+              f.v[i] = make_uint4(0, 0, 0, 0);
+            }
+          }
+        }
+      };
+
+      // FULL: every token of the slab lies inside [t0, t1)
+      auto compute = [&](int sl, const Frag<DT, D>& f, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int kp = sl / spp;
+        const int sub = sl - kp * spp;
+        const int tb = s_lp[kp] * P + sub * kSlab;
+
+        // scores: dot[i][g] for this row's token of wave load i
+        float dot[L::NI][G];
+#pragma unroll
+        for (int i = 0; i < L::NI; ++i) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d;
+            if constexpr (DT == 1) {
+              d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
+              d = dot2_bf16(f.k[i].y, qv[g].y, d);
+              d = dot2_bf16(f.k[i].z, qv[g].z, d);
+              d = dot2_bf16(f.k[i].w, qv[g].w, d);
+            } else {
+              d = __builtin_bit_cast(float, f.k[i].x) * __builtin_bit_cast(float, qv[g].x);
+              d = fmaf(__builtin_bit_cast(float, f.k[i].y), __builtin_bit_cast(float, qv[g].y), d);
+              d = fmaf(__builtin_bit_cast(float, f.k[i].z), __builtin_bit_cast(float, qv[g].z), d);
+              d = fmaf(__builtin_bit_cast(float, f.k[i].w), __builtin_bit_cast(float, qv[g].w), d);
+            }
+            dot[i][g] = group_sum<L::LPT>(d);
+          }
+        }
+
+        bool valid[L::NI];
+#pragma unroll
+        for (int i = 0; i < L::NI; ++i) {
+          const int t = tb + i * L::TPI + row;
+          valid[i] = FULL || (t >= t0 && t < t1);
+        }
+
+        // online softmax update, once per slab
+        float pw[L::NI][G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float mx = m_[g];
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) mx = fmaxf(mx, valid[i] ? dot[i][g] : neg_inf());
+          const float ms = (FULL || mx != neg_inf()) ? mx : 0.f;
+          const float alpha = fast_exp2((m_[g] - ms) * c);
+          const float nmc = -ms * c;
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            const float w = valid[i] ? fast_exp2(fmaf(dot[i][g], c, nmc)) : 0.f;
+            pw[i][g] = w;
+            sum += w;
+          }
+          e_[g] = fmaf(e_[g], alpha, sum);
+          m_[g] = mx;
+#pragma unroll
+          for (int k = 0; k < L::EPL; ++k) acc[g][k] *= alpha;
+        }
+
+        // weighted value sum
+#pragma unroll
+        for (int i = 0; i < L::NI; ++i) {
+          float vf[L::EPL];
+          if constexpr (DT == 1) {
+            const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              vf[2 * k] = bf16_lo(w4[k]);
+              vf[2 * k + 1] = bf16_hi(w4[k]);
+            }
+          } else {
+            vf[0] = __builtin_bit_cast(float, f.v[i].x);
+            vf[1] = __builtin_bit_cast(float, f.v[i].y);
+            vf[2] = __builtin_bit_cast(float, f.v[i].z);
+            vf[3] = __builtin_bit_cast(float, f.v[i].w);
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pw[i][g], vf[k], acc[g][k]);
+          }
+        }
+      };
+
+      auto step = [&](int sl, const Frag<DT, D>& f) {
+        const int kp = sl / spp;
+        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+        if (tb >= t0 && tb + kSlab <= t1)
+          compute(sl, f, Bool<true>{});
+        else
+          compute(sl, f, Bool<false>{});
+      };
+
+      Frag<DT, D> fa, fb;
+      int sl = wave;
+      if (sl < nslab) load(sl, fa);
+      while (sl < nslab) {
+        int sn = sl + kWaves;
+        if (sn < nslab) load(sn, fb);
+        step(sl, fa);
+        sl = sn;
+        if (sl >= nslab) break;
+        sn = sl + kWaves;
+        if (sn < nslab) load(sn, fa);
+        step(sl, fb);
+        sl = sn;
+      }
+      __syncthreads();  // the page list is rewritten by the next batch
+    }
+  }
+
+  // ---- combine the rows of each wave (lanes l and l ^ (k * LPT)) ----
+#pragma unroll
+  for (int off = L::LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m_[g], off, kWave);
+      const float eo = __shfl_xor(e_[g], off, kWave);
+      const float M = fmaxf(m_[g], mo);
+      const float Ms = (M == neg_inf()) ? 0.f : M;
+      const float a = fast_exp2((m_[g] - Ms) * c);
+      const float b = fast_exp2((mo - Ms) * c);
+      e_[g] = e_[g] * a + eo * b;
+#pragma unroll
+      for (int k = 0; k < L::EPL; ++k) {
+        const float ao = __shfl_xor(acc[g][k], off, kWave);
+        acc[g][k] = acc[g][k] * a + ao * b;
+      }
+      m_[g] = M;
+    }
+  }
+
+  // ---- combine the waves through LDS and write the partials ----
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int k = 0; k < L::EPL; ++k) s_acc[wave][g][chunk * L::EPL + k] = acc[g][k];
+      if (chunk == 0) {
+        s_m[wave][g] = m_[g];
+        s_e[wave][g] = e_[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    const float Ms = (M == neg_inf()) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2((s_m[w][g] - Ms) * c);
+      num = fmaf(s_acc[w][g][d], f, num);
+      den = fmaf(s_e[w][g], f, den);
+    }
+    const size_t o = (size_t)(s * p.Hq + h0 + g) * p.max_splits + j;
+    p.MA[o * D + d] = num;
+    if (d == 0) {
+      p.m[o] = M * p.scale;
+      p.e[o] = den;
+    }
+  }
+}
+
+template <int DT, int D, int G>
+hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
+  const long long items = (long long)p.S * p.Hkv * p.max_splits;
+  hipLaunchKernelGGL((micro_kernel<DT, D, G>), dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_one<DT, D, 1>(p, stream);
+    case 2: return launch_one<DT, D, 2>(p, stream);
+    case 4: return launch_one<DT, D, 4>(p, stream);
+    case 8: return launch_one<DT, D, 8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool micro_supported(int dtype, int D, int G) {
+  return (dtype == 0 || dtype == 1) && (D == 64 || D == 128) &&
+         (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream_t stream) {
+  if (!micro_supported(dtype, D, G)) return hipErrorInvalidValue;
+  if (dtype == 0) return D == 64 ? dispatch_g<0, 64>(G, p, stream) : dispatch_g<0, 128>(G, p, stream);
+  return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
+}
+
+}  // namespace da

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/da.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is launched."""
+
+import ctypes
+import os
+
+import pytest
+
+from long_context_decode_microattention_amd import _lib
+from long_context_decode_microattention_amd import build as da_build
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        da_build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert {"da_micro_attention", "da_merge", "da_last_error", "da_check_inputs"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libda.so does not export {n}"
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def good_shape(**kw):
+    base = dict(S=2, Hq=8, Hkv=2, D=128, P=16, max_pages=4, max_splits=2, bounds_per_head=0,
+                dtype=_lib.DA_BF16, scale=0.088, NP=8)
+    base.update(kw)
+    return _lib.DaShape(**base)
+
+
+def call_micro(lib, sh, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, bounds=FAKE, mask=None,
+                MA=FAKE, m=FAKE, e=FAKE)
+    args.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.da_micro_attention(None if sh is None else ctypes.byref(sh),
+                                  *(vp(args[k]) for k in ("q", "k", "v", "table", "lens", "bounds",
+                                                          "mask", "MA", "m", "e")), None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(sh=None), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(S=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(Hq=6, Hkv=4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(max_splits=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(scale=0.0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(scale=float("inf"))), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(dtype=7)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(bounds_per_head=2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(max_pages=1 << 28, P=16)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(q=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(e=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(k=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(MA=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(lens=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(P=24)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(Hq=32, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
+], ids=lambda x: str(x))
+def test_micro_rejects(lib, case, status):
+    sh = None if "sh" in case else good_shape(**case.get("shape", {}))
+    got = call_micro(lib, sh, **case.get("ptrs", {}))
+    assert got == status, (got, lib.da_last_error())
+    assert len(lib.da_last_error()) > 0
+
+
+def test_merge_rejects(lib):
+    sh = good_shape()
+    vp = ctypes.c_void_p
+    assert lib.da_merge(None, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_merge(ctypes.byref(sh), None, vp(FAKE), vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    bad = good_shape(max_splits=0)
+    assert lib.da_merge(ctypes.byref(bad), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_merge(ctypes.byref(sh), vp(FAKE + 2), vp(FAKE), vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+
+
+def test_check_inputs_and_stream_read_reject(lib):
+    vp = ctypes.c_void_p
+    sh = good_shape()
+    assert lib.da_check_inputs(ctypes.byref(sh), None, vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_stream_read(None, 16, vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_stream_read(vp(FAKE), 15, vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_stream_read_sink_words() >= 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 64)
+    with pytest.raises((ValueError, TypeError, RuntimeError)):
+        _lib.micro_attention(q, torch.zeros(2, 4, 16, 64), torch.zeros(2, 4, 16, 64),
+                             torch.zeros(1, 2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                             torch.zeros(1, 1, 2, dtype=torch.int64))
