@@ -54,4 +54,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint: data read once (the KV stream)
+// bypasses cache allocation, which sustains a markedly higher HBM read rate
+// on gfx950 than a plain load.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 }  // namespace da

@@ -1,35 +1,114 @@
-// Aggregation kernel: one wave per (request, query head) folds the b
+// Aggregation kernel: one workgroup per (request, query head) folds the b
 // MicroAttention partials into the attention output
 //   m_g = max_j m_j,  e_g = sum_j e_j exp(m_j - m_g),  out = sum_j MA_j exp(m_j - m_g) / e_g
 // (Infinite-LLM page, section 方法细节, aggregation equations).  Empty
 // partials (m_j = -inf) get weight exp(-inf) = 0; if all are empty, out = 0.
+//
+// The split weights exp(m_j - m_g) are computed once per chunk of 256 splits
+// into LDS; the 256 lanes then cover (split phase, dimension) pairs so that
+// the loads of MA_j for many splits are in flight together.
 #include "device_common.h"
 #include "launch.h"
 
 namespace da {
 namespace {
 
-__global__ __launch_bounds__(kWave) void merge_kernel(const float* __restrict__ MA,
-                                                      const float* __restrict__ m,
-                                                      const float* __restrict__ e,
-                                                      float* __restrict__ out, int D, int B) {
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / kWave;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ MA,
+                                                              const float* __restrict__ m,
+                                                              const float* __restrict__ e,
+                                                              float* __restrict__ out, int D,
+                                                              int B) {
+  __shared__ float s_w[kMergeThreads];
+  __shared__ float s_red[kMergeWaves];
+  __shared__ float s_acc[kMergeThreads];
   const size_t sh = blockIdx.x;  // s * Hq + h
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const float* mr = m + sh * B;
   const float* er = e + sh * B;
   const float* MAr = MA + sh * (size_t)B * D;
 
-  float M = neg_inf();
-  for (int j = 0; j < B; ++j) M = fmaxf(M, mr[j]);
+  // m_g
+  float lm = neg_inf();
+  for (int j = tid; j < B; j += kMergeThreads) lm = fmaxf(lm, mr[j]);
+  lm = wave_max(lm);
+  if (lane == 0) s_red[wave] = lm;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_red[w]);
   const float Ms = (M == neg_inf()) ? 0.f : M;
 
-  float eg = 0.f;
-  for (int j = 0; j < B; ++j) eg = fmaf(er[j], expf(mr[j] - Ms), eg);
+  // lanes cover (phase, d): phase p sums splits p, p + NPH, ... of each chunk
+  const int nph = D <= kMergeThreads ? kMergeThreads / D : 1;
+  const int p = D <= kMergeThreads ? tid / D : 0;
+  const int d = D <= kMergeThreads ? tid - p * D : tid;
+  float acc = 0.f, le = 0.f;
+  for (int jc = 0; jc < B; jc += kMergeThreads) {
+    __syncthreads();  // s_w of the previous chunk is consumed; s_red is read
+    const int jn = min(kMergeThreads, B - jc);
+    if (tid < jn) {
+      const float w = expf(mr[jc + tid] - Ms);
+      s_w[tid] = w;
+      le = fmaf(er[jc + tid], w, le);
+    }
+    __syncthreads();
+    if (d < D && p < nph) {
+      int jj = p;
+      for (; jj + 3 * nph < jn; jj += 4 * nph) {
+        const float a0 = MAr[(size_t)(jc + jj) * D + d];
+        const float a1 = MAr[(size_t)(jc + jj + nph) * D + d];
+        const float a2 = MAr[(size_t)(jc + jj + 2 * nph) * D + d];
+        const float a3 = MAr[(size_t)(jc + jj + 3 * nph) * D + d];
+        acc = fmaf(a0, s_w[jj], acc);
+        acc = fmaf(a1, s_w[jj + nph], acc);
+        acc = fmaf(a2, s_w[jj + 2 * nph], acc);
+        acc = fmaf(a3, s_w[jj + 3 * nph], acc);
+      }
+      for (; jj < jn; jj += nph) acc = fmaf(MAr[(size_t)(jc + jj) * D + d], s_w[jj], acc);
+    }
+  }
 
-  for (int d = lane; d < D; d += kWave) {
-    float acc = 0.f;
-    for (int j = 0; j < B; ++j) acc = fmaf(MAr[(size_t)j * D + d], expf(mr[j] - Ms), acc);
-    out[sh * D + d] = eg > 0.f ? acc / eg : 0.f;
+  // e_g
+  le = wave_sum(le);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = le;
+  s_acc[tid] = acc;
+  __syncthreads();
+  float eg = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) eg += s_red[w];
+
+  if (D <= kMergeThreads) {
+    if (tid < D) {
+      float total = 0.f;
+      for (int q = 0; q < nph; ++q) total += s_acc[q * D + tid];
+      out[sh * D + tid] = eg > 0.f ? total / eg : 0.f;
+    }
+  } else {
+    // D > 256: every lane owns a strided set of dimensions (not used by the
+    // micro-attention kernels, which produce D = 64 or 128)
+    for (int dd = tid; dd < D; dd += kMergeThreads) {
+      float t = 0.f;
+      for (int j = 0; j < B; ++j) t = fmaf(MAr[(size_t)j * D + dd], expf(mr[j] - Ms), t);
+      out[sh * D + dd] = eg > 0.f ? t / eg : 0.f;
+    }
   }
 }
 
@@ -38,7 +117,8 @@ __global__ __launch_bounds__(kWave) void merge_kernel(const float* __restrict__ 
 hipError_t launch_merge(const float* MA, const float* m, const float* e, float* out, int S, int Hq,
                         int D, int B, hipStream_t stream) {
   const long long n = (long long)S * Hq;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n), dim3(kWave), 0, stream, MA, m, e, out, D, B);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n), dim3(kMergeThreads), 0, stream, MA, m, e,
+                     out, D, B);
   return hipGetLastError();
 }
 

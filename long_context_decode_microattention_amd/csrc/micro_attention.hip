@@ -149,16 +149,16 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
         if (tb >= t0 && tb + kSlab <= t1) {
 #pragma unroll
           for (int i = 0; i < L::NI; ++i) {
-            f.k[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
-            f.v[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+            f.k[i] = load_stream16(kbase + off + i * 1024);
+            f.v[i] = load_stream16(vbase + off + i * 1024);
           }
         } else {
 #pragma unroll
           for (int i = 0; i < L::NI; ++i) {
             const int t = tb + i * L::TPI + row;
             if (t >= t0 && t < t1) {
-              f.k[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
-              f.v[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+              f.k[i] = load_stream16(kbase + off + i * 1024);
+              f.v[i] = load_stream16(vbase + off + i * 1024);
             } else {
               f.k[i] = make_uint4(0, 0, 0, 0);
               f.v[i] = make_uint4(0, 0, 0, 0);
