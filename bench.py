@@ -19,6 +19,7 @@ the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +35,26 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(key):
+    """HBM bytes per MicroAttention launch from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or
+    None when the kernel sources changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_decode_microattention_amd", "csrc")
+    for name in rec.get("files", []):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    w = rec.get("workloads", {}).get(key)
+    return None if w is None else int(w["traffic_bytes"])
 
 
 def parse():
@@ -192,6 +213,7 @@ def main():
     for key in [k for k in a.secondary.split(",") if k and k != a.workload]:
         b2, r2 = time_workload(key, a.steps, a.warmup, dev)
         r2["roofline_frac"] = r2["micro_GBps"] / HBM_PEAK_GBPS
+        r2["traffic"] = measured_traffic(key)
         secondary[key] = r2
         del b2
         torch.cuda.empty_cache()
@@ -219,7 +241,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(head["micro_GBps"] / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(a.workload),
             "kernel": "micro_kernel (da_micro_attention)",
             "us_per_launch": round(head["us_micro"], 2),
         },

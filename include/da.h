@@ -24,7 +24,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every array argument is DEVICE memory owned by the caller.  The library
- *   keeps no pointer after a call returns and allocates nothing.
+ *   keeps no pointer after a call returns and allocates nothing: scratch
+ *   space comes in as a caller-provided workspace.
  * - Calls only enqueue work on `stream` (0 = the null stream) and return; the
  *   caller synchronises.  Calls are re-entrant and may run concurrently on
  *   different streams when their output buffers do not overlap.
@@ -76,6 +77,9 @@ typedef struct da_shape {
   int32_t dtype;           /* da_dtype of q, k_pages and v_pages               */
   float scale;             /* score scale, > 0 and finite (usually 1/sqrt(D))  */
   int64_t NP;              /* pages in k_pages / v_pages, >= 1                 */
+  int32_t chunks;          /* 0: library choice; 1..64: each split is cut into  */
+                           /* this many page ranges, processed independently   */
+                           /* and folded back (needs a workspace)              */
 } da_shape;
 
 /*
@@ -105,6 +109,14 @@ typedef struct da_shape {
  *   m, e         [S, Hq, b] float32.  m is in the natural-log domain of the
  *                scaled score.  An empty split (no kept token) is written as
  *                MA = 0, m = -inf, e = 0.
+ * Workspace (device, caller-owned, 16-byte aligned, contents irrelevant):
+ *   When few (request, KV head, split) items exist, the library cuts every
+ *   split into page-range chunks so that all compute units get balanced work,
+ *   and folds the chunk partials back into the split partials.  That needs
+ *   da_micro_attention_workspace_size() bytes.  With sh->chunks == 0 and a
+ *   NULL or smaller workspace the call runs unchunked (same results, possibly
+ *   slower); with sh->chunks > 1 a missing workspace is DA_ERR_INVALID_ARG.
+ *   Concurrent calls must not share a workspace.
  * Errors: DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED (D, P, dtype or G = Hq/Hkv
  * outside the built set {1, 2, 4, 8}), DA_ERR_HIP.
  */
@@ -112,7 +124,11 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
                              const void* v_pages, const int32_t* block_table,
                              const int32_t* seq_lens, const int32_t* split_bounds,
                              const uint8_t* block_mask, float* MA, float* m, float* e,
-                             hipStream_t stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes da_micro_attention uses for this shape (0 if it runs
+ * unchunked).  Host-only; writes *bytes. */
+da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes);
 
 /*
  * Aggregate b partials per (request, query head) into attention output.

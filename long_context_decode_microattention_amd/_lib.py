@@ -39,6 +39,7 @@ class DaShape(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("NP", ctypes.c_int64),
+        ("chunks", ctypes.c_int32),
     ]
 
 
@@ -63,8 +64,11 @@ def load() -> ctypes.CDLL:
             f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
     lib = ctypes.CDLL(LIB_PATH)
     sp = ctypes.POINTER(DaShape)
-    lib.da_micro_attention.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.da_micro_attention.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, ctypes.c_size_t, _VP]
     lib.da_micro_attention.restype = ctypes.c_int
+    lib.da_micro_attention_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.da_micro_attention_workspace_size.restype = ctypes.c_int
     lib.da_merge.argtypes = [sp, _VP, _VP, _VP, _VP, _VP]
     lib.da_merge.restype = ctypes.c_int
     lib.da_check_inputs.argtypes = [sp, _VP, _VP, _VP, _VP]
@@ -112,7 +116,8 @@ def _need(t: torch.Tensor, name: str, dtype, device, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
-def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None) -> DaShape:
+def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None,
+             chunks: int = 0) -> DaShape:
     S, Hq, D = q.shape
     NP, Hkv, P, D2 = k_pages.shape
     if D2 != D:
@@ -128,12 +133,40 @@ def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = Non
         raise TypeError(f"unsupported dtype {q.dtype}")
     return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=block_table.shape[1],
                    max_splits=split_bounds.shape[2] - 1, bounds_per_head=int(nbh == Hkv and Hkv > 1),
-                   dtype=dt, scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), NP=NP)
+                   dtype=dt, scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), NP=NP,
+                   chunks=int(chunks))
+
+
+_WORKSPACE = {}
+
+
+def workspace_size(sh: DaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _cached_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    """A per-device scratch tensor of at least nbytes, reused across calls.
+    Calls that may overlap on different streams must pass their own."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACE[key] = ws
+    return ws
 
 
 def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
-                    *, scale: Optional[float] = None, out=None):
-    """MicroAttention partials (MA [S,Hq,b,D], m [S,Hq,b], e [S,Hq,b]) via da_micro_attention."""
+                    *, scale: Optional[float] = None, out=None, chunks: int = 0,
+                    workspace: Optional[torch.Tensor] = None):
+    """MicroAttention partials (MA [S,Hq,b,D], m [S,Hq,b], e [S,Hq,b]) via da_micro_attention.
+
+    chunks: 0 lets the library cut splits into page ranges when that balances
+    the launch; a positive value forces that many.  workspace: a uint8
+    device tensor; by default a cached per-device one is used."""
     dev = q.device
     _need(q, "q", None, dev, 3)
     _need(k_pages, "k_pages", q.dtype, dev, 4)
@@ -145,7 +178,7 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
     _need(split_bounds, "split_bounds", torch.int32, dev, 3)
     if block_mask is not None:
         _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_pages, block_table, split_bounds, scale)
+    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks)
     if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
         raise ValueError("block_table, seq_lens and split_bounds must have S rows")
     if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
@@ -156,9 +189,15 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
         e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
     else:
         MA, m, e = out
+    if workspace is None:
+        workspace = _cached_workspace(dev, workspace_size(sh))
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().da_micro_attention(
         ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
-        _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m), _ptr(e), _stream(dev)))
+        _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m), _ptr(e), _ptr(workspace),
+        ws_bytes, _stream(dev)))
     return MA, m, e
 
 
@@ -180,10 +219,10 @@ def merge(MA, m, e, *, out=None):
 
 
 def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
-              *, scale: Optional[float] = None):
+              *, scale: Optional[float] = None, chunks: int = 0):
     """One decode step: micro_attention then merge."""
     MA, m, e = micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds,
-                               block_mask, scale=scale)
+                               block_mask, scale=scale, chunks=chunks)
     return merge(MA, m, e)
 
 

@@ -12,6 +12,9 @@
 
 namespace {
 
+constexpr int kMaxChunks = 64;
+constexpr int kAutoMaxChunks = 16;
+
 thread_local std::string g_last_error;
 
 da_status fail(da_status st, const char* fmt, ...) {
@@ -49,7 +52,46 @@ da_status check_shape(const da_shape* sh) {
     return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits exceeds the launch range");
   if (sh->NP > (long long)INT_MAX + 1)
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
+  if (sh->chunks < 0 || sh->chunks > kMaxChunks)
+    return fail(DA_ERR_INVALID_ARG, "chunks must be 0 (library choice) or 1..%d (got %d)",
+                kMaxChunks, sh->chunks);
   return DA_OK;
+}
+
+// Chunks per split.  A launch wants enough workgroups that every compute
+// unit holds several and the dispatcher can even out unequal items (dense vs
+// masked heads, ragged lengths); below that target, splits are cut into page
+// ranges, at most as many as a split of an evenly divided max-length request
+// has pages.
+int resolve_chunks(const da_shape* sh) {
+  if (sh->chunks > 0) return sh->chunks;
+  const long long target = da::micro_target_items(sh->dtype, sh->D, sh->Hq / sh->Hkv);
+  const long long items = (long long)sh->S * sh->Hkv * sh->max_splits;
+  if (items >= target) return 1;
+  long long c = (target + items - 1) / items;
+  if (c > kAutoMaxChunks) c = kAutoMaxChunks;
+  const long long pages_per_split = sh->max_pages / sh->max_splits;  // typical split size
+  if (c > pages_per_split) c = pages_per_split;
+  return c < 1 ? 1 : (int)c;
+}
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Workspace layout: chunk MA [n, chunks, D], then chunk m and e [n, chunks],
+// n = S * Hq * max_splits, each part 16-byte aligned.
+struct WsLayout {
+  size_t ma, m, e, total;
+};
+
+WsLayout ws_layout(const da_shape* sh, int chunks) {
+  WsLayout w{0, 0, 0, 0};
+  if (chunks <= 1) return w;
+  const size_t n = (size_t)sh->S * sh->Hq * sh->max_splits * chunks;
+  w.ma = 0;
+  w.m = align16(n * sh->D * sizeof(float));
+  w.e = w.m + align16(n * sizeof(float));
+  w.total = w.e + align16(n * sizeof(float));
+  return w;
 }
 
 }  // namespace
@@ -60,7 +102,7 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
                              const void* v_pages, const int32_t* block_table,
                              const int32_t* seq_lens, const int32_t* split_bounds,
                              const uint8_t* block_mask, float* MA, float* m, float* e,
-                             hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   da_status st = check_shape(sh);
   if (st != DA_OK) return st;
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds || !MA || !m || !e)
@@ -78,6 +120,20 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   if (!da::micro_supported(sh->dtype, sh->D, G))
     return fail(DA_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", G);
 
+  int chunks = resolve_chunks(sh);
+  WsLayout ws = ws_layout(sh, chunks);
+  if (chunks > 1 && (workspace == nullptr || workspace_bytes < ws.total)) {
+    if (sh->chunks > 1)
+      return fail(DA_ERR_INVALID_ARG, "chunks=%d needs a workspace of %zu bytes (got %zu)",
+                  chunks, ws.total, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    chunks = 1;
+    ws = ws_layout(sh, 1);
+  }
+  if ((long long)sh->S * sh->Hkv * sh->max_splits * chunks > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits * chunks exceeds the launch range");
+  if (chunks > 1 && !aligned(workspace, 16))
+    return fail(DA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
   da::MicroParams p{};
   p.q = q;
   p.k = k_pages;
@@ -86,9 +142,11 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   p.lens = seq_lens;
   p.bounds = split_bounds;
   p.mask = block_mask;
-  p.MA = MA;
-  p.m = m;
-  p.e = e;
+  char* wsb = static_cast<char*>(workspace);
+  p.MA = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.ma) : MA;
+  p.m = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.m) : m;
+  p.e = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.e) : e;
+  p.chunks = chunks;
   p.S = sh->S;
   p.Hq = sh->Hq;
   p.Hkv = sh->Hkv;
@@ -97,9 +155,23 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   p.max_splits = sh->max_splits;
   p.bounds_per_head = sh->bounds_per_head;
   p.scale = sh->scale;
-  const hipError_t err = da::launch_micro(sh->dtype, sh->D, G, p, stream);
+  hipError_t err = da::launch_micro(sh->dtype, sh->D, G, p, stream);
   if (err != hipSuccess)
     return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
+  if (chunks > 1) {
+    err = da::launch_combine(p.MA, p.m, p.e, MA, m, e, (long long)sh->S * sh->Hq * sh->max_splits,
+                             chunks, sh->D, stream);
+    if (err != hipSuccess)
+      return fail(DA_ERR_HIP, "chunk-combine launch failed: %s", hipGetErrorString(err));
+  }
+  return DA_OK;
+}
+
+da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
+  if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
+  da_status st = check_shape(sh);
+  if (st != DA_OK) return st;
+  *bytes = ws_layout(sh, resolve_chunks(sh)).total;
   return DA_OK;
 }
 

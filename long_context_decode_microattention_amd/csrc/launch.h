@@ -16,10 +16,11 @@ struct MicroParams {
   const int32_t* lens;
   const int32_t* bounds;
   const uint8_t* mask;  // may be null
-  float* MA;
-  float* m;
+  float* MA;  // [S, Hq, max_splits, chunks, D]: the split partials when chunks == 1,
+  float* m;   // else one partial per chunk (workspace), folded by launch_combine
   float* e;
   int S, Hq, Hkv, P, max_pages, max_splits, bounds_per_head;
+  int chunks;  // page-range pieces per split, >= 1
   float scale;
 };
 
@@ -27,6 +28,15 @@ struct MicroParams {
 // built; callers check the combination before calling.
 hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream_t stream);
 bool micro_supported(int dtype, int D, int G);
+// Workgroups a launch of that kernel wants for balance (the chunk heuristic's
+// target): the matrix-core kernel holds fewer workgroups per CU and gains
+// from finer pieces.
+long long micro_target_items(int dtype, int D, int G);
+
+// Folds `chunks` partials per (request, head, split) into one:
+// cMA [n, chunks, D], cm/ce [n, chunks] -> MA [n, D], m/e [n], n = S*Hq*max_splits.
+hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
+                          float* e, long long n, int chunks, int D, hipStream_t stream);
 
 hipError_t launch_merge(const float* MA, const float* m, const float* e, float* out, int S, int Hq,
                         int D, int B, hipStream_t stream);

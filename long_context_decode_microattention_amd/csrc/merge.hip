@@ -112,7 +112,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   }
 }
 
+// Folds the page-range chunks of each split back into the split's triple
+// (the same aggregation rule, keeping the triple form): one wave per
+// (request, head, split).
+__global__ __launch_bounds__(kWave) void combine_kernel(const float* __restrict__ cMA,
+                                                        const float* __restrict__ cm,
+                                                        const float* __restrict__ ce,
+                                                        float* __restrict__ MA,
+                                                        float* __restrict__ m,
+                                                        float* __restrict__ e, int chunks, int D) {
+  const size_t o = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* mr = cm + o * chunks;
+  const float* er = ce + o * chunks;
+  const float* MAr = cMA + o * (size_t)chunks * D;
+  float M = neg_inf();
+  for (int c = 0; c < chunks; ++c) M = fmaxf(M, mr[c]);
+  const float Ms = (M == neg_inf()) ? 0.f : M;
+  float eg = 0.f;
+  for (int c = 0; c < chunks; ++c) eg = fmaf(er[c], expf(mr[c] - Ms), eg);
+  for (int d = lane; d < D; d += kWave) {
+    float acc = 0.f;
+    for (int c = 0; c < chunks; ++c) acc = fmaf(MAr[(size_t)c * D + d], expf(mr[c] - Ms), acc);
+    MA[o * D + d] = acc;
+  }
+  if (lane == 0) {
+    m[o] = M;
+    e[o] = eg;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
+                          float* e, long long n, int chunks, int D, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n), dim3(kWave), 0, stream, cMA, cm, ce, MA, m,
+                     e, chunks, D);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const float* MA, const float* m, const float* e, float* out, int S, int Hq,
                         int D, int B, hipStream_t stream) {

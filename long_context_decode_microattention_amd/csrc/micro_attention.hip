@@ -1,22 +1,23 @@
-// MicroAttention kernel for gfx950: per (request, KV head, split) work item,
-// the partial softmax statistics and unnormalised value sum of every query
-// head of the KV head's group over the split's kept tokens:
+// MicroAttention on the vector ALUs, for one query head per KV head (G = 1)
+// and for fp32 K/V: per work item, the partial softmax statistics and
+// unnormalised value sum of every query head of the KV head's group over the
+// item's kept tokens:
 //   m_j = max_i s_i,  e_j = sum_i exp(s_i - m_j),  MA_j = sum_i exp(s_i - m_j) v_i
 // (Infinite-LLM page, section 方法细节, MicroAttention equations), with
 // s_i = scale * (q . k_i).  Whole pages with a zero block-mask entry are
 // neither loaded nor computed (LServe blog page, section 2.1.1).
 //
 // Work decomposition.  One 256-lane workgroup (4 waves) per work item.  The
-// item's kept logical pages are compacted into an LDS list (wave ballots, no
-// per-token branches), then cut into 16-token slabs that the 4 waves take
-// round-robin.  A slab of one KV head is contiguous in the pool
-// ([page, head, slot, D] layout), so every wave-wide 16-byte load reads 1 KiB
-// of consecutive bytes.  Each lane holds 16 bytes of one token row: a row of
-// LPT = D*sizeof(elem)/16 consecutive lanes covers one token, so a wave load
-// covers 64/LPT tokens ("rows").  Dot products are reduced inside each row
-// with DPP; every row keeps its own online (m, e, MA) state -- the triple is
-// closed under the aggregation rule, so rows never exchange maxima in the
-// loop -- and rows and waves are combined once at the end of the item.
+// item's kept logical pages are compacted into an LDS list, then cut into
+// 16-token slabs that the 4 waves take round-robin.  A slab of one KV head is
+// contiguous in the pool ([page, head, slot, D] layout), so every wave-wide
+// 16-byte load reads 1 KiB of consecutive bytes.  Each lane holds 16 bytes of
+// one token row: a row of LPT = D*sizeof(elem)/16 consecutive lanes covers a
+// token, so a wave load covers 64/LPT tokens ("rows").  Dot products are
+// reduced inside each row with DPP; every row keeps its own online (m, e, MA)
+// state -- the triple is closed under the aggregation rule, so rows never
+// exchange maxima in the loop -- and rows and waves are combined once at the
+// end of the item.
 //
 // Arithmetic: fp32 accumulation.  bf16 scores use v_dot2 (bf16 pairs, fp32
 // accumulate); bf16 values are widened exactly by bit shifts.  Exponentials
@@ -24,16 +25,14 @@
 // exp2((d - d_max) * scale*log2(e)); the reported m_j is scale * d_max.
 #include <type_traits>
 
-#include "device_common.h"
-#include "launch.h"
+#include "micro_common.h"
 
 namespace da {
-namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kPageCap = 1024;  // kept pages staged in LDS per batch
-constexpr int kSlab = 16;       // tokens per slab
+hipError_t launch_micro_mfma(int D, int G, const MicroParams& p, hipStream_t stream);
+bool micro_mfma_supported(int dtype, int D, int G);
+
+namespace {
 
 template <int DT, int D>
 struct Layout {
@@ -57,14 +56,12 @@ template <bool B>
 using Bool = std::integral_constant<bool, B>;
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
+__global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   using L = Layout<DT, D>;
   __shared__ int s_phys[kPageCap];
   __shared__ int s_lp[kPageCap];
-  __shared__ int s_cnt[kWaves];
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_e[kWaves][G];
+  __shared__ int s_cnt[kMicroWaves];
+  __shared__ FinishLds<G, D> s_fin;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -72,21 +69,10 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
   const int row = lane / L::LPT;
   const int chunk = lane % L::LPT;
 
-  const int item = blockIdx.x;
-  const int j = item % p.max_splits;
-  const int sk = item / p.max_splits;
-  const int kvh = sk % p.Hkv;
-  const int s = sk / p.Hkv;
-  const int h0 = kvh * G;
+  const Item it = decode_item(p);
+  const int s = it.s, kvh = it.kvh, h0 = kvh * G;
+  const int t0 = it.t0, t1 = it.t1;
   const int P = p.P;
-
-  int Ls = p.lens[s];
-  Ls = max(0, min(Ls, p.max_pages * P));
-  const int32_t* sb =
-      p.bounds + ((size_t)s * (p.bounds_per_head ? p.Hkv : 1) + (p.bounds_per_head ? kvh : 0)) *
-                     (size_t)(p.max_splits + 1);
-  const int t0 = max(sb[j], 0);
-  const int t1 = min(sb[j + 1], Ls);
   const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
   // Query fragment of every head in the group: the lane's 16-byte column.
@@ -108,8 +94,6 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
   }
 
   if (t0 < t1) {
-    const int lp0 = t0 / P;
-    const int lp1 = (t1 + P - 1) / P;
     const uint8_t* mrow = p.mask ? p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages : nullptr;
     const int32_t* trow = p.table + (size_t)s * p.max_pages;
     const int spp = P / kSlab;  // slabs per page
@@ -117,26 +101,8 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
     const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
     const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
 
-    for (int base = lp0; base < lp1; base += kPageCap) {
-      // ---- compact the kept pages of [base, base + kPageCap) into LDS ----
-      int nk = 0;
-      const int span = min(kPageCap, lp1 - base);
-      for (int r = 0; r < span; r += kThreads) {
-        const int lp = base + r + tid;
-        const bool keep = lp < lp1 && (mrow == nullptr || mrow[lp] != 0);
-        const uint64_t bal = __ballot(keep);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) s_cnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = nk;
-        for (int w = 0; w < wave; ++w) off += s_cnt[w];
-        if (keep) {
-          s_phys[off + pre] = trow[lp];
-          s_lp[off + pre] = lp;
-        }
-        nk += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-        __syncthreads();
-      }
+    for (int base = it.lp0; base < it.lp1; base += kPageCap) {
+      const int nk = compact_pages(base, it.lp1, mrow, trow, s_phys, s_lp, s_cnt);
 
       // ---- stream the slabs: wave w takes slabs w, w+4, ... ----
       const int nslab = nk * spp;
@@ -260,18 +226,15 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
           compute(sl, f, Bool<false>{});
       };
 
-      Frag<DT, D> fa, fb;
+      // one slab in flight ahead of the one being computed
+      Frag<DT, D> cur, nxt;
       int sl = wave;
-      if (sl < nslab) load(sl, fa);
+      if (sl < nslab) load(sl, cur);
       while (sl < nslab) {
-        int sn = sl + kWaves;
-        if (sn < nslab) load(sn, fb);
-        step(sl, fa);
-        sl = sn;
-        if (sl >= nslab) break;
-        sn = sl + kWaves;
-        if (sn < nslab) load(sn, fa);
-        step(sl, fb);
+        const int sn = sl + kMicroWaves;
+        if (sn < nslab) load(sn, nxt);
+        step(sl, cur);
+        cur = nxt;
         sl = sn;
       }
       __syncthreads();  // the page list is rewritten by the next batch
@@ -298,47 +261,14 @@ __global__ __launch_bounds__(kThreads) void micro_kernel(MicroParams p) {
       m_[g] = M;
     }
   }
-
-  // ---- combine the waves through LDS and write the partials ----
-  if (row == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int k = 0; k < L::EPL; ++k) s_acc[wave][g][chunk * L::EPL + k] = acc[g][k];
-      if (chunk == 0) {
-        s_m[wave][g] = m_[g];
-        s_e[wave][g] = e_[g];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    const float Ms = (M == neg_inf()) ? 0.f : M;
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2((s_m[w][g] - Ms) * c);
-      num = fmaf(s_acc[w][g][d], f, num);
-      den = fmaf(s_e[w][g], f, den);
-    }
-    const size_t o = (size_t)(s * p.Hq + h0 + g) * p.max_splits + j;
-    p.MA[o * D + d] = num;
-    if (d == 0) {
-      p.m[o] = M * p.scale;
-      p.e[o] = den;
-    }
-  }
+  finish_item<G, D, L::LPT, L::EPL>(p, it, s_fin, m_, e_, acc, c);
 }
 
 template <int DT, int D, int G>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  const long long items = (long long)p.S * p.Hkv * p.max_splits;
-  hipLaunchKernelGGL((micro_kernel<DT, D, G>), dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+  const long long items = (long long)p.S * p.Hkv * p.max_splits * p.chunks;
+  hipLaunchKernelGGL((micro_kernel<DT, D, G>), dim3((unsigned)items), dim3(kMicroThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -360,8 +290,15 @@ bool micro_supported(int dtype, int D, int G) {
          (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+long long micro_target_items(int dtype, int D, int G) {
+  return micro_mfma_supported(dtype, D, G) ? 4096 : 2048;
+}
+
+// bf16 with grouped query heads goes to the matrix-core kernel; one query
+// head per KV head and fp32 K/V stay on the vector ALUs.
 hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream_t stream) {
   if (!micro_supported(dtype, D, G)) return hipErrorInvalidValue;
+  if (micro_mfma_supported(dtype, D, G)) return launch_micro_mfma(D, G, p, stream);
   if (dtype == 0) return D == 64 ? dispatch_g<0, 64>(G, p, stream) : dispatch_g<0, 128>(G, p, stream);
   return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
 }

@@ -1,0 +1,329 @@
+// MicroAttention on the matrix cores, for bf16 K/V with G = 2, 4 or 8 query
+// heads per KV head (grouped-query attention).  Same per-item result as the
+// vector kernel -- m_j, e_j and MA_j of the MicroAttention equations
+// (Infinite-LLM page, section 方法细节) for every query head of the group --
+// with the page list, slabs and block-mask skipping of that kernel.
+//
+// With G query heads per KV head the scores and the value sums are small
+// dense contractions, and on the vector ALUs they cost about 3 instructions
+// per KV byte, too close to the issue budget to keep HBM saturated.  Per
+// 16-token slab a wave instead runs:
+//
+//   scores   S[h][t] = q_h . k_t on v_mfma_f32_16x16x32_bf16: A = the query
+//            heads (16 rows, G used), B = the slab's keys (16 columns), K =
+//            D in 32-wide steps.  The B operand wants lane l to hold 8
+//            consecutive dims of token l%16, so each key load reads 64
+//            contiguous bytes of 16 token rows (the dims are visited in the
+//            order chunk = 4*step + l/16; q uses the same order).  Lane l,
+//            register i receives S[4*(l/16) + i][l % 16].
+//   softmax  per-head slab maxima by DPP reductions over the 16 lanes of a
+//            row, read out as wave-uniform values; the running maximum is
+//            per wave, so the value accumulators are rescaled only when a
+//            head's maximum rises (wave-uniform branch).
+//   values   on v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4x4, K = 1): block
+//            b = l/4 takes A = p of heads 0..3 from lanes 4b..4b+3 and B = one
+//            value element from each of its 4 lanes, so the values are used
+//            in the coalesced layout of the vector kernel (lane l holds 8
+//            dims of token row l/LPT) and every lane ends up with its own 8
+//            dims x 4 heads, all four block rows useful for G >= 4.  The
+//            probabilities move from the score layout to that operand
+//            layout through a 16 x G float scratch in LDS per wave.
+#include "micro_common.h"
+
+namespace da {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MLayout {
+  static constexpr int TOKB = D * 2;       // bf16 token row bytes
+  static constexpr int LPT = TOKB / 16;    // value lanes per token row
+  static constexpr int TPI = kWave / LPT;  // token rows per value load
+  static constexpr int NI = kSlab / TPI;   // value loads per slab
+  static constexpr int KS = D / 32;        // score k-steps
+  static constexpr int EPL = 8;            // bf16 elements per lane
+};
+
+template <int D>
+struct MFrag {
+  uint4 k[MLayout<D>::KS];
+  uint4 v[MLayout<D>::NI];
+};
+
+template <bool B>
+using Bool = std::integral_constant<bool, B>;
+
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
+// Two waves per SIMD: the register budget that holds the prefetched slab, the
+// query operand and the accumulators without spilling (measured faster than
+// three waves with spills).
+template <int D, int G>
+__global__ __launch_bounds__(kMicroThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
+  using L = MLayout<D>;
+  constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
+  static_assert(G == 2 || G == 4 || G == 8, "group size");
+  __shared__ int s_phys[kPageCap];
+  __shared__ int s_lp[kPageCap];
+  __shared__ int s_cnt[kMicroWaves];
+  __shared__ float s_p[kMicroWaves][kSlab * G];
+  __shared__ FinishLds<G, D> s_fin;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;  // score column: token within the slab
+  const int grp = lane >> 4;  // score row group: heads 4*grp .. 4*grp+3
+  const int vrow = lane / L::LPT;
+  const int quad = lane & 3;  // head within a 4x4 block of the value product
+
+  const Item it = decode_item(p);
+  const int s = it.s, kvh = it.kvh, h0 = kvh * G;
+  const int t0 = it.t0, t1 = it.t1;
+  const int P = p.P;
+  const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
+
+  // score operand A: lane l -> head l%16 (zero beyond G), dims chunk 4*step + l/16
+  uint4 qa[L::KS];
+#pragma unroll
+  for (int st = 0; st < L::KS; ++st) {
+    qa[st] = make_uint4(0, 0, 0, 0);
+    if (col < G) {
+      const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * L::TOKB +
+                       (size_t)(4 * st + grp) * 16;
+      qa[st] = *reinterpret_cast<const uint4*>(qp);
+    }
+  }
+
+  float m_h[G];        // running raw-dot maximum per head (wave-uniform)
+  float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
+  f32x4_t acc[HS][8];  // value sums: block layout, register i = head 4*hs + i
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_h[h] = neg_inf();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e_l[i] = 0.f;
+#pragma unroll
+  for (int hs = 0; hs < HS; ++hs)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (t0 < t1) {
+    const uint8_t* mrow = p.mask ? p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages : nullptr;
+    const int32_t* trow = p.table + (size_t)s * p.max_pages;
+    const int spp = P / kSlab;
+    const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+    const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB +
+                        (size_t)col * L::TOKB + (size_t)grp * 16;
+    const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+
+    for (int base = it.lp0; base < it.lp1; base += kPageCap) {
+      const int nk = compact_pages(base, it.lp1, mrow, trow, s_phys, s_lp, s_cnt);
+      const int nslab = nk * spp;
+
+      auto load = [&](int sl, MFrag<D>& f) {
+        const int kp = sl / spp;
+        const int sub = sl - kp * spp;
+        const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
+        const int tb = s_lp[kp] * P + sub * kSlab;
+        if (tb >= t0 && tb + kSlab <= t1) {
+#pragma unroll
+          for (int st = 0; st < L::KS; ++st) f.k[st] = load_stream16(kbase + off + st * 64);
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) f.v[i] = load_stream16(vbase + off + i * 1024);
+        } else {
+          const int tk = tb + col;
+          const bool kok = tk >= t0 && tk < t1;
+#pragma unroll
+          for (int st = 0; st < L::KS; ++st)
+            f.k[st] = kok ? load_stream16(kbase + off + st * 64) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            const int tv = tb + i * L::TPI + vrow;
+            f.v[i] = (tv >= t0 && tv < t1) ? load_stream16(vbase + off + i * 1024)
+                                           : make_uint4(0, 0, 0, 0);
+          }
+        }
+      };
+
+      auto compute = [&](int sl, const MFrag<D>& f, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int kp = sl / spp;
+        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+
+        // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < L::KS; ++st)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                      __builtin_bit_cast(bf16x8_t, f.k[st]), sc,
+                                                      0, 0, 0);
+        const bool kvalid = FULL || (tb + col >= t0 && tb + col < t1);
+
+        // slab maxima per head, then the running maxima (wave-uniform)
+        float rm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rm[i] = row_max16(kvalid ? sc[i] : neg_inf());
+        float alpha_h[G], nmc_h[G];
+        bool moved = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
+          const float mn = fmaxf(m_h[h], mx);
+          const float ms = (FULL || mn != neg_inf()) ? mn : 0.f;
+          alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
+          nmc_h[h] = -ms * c;
+          moved |= mn != m_h[h];
+          m_h[h] = mn;
+        }
+
+        // probabilities in the score layout; exp-sums per token column
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hi = (i < G) ? i : 0;
+          float nmc = nmc_h[hi], al = alpha_h[hi];
+          if constexpr (G > 4) {
+            if (grp == 1) {
+              nmc = nmc_h[4 + i];
+              al = alpha_h[4 + i];
+            }
+          }
+          pw[i] = kvalid ? fast_exp2(fmaf(sc[i], c, nmc)) : 0.f;
+          e_l[i] = fmaf(e_l[i], al, pw[i]);
+        }
+
+        // probabilities to the value-product operand layout (per-wave LDS)
+        float* sp = s_p[wave];
+        if (grp < HS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * grp + i < G) sp[col * G + 4 * grp + i] = pw[i];
+        }
+
+        if (moved) {
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs)
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
+        }
+
+        // value sums: acc[hs][k] += p[4hs + i][token] * v[token][dim k of this lane]
+#pragma unroll
+        for (int j = 0; j < L::NI; ++j) {
+          float pa[HS];
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs)
+            pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
+          const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = bf16_lo(w4[k]);
+            const float hi = bf16_hi(w4[k]);
+#pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
+              acc[hs][2 * k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], lo, acc[hs][2 * k], 0, 0, 0);
+              acc[hs][2 * k + 1] =
+                  __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], hi, acc[hs][2 * k + 1], 0, 0, 0);
+            }
+          }
+        }
+      };
+
+      auto step = [&](int sl, const MFrag<D>& f) {
+        const int kp = sl / spp;
+        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+        if (tb >= t0 && tb + kSlab <= t1)
+          compute(sl, f, Bool<true>{});
+        else
+          compute(sl, f, Bool<false>{});
+      };
+
+      MFrag<D> fa, fb;
+      int sl = wave;
+      if (sl < nslab) load(sl, fa);
+      while (sl < nslab) {
+        int sn = sl + kMicroWaves;
+        if (sn < nslab) load(sn, fb);
+        step(sl, fa);
+        sl = sn;
+        if (sl >= nslab) break;
+        sn = sl + kMicroWaves;
+        if (sn < nslab) load(sn, fa);
+        step(sl, fb);
+        sl = sn;
+      }
+      __syncthreads();  // the page list is rewritten by the next batch
+    }
+  }
+
+  // ---- per-wave totals: exp-sums over token columns, values over token rows ----
+  float we[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x = e_l[h & 3];
+    x = x + dpp<kDppQuadXor1>(x);
+    x = x + dpp<kDppQuadXor2>(x);
+    x = x + dpp<kDppHalfMirror>(x);
+    x = x + dpp<kDppRowMirror>(x);
+    we[h] = lane_value(x, 16 * (h >> 2));
+  }
+  float accg[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
+#pragma unroll
+  for (int off = L::LPT; off < kWave; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) accg[h][k] += __shfl_xor(accg[h][k], off, kWave);
+
+  finish_item<G, D, L::LPT, 8>(p, it, s_fin, m_h, we, accg, c);
+}
+
+template <int D, int G>
+hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
+  const long long items = (long long)p.S * p.Hkv * p.max_splits * p.chunks;
+  hipLaunchKernelGGL((micro_mfma_kernel<D, G>), dim3((unsigned)items), dim3(kMicroThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
+  switch (G) {
+    case 2: return launch_one<D, 2>(p, stream);
+    case 4: return launch_one<D, 4>(p, stream);
+    case 8: return launch_one<D, 8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool micro_mfma_supported(int dtype, int D, int G) {
+  return dtype == 1 && (D == 64 || D == 128) && (G == 2 || G == 4 || G == 8);
+}
+
+hipError_t launch_micro_mfma(int D, int G, const MicroParams& p, hipStream_t stream) {
+  return D == 64 ? dispatch_g<64>(G, p, stream) : dispatch_g<128>(G, p, stream);
+}
+
+}  // namespace da

@@ -30,19 +30,20 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 def good_shape(**kw):
     base = dict(S=2, Hq=8, Hkv=2, D=128, P=16, max_pages=4, max_splits=2, bounds_per_head=0,
-                dtype=_lib.DA_BF16, scale=0.088, NP=8)
+                dtype=_lib.DA_BF16, scale=0.088, NP=8, chunks=0)
     base.update(kw)
     return _lib.DaShape(**base)
 
 
 def call_micro(lib, sh, **ptrs):
     args = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, bounds=FAKE, mask=None,
-                MA=FAKE, m=FAKE, e=FAKE)
+                MA=FAKE, m=FAKE, e=FAKE, ws=None, ws_bytes=0)
     args.update(ptrs)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.da_micro_attention(None if sh is None else ctypes.byref(sh),
                                   *(vp(args[k]) for k in ("q", "k", "v", "table", "lens", "bounds",
-                                                          "mask", "MA", "m", "e")), None)
+                                                          "mask", "MA", "m", "e", "ws")),
+                                  args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("case,status", [
@@ -60,6 +61,10 @@ def call_micro(lib, sh, **ptrs):
     (dict(ptrs=dict(k=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(MA=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(lens=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(chunks=-1)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(chunks=65)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(chunks=4)), _lib.DA_ERR_INVALID_ARG),  # forced chunks, no workspace
+    (dict(shape=dict(chunks=4), ptrs=dict(ws=FAKE, ws_bytes=16)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
     (dict(shape=dict(P=24)), _lib.DA_ERR_UNSUPPORTED),
     (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
@@ -70,6 +75,27 @@ def test_micro_rejects(lib, case, status):
     got = call_micro(lib, sh, **case.get("ptrs", {}))
     assert got == status, (got, lib.da_last_error())
     assert len(lib.da_last_error()) > 0
+
+
+def test_workspace_size(lib):
+    n = ctypes.c_size_t(7)
+    # few items: the library cuts splits into chunks and needs a workspace
+    sh = good_shape(S=1, Hq=32, Hkv=8, max_pages=8192, max_splits=16, P=64)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
+    chunks = 2  # 128 items -> 2048 / 128 = 16 chunks (capped at 16)
+    assert n.value > 0
+    # many items: no chunks, no workspace
+    sh = good_shape(S=64, Hq=40, Hkv=40, max_pages=2048, max_splits=16, P=16)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
+    assert n.value == 0
+    # forced chunks: exactly the three chunk arrays, 16-byte aligned each
+    sh = good_shape(S=2, Hq=8, Hkv=2, D=128, max_splits=3, chunks=5)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
+    rows = 2 * 8 * 3 * 5
+    align = lambda x: (x + 15) // 16 * 16
+    assert n.value == align(rows * 128 * 4) + 2 * align(rows * 4)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), None) == _lib.DA_ERR_INVALID_ARG
+    del chunks
 
 
 def test_merge_rejects(lib):

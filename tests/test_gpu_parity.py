@@ -57,6 +57,23 @@ def test_reduced_config_parity(cfg, seed):
                      f"{cfg}/{seed} partials")
 
 
+@pytest.mark.parametrize("chunks", [1, 3, 7])
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C4", "C5"])
+def test_forced_chunks_parity(cfg, chunks):
+    """Splits cut into a forced number of page-range chunks (folded back by
+    the combine kernel) give the same partials and outputs within tolerance."""
+    spec = REDUCED[cfg]
+    announce("chunks", cfg, chunks)
+    b = wl.build(spec, 4, DEV)
+    out, MA, m, e = run_gpu(b, chunks=chunks)
+    inp = host_inputs(b)
+    tol = TOL_OUT[spec.dtype]
+    compare_out(out.cpu().numpy(), oracle_out(inp, b.scale), tol, f"{cfg} chunks={chunks}")
+    oMA, om, oe = oracle_micro(inp, b.scale)
+    compare_partials(MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy(), oMA, om, oe, tol,
+                     f"{cfg} chunks={chunks} partials")
+
+
 # Full-size workloads: outputs sampled at (request, KV-head range) units the
 # oracle computes one by one.
 FULL_SAMPLES = {
@@ -134,20 +151,21 @@ def _fill_pool_from_logical(b: wl.Batch, values: np.ndarray, target: torch.Tenso
     target.copy_(host.to(target.dtype))
 
 
+@pytest.mark.parametrize("chunks", [0, 5])
 @pytest.mark.parametrize("cfg", ["C1", "C3", "C5"])
-def test_fingerprint_counts_bit_exact(cfg):
+def test_fingerprint_counts_bit_exact(cfg, chunks):
     """q = 0 makes every weight exp(0) = 1: m_j = 0, e_j = kept-token count and
     MA_j[c] = number of kept tokens whose fingerprint has bit c set -- exact
     integers, compared bitwise with numpy counts."""
     spec = REDUCED[cfg].replace(S=min(REDUCED[cfg].S, 3))
-    announce("fingerprint", cfg)
+    announce("fingerprint", cfg, chunks)
     b = wl.build(spec, 5, DEV)
     b.q.zero_()
     sp = b.spec
     L = int(b.seq_lens.max().item())
     bits = fingerprint(sp.S, sp.Hkv, L, sp.D)
     _fill_pool_from_logical(b, bits, b.v_pages)
-    _, MA, m, e = run_gpu(b)
+    _, MA, m, e = run_gpu(b, chunks=chunks)
     MA, m, e = MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy()
     lens = b.seq_lens.cpu().numpy()
     sb = b.split_bounds.cpu().numpy()
