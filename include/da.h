@@ -80,6 +80,9 @@ typedef struct da_shape {
   int32_t chunks;          /* 0: library choice; 1..64: each split is cut into  */
                            /* this many page ranges, processed independently   */
                            /* and folded back (needs a workspace)              */
+  int32_t schedule;        /* 0: library choice; 1: one workgroup per item;     */
+                           /* 2: persistent workgroups claiming items from a   */
+                           /* work queue in the workspace                      */
 } da_shape;
 
 /*
@@ -110,13 +113,15 @@ typedef struct da_shape {
  *                scaled score.  An empty split (no kept token) is written as
  *                MA = 0, m = -inf, e = 0.
  * Workspace (device, caller-owned, 16-byte aligned, contents irrelevant):
- *   When few (request, KV head, split) items exist, the library cuts every
- *   split into page-range chunks so that all compute units get balanced work,
- *   and folds the chunk partials back into the split partials.  That needs
- *   da_micro_attention_workspace_size() bytes.  With sh->chunks == 0 and a
- *   NULL or smaller workspace the call runs unchunked (same results, possibly
- *   slower); with sh->chunks > 1 a missing workspace is DA_ERR_INVALID_ARG.
- *   Concurrent calls must not share a workspace.
+ *   da_micro_attention_workspace_size() bytes.  It holds a work-queue
+ *   counter (reset on `stream` by the call itself) used when the grid of
+ *   (request, KV head, split) items is far larger than the GPU can hold at
+ *   once, and, when there are few items, the partials of page-range chunks
+ *   that every split is cut into for balance and folded back afterwards.
+ *   With sh->chunks == 0 and a NULL or smaller workspace the call runs with
+ *   one workgroup per unchunked item (same results, possibly slower); with
+ *   sh->chunks > 1 a missing workspace is DA_ERR_INVALID_ARG.  Concurrent
+ *   calls must not share a workspace.
  * Errors: DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED (D, P, dtype or G = Hq/Hkv
  * outside the built set {1, 2, 4, 8}), DA_ERR_HIP.
  */

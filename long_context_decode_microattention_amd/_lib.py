@@ -40,6 +40,7 @@ class DaShape(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("NP", ctypes.c_int64),
         ("chunks", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -117,7 +118,7 @@ def _need(t: torch.Tensor, name: str, dtype, device, ndim: int):
 
 
 def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None,
-             chunks: int = 0) -> DaShape:
+             chunks: int = 0, schedule: int = 0) -> DaShape:
     S, Hq, D = q.shape
     NP, Hkv, P, D2 = k_pages.shape
     if D2 != D:
@@ -134,7 +135,7 @@ def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = Non
     return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=block_table.shape[1],
                    max_splits=split_bounds.shape[2] - 1, bounds_per_head=int(nbh == Hkv and Hkv > 1),
                    dtype=dt, scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), NP=NP,
-                   chunks=int(chunks))
+                   chunks=int(chunks), schedule=int(schedule))
 
 
 _WORKSPACE = {}
@@ -161,12 +162,14 @@ def _cached_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tenso
 
 def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
                     *, scale: Optional[float] = None, out=None, chunks: int = 0,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None, schedule: int = 0):
     """MicroAttention partials (MA [S,Hq,b,D], m [S,Hq,b], e [S,Hq,b]) via da_micro_attention.
 
     chunks: 0 lets the library cut splits into page ranges when that balances
     the launch; a positive value forces that many.  workspace: a uint8
-    device tensor; by default a cached per-device one is used."""
+    device tensor; None uses a cached per-device one; False passes none (one
+    workgroup per item, no chunks).  schedule: 0 library choice, 1 one
+    workgroup per item, 2 persistent workgroups on a work queue."""
     dev = q.device
     _need(q, "q", None, dev, 3)
     _need(k_pages, "k_pages", q.dtype, dev, 4)
@@ -178,7 +181,7 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
     _need(split_bounds, "split_bounds", torch.int32, dev, 3)
     if block_mask is not None:
         _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks)
+    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule)
     if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
         raise ValueError("block_table, seq_lens and split_bounds must have S rows")
     if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
@@ -189,7 +192,9 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
         e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
     else:
         MA, m, e = out
-    if workspace is None:
+    if workspace is False:
+        workspace = None
+    elif workspace is None:
         workspace = _cached_workspace(dev, workspace_size(sh))
     elif workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the device of q")

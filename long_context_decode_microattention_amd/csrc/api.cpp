@@ -52,6 +52,8 @@ da_status check_shape(const da_shape* sh) {
     return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits exceeds the launch range");
   if (sh->NP > (long long)INT_MAX + 1)
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
+  if (sh->schedule < 0 || sh->schedule > 2)
+    return fail(DA_ERR_INVALID_ARG, "schedule must be 0, 1 or 2 (got %d)", sh->schedule);
   if (sh->chunks < 0 || sh->chunks > kMaxChunks)
     return fail(DA_ERR_INVALID_ARG, "chunks must be 0 (library choice) or 1..%d (got %d)",
                 kMaxChunks, sh->chunks);
@@ -77,18 +79,20 @@ int resolve_chunks(const da_shape* sh) {
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Workspace layout: chunk MA [n, chunks, D], then chunk m and e [n, chunks],
-// n = S * Hq * max_splits, each part 16-byte aligned.
+// Workspace layout: the work-queue counter of the persistent launch
+// (16 bytes), then, when splits are cut into chunks, chunk MA
+// [n, chunks, D] and chunk m and e [n, chunks], n = S * Hq * max_splits,
+// each part 16-byte aligned.
 struct WsLayout {
-  size_t ma, m, e, total;
+  size_t queue, ma, m, e, total;
 };
 
 WsLayout ws_layout(const da_shape* sh, int chunks) {
-  WsLayout w{0, 0, 0, 0};
+  WsLayout w{0, 16, 16, 16, 16};
   if (chunks <= 1) return w;
   const size_t n = (size_t)sh->S * sh->Hq * sh->max_splits * chunks;
-  w.ma = 0;
-  w.m = align16(n * sh->D * sizeof(float));
+  w.ma = 16;
+  w.m = w.ma + align16(n * sh->D * sizeof(float));
   w.e = w.m + align16(n * sizeof(float));
   w.total = w.e + align16(n * sizeof(float));
   return w;
@@ -122,16 +126,23 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
 
   int chunks = resolve_chunks(sh);
   WsLayout ws = ws_layout(sh, chunks);
-  if (chunks > 1 && (workspace == nullptr || workspace_bytes < ws.total)) {
+  const size_t have = workspace == nullptr ? (size_t)0 : workspace_bytes;
+  if (chunks > 1 && have < ws.total) {
     if (sh->chunks > 1)
       return fail(DA_ERR_INVALID_ARG, "chunks=%d needs a workspace of %zu bytes (got %zu)",
-                  chunks, ws.total, workspace == nullptr ? (size_t)0 : workspace_bytes);
+                  chunks, ws.total, have);
     chunks = 1;
     ws = ws_layout(sh, 1);
   }
+  // with room for the counter the launcher may run persistently (when the
+  // grid far exceeds the resident slots); without, one workgroup per item
+  const bool persistent = have >= ws.total;
+  if (sh->schedule == 2 && !persistent)
+    return fail(DA_ERR_INVALID_ARG, "schedule=2 needs a workspace of %zu bytes (got %zu)",
+                ws.total, have);
   if ((long long)sh->S * sh->Hkv * sh->max_splits * chunks > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits * chunks exceeds the launch range");
-  if (chunks > 1 && !aligned(workspace, 16))
+  if (persistent && !aligned(workspace, 16))
     return fail(DA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   da::MicroParams p{};
@@ -147,6 +158,10 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   p.m = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.m) : m;
   p.e = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.e) : e;
   p.chunks = chunks;
+  p.n_items = sh->S * sh->Hkv * sh->max_splits * chunks;
+  p.grab = 1;
+  p.schedule = sh->schedule;
+  p.queue = persistent ? reinterpret_cast<int*>(wsb + ws.queue) : nullptr;
   p.S = sh->S;
   p.Hq = sh->Hq;
   p.Hkv = sh->Hkv;

@@ -22,6 +22,14 @@ struct MicroParams {
   int S, Hq, Hkv, P, max_pages, max_splits, bounds_per_head;
   int chunks;  // page-range pieces per split, >= 1
   float scale;
+  // Persistent launch: `queue` is a device counter that is zero when the
+  // kernel starts; each workgroup claims `grab` consecutive items at a time
+  // until all n_items = S*Hkv*max_splits*chunks are taken.  queue == null:
+  // one workgroup per item (grid = n_items).
+  int* queue;
+  int n_items;
+  int grab;
+  int schedule;  // 0: launcher's choice, 1: one workgroup per item, 2: persistent
 };
 
 // Returns hipErrorInvalidValue for a (dtype, D, G) combination that is not
@@ -35,6 +43,10 @@ long long micro_target_items(int dtype, int D, int G);
 
 // Folds `chunks` partials per (request, head, split) into one:
 // cMA [n, chunks, D], cm/ce [n, chunks] -> MA [n, D], m/e [n], n = S*Hq*max_splits.
+// Zeroes the persistent-launch counter (a one-lane kernel, not a memset, so
+// it can be captured in a graph).
+hipError_t launch_queue_reset(int* queue, hipStream_t stream);
+
 hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
                           float* e, long long n, int chunks, int D, hipStream_t stream);
 

@@ -142,7 +142,16 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const float* __restrict_
   }
 }
 
+__global__ void queue_reset_kernel(int* queue) {
+  if (threadIdx.x == 0) *queue = 0;
+}
+
 }  // namespace
+
+hipError_t launch_queue_reset(int* queue, hipStream_t stream) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, stream, queue);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
                           float* e, long long n, int chunks, int D, hipStream_t stream) {

@@ -69,207 +69,210 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   const int row = lane / L::LPT;
   const int chunk = lane % L::LPT;
 
-  const Item it = decode_item(p);
-  const int s = it.s, kvh = it.kvh, h0 = kvh * G;
-  const int t0 = it.t0, t1 = it.t1;
-  const int P = p.P;
-  const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
+  __shared__ int s_claim;
+  for_each_item(p, &s_claim, [&](int x) {
+    const Item it = plan_item(p, x);
+    const int s = it.s, kvh = it.kvh, h0 = kvh * G;
+    const int t0 = it.t0, t1 = it.t1;
+    const int P = p.P;
+    const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  // Query fragment of every head in the group: the lane's 16-byte column.
-  uint4 qv[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const char* qp = static_cast<const char*>(p.q) +
-                     ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
-    qv[g] = *reinterpret_cast<const uint4*>(qp);
-  }
+    // Query fragment of every head in the group: the lane's 16-byte column.
+    uint4 qv[G];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const char* qp = static_cast<const char*>(p.q) +
+                       ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
+      qv[g] = *reinterpret_cast<const uint4*>(qp);
+    }
 
-  float m_[G], e_[G], acc[G][L::EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_[g] = neg_inf();
-    e_[g] = 0.f;
-#pragma unroll
-    for (int k = 0; k < L::EPL; ++k) acc[g][k] = 0.f;
-  }
+    float m_[G], e_[G], acc[G][L::EPL];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_[g] = neg_inf();
+      e_[g] = 0.f;
+  #pragma unroll
+      for (int k = 0; k < L::EPL; ++k) acc[g][k] = 0.f;
+    }
 
-  if (t0 < t1) {
-    const uint8_t* mrow = p.mask ? p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages : nullptr;
-    const int32_t* trow = p.table + (size_t)s * p.max_pages;
-    const int spp = P / kSlab;  // slabs per page
-    const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
-    const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
-    const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+    if (it.scan0 < it.scan1) {
+      const int32_t* trow = p.table + (size_t)s * p.max_pages;
+      const int spp = P / kSlab;  // slabs per page
+      const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+      const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
+      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
 
-    for (int base = it.lp0; base < it.lp1; base += kPageCap) {
-      const int nk = compact_pages(base, it.lp1, mrow, trow, s_phys, s_lp, s_cnt);
+      for (int base = it.scan0; base < it.scan1; base += kPageCap) {
+        const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
 
-      // ---- stream the slabs: wave w takes slabs w, w+4, ... ----
-      const int nslab = nk * spp;
+        // ---- stream the piece's slabs: wave w takes slabs w, w+4, ... ----
+        const int nslab = nk * spp;
 
-      auto load = [&](int sl, Frag<DT, D>& f) {
-        const int kp = sl / spp;
-        const int sub = sl - kp * spp;
-        const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
-        const int tb = s_lp[kp] * P + sub * kSlab;
-        if (tb >= t0 && tb + kSlab <= t1) {
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) {
-            f.k[i] = load_stream16(kbase + off + i * 1024);
-            f.v[i] = load_stream16(vbase + off + i * 1024);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) {
-            const int t = tb + i * L::TPI + row;
-            if (t >= t0 && t < t1) {
+        auto load = [&](int sl, Frag<DT, D>& f) {
+          const int kp = sl / spp;
+          const int sub = sl - kp * spp;
+          const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
+          const int tb = s_lp[kp] * P + sub * kSlab;
+          if (tb >= t0 && tb + kSlab <= t1) {
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
               f.k[i] = load_stream16(kbase + off + i * 1024);
               f.v[i] = load_stream16(vbase + off + i * 1024);
-            } else {
-              f.k[i] = make_uint4(0, 0, 0, 0);
-              f.v[i] = make_uint4(0, 0, 0, 0);
-            }
-          }
-        }
-      };
-
-      // FULL: every token of the slab lies inside [t0, t1)
-      auto compute = [&](int sl, const Frag<DT, D>& f, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        const int kp = sl / spp;
-        const int sub = sl - kp * spp;
-        const int tb = s_lp[kp] * P + sub * kSlab;
-
-        // scores: dot[i][g] for this row's token of wave load i
-        float dot[L::NI][G];
-#pragma unroll
-        for (int i = 0; i < L::NI; ++i) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float d;
-            if constexpr (DT == 1) {
-              d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
-              d = dot2_bf16(f.k[i].y, qv[g].y, d);
-              d = dot2_bf16(f.k[i].z, qv[g].z, d);
-              d = dot2_bf16(f.k[i].w, qv[g].w, d);
-            } else {
-              d = __builtin_bit_cast(float, f.k[i].x) * __builtin_bit_cast(float, qv[g].x);
-              d = fmaf(__builtin_bit_cast(float, f.k[i].y), __builtin_bit_cast(float, qv[g].y), d);
-              d = fmaf(__builtin_bit_cast(float, f.k[i].z), __builtin_bit_cast(float, qv[g].z), d);
-              d = fmaf(__builtin_bit_cast(float, f.k[i].w), __builtin_bit_cast(float, qv[g].w), d);
-            }
-            dot[i][g] = group_sum<L::LPT>(d);
-          }
-        }
-
-        bool valid[L::NI];
-#pragma unroll
-        for (int i = 0; i < L::NI; ++i) {
-          const int t = tb + i * L::TPI + row;
-          valid[i] = FULL || (t >= t0 && t < t1);
-        }
-
-        // online softmax update, once per slab
-        float pw[L::NI][G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float mx = m_[g];
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) mx = fmaxf(mx, valid[i] ? dot[i][g] : neg_inf());
-          const float ms = (FULL || mx != neg_inf()) ? mx : 0.f;
-          const float alpha = fast_exp2((m_[g] - ms) * c);
-          const float nmc = -ms * c;
-          float sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) {
-            const float w = valid[i] ? fast_exp2(fmaf(dot[i][g], c, nmc)) : 0.f;
-            pw[i][g] = w;
-            sum += w;
-          }
-          e_[g] = fmaf(e_[g], alpha, sum);
-          m_[g] = mx;
-#pragma unroll
-          for (int k = 0; k < L::EPL; ++k) acc[g][k] *= alpha;
-        }
-
-        // weighted value sum
-#pragma unroll
-        for (int i = 0; i < L::NI; ++i) {
-          float vf[L::EPL];
-          if constexpr (DT == 1) {
-            const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              vf[2 * k] = bf16_lo(w4[k]);
-              vf[2 * k + 1] = bf16_hi(w4[k]);
             }
           } else {
-            vf[0] = __builtin_bit_cast(float, f.v[i].x);
-            vf[1] = __builtin_bit_cast(float, f.v[i].y);
-            vf[2] = __builtin_bit_cast(float, f.v[i].z);
-            vf[3] = __builtin_bit_cast(float, f.v[i].w);
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
+              const int t = tb + i * L::TPI + row;
+              if (t >= t0 && t < t1) {
+                f.k[i] = load_stream16(kbase + off + i * 1024);
+                f.v[i] = load_stream16(vbase + off + i * 1024);
+              } else {
+                f.k[i] = make_uint4(0, 0, 0, 0);
+                f.v[i] = make_uint4(0, 0, 0, 0);
+              }
+            }
           }
-#pragma unroll
+        };
+
+        // FULL: every token of the slab lies inside [t0, t1)
+        auto compute = [&](int sl, const Frag<DT, D>& f, auto full_tag) {
+          constexpr bool FULL = decltype(full_tag)::value;
+          const int kp = sl / spp;
+          const int sub = sl - kp * spp;
+          const int tb = s_lp[kp] * P + sub * kSlab;
+
+          // scores: dot[i][g] for this row's token of wave load i
+          float dot[L::NI][G];
+  #pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+  #pragma unroll
+            for (int g = 0; g < G; ++g) {
+              float d;
+              if constexpr (DT == 1) {
+                d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
+                d = dot2_bf16(f.k[i].y, qv[g].y, d);
+                d = dot2_bf16(f.k[i].z, qv[g].z, d);
+                d = dot2_bf16(f.k[i].w, qv[g].w, d);
+              } else {
+                d = __builtin_bit_cast(float, f.k[i].x) * __builtin_bit_cast(float, qv[g].x);
+                d = fmaf(__builtin_bit_cast(float, f.k[i].y), __builtin_bit_cast(float, qv[g].y), d);
+                d = fmaf(__builtin_bit_cast(float, f.k[i].z), __builtin_bit_cast(float, qv[g].z), d);
+                d = fmaf(__builtin_bit_cast(float, f.k[i].w), __builtin_bit_cast(float, qv[g].w), d);
+              }
+              dot[i][g] = group_sum<L::LPT>(d);
+            }
+          }
+
+          bool valid[L::NI];
+  #pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            const int t = tb + i * L::TPI + row;
+            valid[i] = FULL || (t >= t0 && t < t1);
+          }
+
+          // online softmax update, once per slab
+          float pw[L::NI][G];
+  #pragma unroll
           for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pw[i][g], vf[k], acc[g][k]);
+            float mx = m_[g];
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) mx = fmaxf(mx, valid[i] ? dot[i][g] : neg_inf());
+            const float ms = (FULL || mx != neg_inf()) ? mx : 0.f;
+            const float alpha = fast_exp2((m_[g] - ms) * c);
+            const float nmc = -ms * c;
+            float sum = 0.f;
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
+              const float w = valid[i] ? fast_exp2(fmaf(dot[i][g], c, nmc)) : 0.f;
+              pw[i][g] = w;
+              sum += w;
+            }
+            e_[g] = fmaf(e_[g], alpha, sum);
+            m_[g] = mx;
+  #pragma unroll
+            for (int k = 0; k < L::EPL; ++k) acc[g][k] *= alpha;
           }
+
+          // weighted value sum
+  #pragma unroll
+          for (int i = 0; i < L::NI; ++i) {
+            float vf[L::EPL];
+            if constexpr (DT == 1) {
+              const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
+  #pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                vf[2 * k] = bf16_lo(w4[k]);
+                vf[2 * k + 1] = bf16_hi(w4[k]);
+              }
+            } else {
+              vf[0] = __builtin_bit_cast(float, f.v[i].x);
+              vf[1] = __builtin_bit_cast(float, f.v[i].y);
+              vf[2] = __builtin_bit_cast(float, f.v[i].z);
+              vf[3] = __builtin_bit_cast(float, f.v[i].w);
+            }
+  #pragma unroll
+            for (int g = 0; g < G; ++g) {
+  #pragma unroll
+              for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pw[i][g], vf[k], acc[g][k]);
+            }
+          }
+        };
+
+        auto step = [&](int sl, const Frag<DT, D>& f) {
+          const int kp = sl / spp;
+          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+          if (tb >= t0 && tb + kSlab <= t1)
+            compute(sl, f, Bool<true>{});
+          else
+            compute(sl, f, Bool<false>{});
+        };
+
+        // two slabs in flight ahead of the one being computed
+        Frag<DT, D> f0, f1, f2;
+        int sl = wave;
+        if (sl < nslab) load(sl, f0);
+        if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
+        while (sl < nslab) {
+          if (sl + 2 * kMicroWaves < nslab) load(sl + 2 * kMicroWaves, f2);
+          step(sl, f0);
+          f0 = f1;
+          f1 = f2;
+          sl += kMicroWaves;
         }
-      };
-
-      auto step = [&](int sl, const Frag<DT, D>& f) {
-        const int kp = sl / spp;
-        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
-        if (tb >= t0 && tb + kSlab <= t1)
-          compute(sl, f, Bool<true>{});
-        else
-          compute(sl, f, Bool<false>{});
-      };
-
-      // one slab in flight ahead of the one being computed
-      Frag<DT, D> cur, nxt;
-      int sl = wave;
-      if (sl < nslab) load(sl, cur);
-      while (sl < nslab) {
-        const int sn = sl + kMicroWaves;
-        if (sn < nslab) load(sn, nxt);
-        step(sl, cur);
-        cur = nxt;
-        sl = sn;
+        __syncthreads();  // the page list is rewritten by the next batch
       }
-      __syncthreads();  // the page list is rewritten by the next batch
     }
-  }
 
-  // ---- combine the rows of each wave (lanes l and l ^ (k * LPT)) ----
-#pragma unroll
-  for (int off = L::LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m_[g], off, kWave);
-      const float eo = __shfl_xor(e_[g], off, kWave);
-      const float M = fmaxf(m_[g], mo);
-      const float Ms = (M == neg_inf()) ? 0.f : M;
-      const float a = fast_exp2((m_[g] - Ms) * c);
-      const float b = fast_exp2((mo - Ms) * c);
-      e_[g] = e_[g] * a + eo * b;
-#pragma unroll
-      for (int k = 0; k < L::EPL; ++k) {
-        const float ao = __shfl_xor(acc[g][k], off, kWave);
-        acc[g][k] = acc[g][k] * a + ao * b;
+    // ---- combine the rows of each wave (lanes l and l ^ (k * LPT)) ----
+  #pragma unroll
+    for (int off = L::LPT; off < kWave; off <<= 1) {
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(m_[g], off, kWave);
+        const float eo = __shfl_xor(e_[g], off, kWave);
+        const float M = fmaxf(m_[g], mo);
+        const float Ms = (M == neg_inf()) ? 0.f : M;
+        const float a = fast_exp2((m_[g] - Ms) * c);
+        const float b = fast_exp2((mo - Ms) * c);
+        e_[g] = e_[g] * a + eo * b;
+  #pragma unroll
+        for (int k = 0; k < L::EPL; ++k) {
+          const float ao = __shfl_xor(acc[g][k], off, kWave);
+          acc[g][k] = acc[g][k] * a + ao * b;
+        }
+        m_[g] = M;
       }
-      m_[g] = M;
     }
-  }
-  finish_item<G, D, L::LPT, L::EPL>(p, it, s_fin, m_, e_, acc, c);
+    finish_item<G, D, L::LPT, L::EPL>(p, it, s_fin, m_, e_, acc, c);
+  });
 }
+
+// Resident workgroups per CU (0: as many as registers allow).
+constexpr int kValuWorkgroupsPerCU = 0;
 
 template <int DT, int D, int G>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  const long long items = (long long)p.S * p.Hkv * p.max_splits * p.chunks;
-  hipLaunchKernelGGL((micro_kernel<DT, D, G>), dim3((unsigned)items), dim3(kMicroThreads), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_micro_kernel(micro_kernel<DT, D, G>, kValuWorkgroupsPerCU, p, stream);
 }
 
 template <int DT, int D>
@@ -291,7 +294,7 @@ bool micro_supported(int dtype, int D, int G) {
 }
 
 long long micro_target_items(int dtype, int D, int G) {
-  return micro_mfma_supported(dtype, D, G) ? 4096 : 2048;
+  return micro_mfma_supported(dtype, D, G) ? 4096 : 1024;
 }
 
 // bf16 with grouped query heads goes to the matrix-core kernel; one query

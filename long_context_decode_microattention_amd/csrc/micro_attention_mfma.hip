@@ -90,220 +90,222 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   const int vrow = lane / L::LPT;
   const int quad = lane & 3;  // head within a 4x4 block of the value product
 
-  const Item it = decode_item(p);
-  const int s = it.s, kvh = it.kvh, h0 = kvh * G;
-  const int t0 = it.t0, t1 = it.t1;
-  const int P = p.P;
-  const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
+  __shared__ int s_claim;
+  for_each_item(p, &s_claim, [&](int x) {
+    const Item it = plan_item(p, x);
+    const int s = it.s, kvh = it.kvh, h0 = kvh * G;
+    const int t0 = it.t0, t1 = it.t1;
+    const int P = p.P;
+    const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  // score operand A: lane l -> head l%16 (zero beyond G), dims chunk 4*step + l/16
-  uint4 qa[L::KS];
-#pragma unroll
-  for (int st = 0; st < L::KS; ++st) {
-    qa[st] = make_uint4(0, 0, 0, 0);
-    if (col < G) {
-      const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * L::TOKB +
-                       (size_t)(4 * st + grp) * 16;
-      qa[st] = *reinterpret_cast<const uint4*>(qp);
-    }
-  }
-
-  float m_h[G];        // running raw-dot maximum per head (wave-uniform)
-  float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
-  f32x4_t acc[HS][8];  // value sums: block layout, register i = head 4*hs + i
-#pragma unroll
-  for (int h = 0; h < G; ++h) m_h[h] = neg_inf();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) e_l[i] = 0.f;
-#pragma unroll
-  for (int hs = 0; hs < HS; ++hs)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if (t0 < t1) {
-    const uint8_t* mrow = p.mask ? p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages : nullptr;
-    const int32_t* trow = p.table + (size_t)s * p.max_pages;
-    const int spp = P / kSlab;
-    const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
-    const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB +
-                        (size_t)col * L::TOKB + (size_t)grp * 16;
-    const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
-
-    for (int base = it.lp0; base < it.lp1; base += kPageCap) {
-      const int nk = compact_pages(base, it.lp1, mrow, trow, s_phys, s_lp, s_cnt);
-      const int nslab = nk * spp;
-
-      auto load = [&](int sl, MFrag<D>& f) {
-        const int kp = sl / spp;
-        const int sub = sl - kp * spp;
-        const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
-        const int tb = s_lp[kp] * P + sub * kSlab;
-        if (tb >= t0 && tb + kSlab <= t1) {
-#pragma unroll
-          for (int st = 0; st < L::KS; ++st) f.k[st] = load_stream16(kbase + off + st * 64);
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) f.v[i] = load_stream16(vbase + off + i * 1024);
-        } else {
-          const int tk = tb + col;
-          const bool kok = tk >= t0 && tk < t1;
-#pragma unroll
-          for (int st = 0; st < L::KS; ++st)
-            f.k[st] = kok ? load_stream16(kbase + off + st * 64) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < L::NI; ++i) {
-            const int tv = tb + i * L::TPI + vrow;
-            f.v[i] = (tv >= t0 && tv < t1) ? load_stream16(vbase + off + i * 1024)
-                                           : make_uint4(0, 0, 0, 0);
-          }
-        }
-      };
-
-      auto compute = [&](int sl, const MFrag<D>& f, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        const int kp = sl / spp;
-        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
-
-        // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < L::KS; ++st)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
-                                                      __builtin_bit_cast(bf16x8_t, f.k[st]), sc,
-                                                      0, 0, 0);
-        const bool kvalid = FULL || (tb + col >= t0 && tb + col < t1);
-
-        // slab maxima per head, then the running maxima (wave-uniform)
-        float rm[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rm[i] = row_max16(kvalid ? sc[i] : neg_inf());
-        float alpha_h[G], nmc_h[G];
-        bool moved = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
-          const float mn = fmaxf(m_h[h], mx);
-          const float ms = (FULL || mn != neg_inf()) ? mn : 0.f;
-          alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
-          nmc_h[h] = -ms * c;
-          moved |= mn != m_h[h];
-          m_h[h] = mn;
-        }
-
-        // probabilities in the score layout; exp-sums per token column
-        float pw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hi = (i < G) ? i : 0;
-          float nmc = nmc_h[hi], al = alpha_h[hi];
-          if constexpr (G > 4) {
-            if (grp == 1) {
-              nmc = nmc_h[4 + i];
-              al = alpha_h[4 + i];
-            }
-          }
-          pw[i] = kvalid ? fast_exp2(fmaf(sc[i], c, nmc)) : 0.f;
-          e_l[i] = fmaf(e_l[i], al, pw[i]);
-        }
-
-        // probabilities to the value-product operand layout (per-wave LDS)
-        float* sp = s_p[wave];
-        if (grp < HS) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * grp + i < G) sp[col * G + 4 * grp + i] = pw[i];
-        }
-
-        if (moved) {
-#pragma unroll
-          for (int hs = 0; hs < HS; ++hs)
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
-        }
-
-        // value sums: acc[hs][k] += p[4hs + i][token] * v[token][dim k of this lane]
-#pragma unroll
-        for (int j = 0; j < L::NI; ++j) {
-          float pa[HS];
-#pragma unroll
-          for (int hs = 0; hs < HS; ++hs)
-            pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
-          const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float lo = bf16_lo(w4[k]);
-            const float hi = bf16_hi(w4[k]);
-#pragma unroll
-            for (int hs = 0; hs < HS; ++hs) {
-              acc[hs][2 * k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], lo, acc[hs][2 * k], 0, 0, 0);
-              acc[hs][2 * k + 1] =
-                  __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], hi, acc[hs][2 * k + 1], 0, 0, 0);
-            }
-          }
-        }
-      };
-
-      auto step = [&](int sl, const MFrag<D>& f) {
-        const int kp = sl / spp;
-        const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
-        if (tb >= t0 && tb + kSlab <= t1)
-          compute(sl, f, Bool<true>{});
-        else
-          compute(sl, f, Bool<false>{});
-      };
-
-      MFrag<D> fa, fb;
-      int sl = wave;
-      if (sl < nslab) load(sl, fa);
-      while (sl < nslab) {
-        int sn = sl + kMicroWaves;
-        if (sn < nslab) load(sn, fb);
-        step(sl, fa);
-        sl = sn;
-        if (sl >= nslab) break;
-        sn = sl + kMicroWaves;
-        if (sn < nslab) load(sn, fa);
-        step(sl, fb);
-        sl = sn;
+    // score operand A: lane l -> head l%16 (zero beyond G), dims chunk 4*step + l/16
+    uint4 qa[L::KS];
+  #pragma unroll
+    for (int st = 0; st < L::KS; ++st) {
+      qa[st] = make_uint4(0, 0, 0, 0);
+      if (col < G) {
+        const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * L::TOKB +
+                         (size_t)(4 * st + grp) * 16;
+        qa[st] = *reinterpret_cast<const uint4*>(qp);
       }
-      __syncthreads();  // the page list is rewritten by the next batch
     }
-  }
 
-  // ---- per-wave totals: exp-sums over token columns, values over token rows ----
-  float we[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = e_l[h & 3];
-    x = x + dpp<kDppQuadXor1>(x);
-    x = x + dpp<kDppQuadXor2>(x);
-    x = x + dpp<kDppHalfMirror>(x);
-    x = x + dpp<kDppRowMirror>(x);
-    we[h] = lane_value(x, 16 * (h >> 2));
-  }
-  float accg[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
-#pragma unroll
-  for (int off = L::LPT; off < kWave; off <<= 1)
-#pragma unroll
+    float m_h[G];        // running raw-dot maximum per head (wave-uniform)
+    float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
+    f32x4_t acc[HS][8];  // value sums: block layout, register i = head 4*hs + i
+  #pragma unroll
+    for (int h = 0; h < G; ++h) m_h[h] = neg_inf();
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) e_l[i] = 0.f;
+  #pragma unroll
+    for (int hs = 0; hs < HS; ++hs)
+  #pragma unroll
+      for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (it.scan0 < it.scan1) {
+      const int32_t* trow = p.table + (size_t)s * p.max_pages;
+      const int spp = P / kSlab;
+      const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+      const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB +
+                          (size_t)col * L::TOKB + (size_t)grp * 16;
+      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+
+      for (int base = it.scan0; base < it.scan1; base += kPageCap) {
+        const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
+        const int nslab = nk * spp;
+
+        auto load = [&](int sl, MFrag<D>& f) {
+          const int kp = sl / spp;
+          const int sub = sl - kp * spp;
+          const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
+          const int tb = s_lp[kp] * P + sub * kSlab;
+          if (tb >= t0 && tb + kSlab <= t1) {
+  #pragma unroll
+            for (int st = 0; st < L::KS; ++st) f.k[st] = load_stream16(kbase + off + st * 64);
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) f.v[i] = load_stream16(vbase + off + i * 1024);
+          } else {
+            const int tk = tb + col;
+            const bool kok = tk >= t0 && tk < t1;
+  #pragma unroll
+            for (int st = 0; st < L::KS; ++st)
+              f.k[st] = kok ? load_stream16(kbase + off + st * 64) : make_uint4(0, 0, 0, 0);
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
+              const int tv = tb + i * L::TPI + vrow;
+              f.v[i] = (tv >= t0 && tv < t1) ? load_stream16(vbase + off + i * 1024)
+                                             : make_uint4(0, 0, 0, 0);
+            }
+          }
+        };
+
+        auto compute = [&](int sl, const MFrag<D>& f, auto full_tag) {
+          constexpr bool FULL = decltype(full_tag)::value;
+          const int kp = sl / spp;
+          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+
+          // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
+          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int st = 0; st < L::KS; ++st)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                        __builtin_bit_cast(bf16x8_t, f.k[st]), sc,
+                                                        0, 0, 0);
+          const bool kvalid = FULL || (tb + col >= t0 && tb + col < t1);
+
+          // slab maxima per head, then the running maxima (wave-uniform)
+          float rm[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) rm[i] = row_max16(kvalid ? sc[i] : neg_inf());
+          float alpha_h[G], nmc_h[G];
+          bool moved = false;
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
+            const float mn = fmaxf(m_h[h], mx);
+            const float ms = (FULL || mn != neg_inf()) ? mn : 0.f;
+            alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
+            nmc_h[h] = -ms * c;
+            moved |= mn != m_h[h];
+            m_h[h] = mn;
+          }
+
+          // probabilities in the score layout; exp-sums per token column
+          float pw[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int hi = (i < G) ? i : 0;
+            float nmc = nmc_h[hi], al = alpha_h[hi];
+            if constexpr (G > 4) {
+              if (grp == 1) {
+                nmc = nmc_h[4 + i];
+                al = alpha_h[4 + i];
+              }
+            }
+            pw[i] = kvalid ? fast_exp2(fmaf(sc[i], c, nmc)) : 0.f;
+            e_l[i] = fmaf(e_l[i], al, pw[i]);
+          }
+
+          // probabilities to the value-product operand layout (per-wave LDS)
+          float* sp = s_p[wave];
+          if (grp < HS) {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * grp + i < G) sp[col * G + 4 * grp + i] = pw[i];
+          }
+
+          if (moved) {
+  #pragma unroll
+            for (int hs = 0; hs < HS; ++hs)
+  #pragma unroll
+              for (int k = 0; k < 8; ++k)
+  #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
+          }
+
+          // value sums: acc[hs][k] += p[4hs + i][token] * v[token][dim k of this lane]
+  #pragma unroll
+          for (int j = 0; j < L::NI; ++j) {
+            float pa[HS];
+  #pragma unroll
+            for (int hs = 0; hs < HS; ++hs)
+              pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
+            const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
+  #pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float lo = bf16_lo(w4[k]);
+              const float hi = bf16_hi(w4[k]);
+  #pragma unroll
+              for (int hs = 0; hs < HS; ++hs) {
+                acc[hs][2 * k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], lo, acc[hs][2 * k], 0, 0, 0);
+                acc[hs][2 * k + 1] =
+                    __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], hi, acc[hs][2 * k + 1], 0, 0, 0);
+              }
+            }
+          }
+        };
+
+        auto step = [&](int sl, const MFrag<D>& f) {
+          const int kp = sl / spp;
+          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+          if (tb >= t0 && tb + kSlab <= t1)
+            compute(sl, f, Bool<true>{});
+          else
+            compute(sl, f, Bool<false>{});
+        };
+
+        MFrag<D> fa, fb;
+        int sl = wave;
+        if (sl < nslab) load(sl, fa);
+        while (sl < nslab) {
+          int sn = sl + kMicroWaves;
+          if (sn < nslab) load(sn, fb);
+          step(sl, fa);
+          sl = sn;
+          if (sl >= nslab) break;
+          sn = sl + kMicroWaves;
+          if (sn < nslab) load(sn, fa);
+          step(sl, fb);
+          sl = sn;
+        }
+        __syncthreads();  // the page list is rewritten by the next batch
+      }
+    }
+
+    // ---- per-wave totals: exp-sums over token columns, values over token rows ----
+    float we[G];
+  #pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x = e_l[h & 3];
+      x = x + dpp<kDppQuadXor1>(x);
+      x = x + dpp<kDppQuadXor2>(x);
+      x = x + dpp<kDppHalfMirror>(x);
+      x = x + dpp<kDppRowMirror>(x);
+      we[h] = lane_value(x, 16 * (h >> 2));
+    }
+    float accg[G][8];
+  #pragma unroll
     for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) accg[h][k] += __shfl_xor(accg[h][k], off, kWave);
+  #pragma unroll
+      for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
+  #pragma unroll
+    for (int off = L::LPT; off < kWave; off <<= 1)
+  #pragma unroll
+      for (int h = 0; h < G; ++h)
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) accg[h][k] += __shfl_xor(accg[h][k], off, kWave);
 
-  finish_item<G, D, L::LPT, 8>(p, it, s_fin, m_h, we, accg, c);
+    finish_item<G, D, L::LPT, 8>(p, it, s_fin, m_h, we, accg, c);
+  });
 }
+
+// Resident workgroups per CU (measured best for the grouped-query workload).
+constexpr int kMfmaWorkgroupsPerCU = 2;
 
 template <int D, int G>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  const long long items = (long long)p.S * p.Hkv * p.max_splits * p.chunks;
-  hipLaunchKernelGGL((micro_mfma_kernel<D, G>), dim3((unsigned)items), dim3(kMicroThreads), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_micro_kernel(micro_mfma_kernel<D, G>, kMfmaWorkgroupsPerCU, p, stream);
 }
 
 template <int D>

@@ -13,18 +13,20 @@ constexpr int kMicroWaves = kMicroThreads / kWave;
 constexpr int kPageCap = 1024;  // kept pages staged in LDS per batch
 constexpr int kSlab = 16;       // tokens per slab
 
-// One work item: (request s, KV head kvh, split j, chunk c).  The chunk is a
-// contiguous range of the split's logical pages; its tokens are
-// [t0, t1) = split range intersected with the chunk's pages.
+// One work item: (request s, KV head kvh, split j, piece c).  A split is the
+// token range [t0, t1) (split bounds intersected with [0, L_s)) on logical
+// pages [pa, pb); piece c of `chunks` takes the logical pages
+// [scan0, scan1) = the c-th equal share of [pa, pb), and within them the
+// pages the block mask keeps.
 struct Item {
   int s, kvh, j, c;
-  int t0, t1;    // token range (empty if t0 >= t1)
-  int lp0, lp1;  // logical page range to scan
+  int t0, t1;        // split token range (empty if t0 >= t1)
+  int scan0, scan1;  // logical pages of this piece
+  const uint8_t* mrow;  // block-mask row of (s, kvh), or null
 };
 
-__device__ __forceinline__ Item decode_item(const MicroParams& p) {
+__device__ __forceinline__ Item plan_item(const MicroParams& p, int x) {
   Item it;
-  int x = blockIdx.x;
   it.c = x % p.chunks;
   x /= p.chunks;
   it.j = x % p.max_splits;
@@ -32,31 +34,58 @@ __device__ __forceinline__ Item decode_item(const MicroParams& p) {
   it.kvh = x % p.Hkv;
   it.s = x / p.Hkv;
   const int P = p.P;
+  it.mrow = p.mask ? p.mask + ((size_t)it.s * p.Hkv + it.kvh) * p.max_pages : nullptr;
   int Ls = p.lens[it.s];
   Ls = max(0, min(Ls, p.max_pages * P));
   const int32_t* sb = p.bounds + ((size_t)it.s * (p.bounds_per_head ? p.Hkv : 1) +
                                   (p.bounds_per_head ? it.kvh : 0)) *
                                      (size_t)(p.max_splits + 1);
-  int t0 = max(sb[it.j], 0);
-  int t1 = min(sb[it.j + 1], Ls);
-  if (t0 < t1) {
-    const int a = t0 / P, b = (t1 + P - 1) / P;  // split's pages
-    const int n = b - a;
-    const int ca = a + (int)(((long long)n * it.c) / p.chunks);
-    const int cb = a + (int)(((long long)n * (it.c + 1)) / p.chunks);
-    t0 = max(t0, ca * P);
-    t1 = min(t1, cb * P);
+  it.t0 = max(sb[it.j], 0);
+  it.t1 = min(sb[it.j + 1], Ls);
+  it.scan0 = it.scan1 = 0;
+  if (it.t0 < it.t1) {
+    const int pa = it.t0 / P, pb = (it.t1 + P - 1) / P;
+    const long long n = pb - pa;
+    it.scan0 = pa + (int)((n * it.c) / p.chunks);
+    it.scan1 = pa + (int)((n * (it.c + 1)) / p.chunks);
   }
-  it.t0 = t0;
-  it.t1 = t1;
-  it.lp0 = t0 < t1 ? t0 / P : 0;
-  it.lp1 = t0 < t1 ? (t1 + P - 1) / P : 0;
   return it;
+}
+
+// Runs body(x) for every work item x this workgroup owns: item blockIdx.x
+// for a one-per-item launch, or, for a persistent launch, items claimed from
+// p.queue `grab` at a time in increasing order until none are left.  The
+// next claim is issued before the current items are processed, so its
+// latency is hidden.  body may use LDS and barriers; every lane calls it with
+// the same x.
+template <class Body>
+__device__ __forceinline__ void for_each_item(const MicroParams& p, int* s_claim, Body&& body) {
+  if (p.queue == nullptr) {
+    body((int)blockIdx.x);
+    return;
+  }
+  const int tid = threadIdx.x;
+  if (tid == 0) *s_claim = atomicAdd(p.queue, p.grab);
+  __syncthreads();
+  int x0 = __builtin_amdgcn_readfirstlane(*s_claim);
+  while (x0 >= 0 && x0 < p.n_items) {  // a counter not reset to 0 ends the loop
+    int next = 0;
+    if (tid == 0) next = atomicAdd(p.queue, p.grab);
+    const int x1 = min(x0 + p.grab, p.n_items);
+    for (int x = x0; x < x1; ++x) {
+      body(x);
+      __syncthreads();  // the item's LDS (page list, combine) is free again
+    }
+    if (tid == 0) *s_claim = next;
+    __syncthreads();
+    x0 = __builtin_amdgcn_readfirstlane(*s_claim);
+  }
 }
 
 // Compacts the kept pages of [base, min(base + kPageCap, lp1)) into LDS
 // (physical page ids and logical page ids, in logical order) with wave
 // ballots; returns the count.  Every thread of the workgroup must call it.
+
 __device__ __forceinline__ int compact_pages(int base, int lp1, const uint8_t* mrow,
                                              const int32_t* trow, int* s_phys, int* s_lp,
                                              int* s_cnt) {
@@ -139,6 +168,70 @@ __device__ __forceinline__ void finish_item(const MicroParams& p, const Item& it
       p.e[o] = den;
     }
   }
+}
+
+// Dynamic LDS that caps a kernel at `wg` resident workgroups per CU (0 = no
+// cap): each workgroup is padded to just over 1/(wg+1) of the CU's LDS.  On
+// gfx950 fewer, deeper streams per CU read HBM faster than many shallow ones.
+inline size_t occupancy_lds(const void* kernel, int wg) {
+  if (wg <= 0) return 0;
+  int dev = 0, per_cu = 0, per_block = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return 0;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return 0;
+  const size_t want = ((size_t)per_cu / (wg + 1) / 1024 + 1) * 1024;  // > per_cu / (wg + 1)
+  if (want * wg > (size_t)per_cu || want > (size_t)per_block || want <= attr.sharedSizeBytes)
+    return 0;
+  return want - attr.sharedSizeBytes;
+}
+
+// Workgroups of `kernel` that fit on the device at once with `lds` bytes of
+// dynamic LDS each (the grid of a persistent launch).
+inline int resident_slots(const void* kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMicroThreads, lds) !=
+          hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+// A grid this many times larger than the resident slots goes persistent.
+constexpr long long kPersistentFactor = 8;
+
+// Launches a MicroAttention kernel.  Normally one workgroup per item: the
+// hardware dispatcher keeps the slots full.  When the grid is far larger
+// than the resident slots (many small or empty items, as in ragged batches)
+// and p.queue provides a counter, the in-order, XCD-round-robin dispatch
+// itself becomes the bottleneck; then the launch is persistent: one
+// workgroup per resident slot, each claiming items from the counter in
+// batches small enough that the tail stays short.
+template <class Kernel>
+hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  const size_t lds = occupancy_lds(fn, wg_per_cu);
+  long long grid = p.n_items;
+  if (p.queue != nullptr) {
+    const int slots = resident_slots(fn, lds);
+    const bool go = p.schedule == 2 || (p.schedule == 0 && p.n_items > kPersistentFactor * slots);
+    if (slots > 0 && go) {
+      const hipError_t err = launch_queue_reset(p.queue, stream);
+      if (err != hipSuccess) return err;
+      grid = slots;
+      const long long per = (long long)p.n_items / ((long long)slots * 16);
+      p.grab = (int)(per < 1 ? 1 : (per > 64 ? 64 : per));
+    } else {
+      p.queue = nullptr;
+    }
+  }
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kMicroThreads), lds, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace da

@@ -19,10 +19,11 @@ from long_context_decode_microattention_amd import workloads as wl
 TOL_OUT = {wl.F32: 1e-5, wl.BF16: 2e-3}
 
 
-def run_gpu(batch: wl.Batch, chunks: int = 0):
+def run_gpu(batch: wl.Batch, chunks: int = 0, workspace=None, schedule: int = 0):
     MA, m, e = _lib.micro_attention(batch.q, batch.k_pages, batch.v_pages, batch.block_table,
                                     batch.seq_lens, batch.split_bounds, batch.block_mask,
-                                    scale=batch.scale, chunks=chunks)
+                                    scale=batch.scale, chunks=chunks, workspace=workspace,
+                                    schedule=schedule)
     out = _lib.merge(MA, m, e)
     torch.cuda.synchronize()
     return out, MA, m, e

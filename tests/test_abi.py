@@ -30,7 +30,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 def good_shape(**kw):
     base = dict(S=2, Hq=8, Hkv=2, D=128, P=16, max_pages=4, max_splits=2, bounds_per_head=0,
-                dtype=_lib.DA_BF16, scale=0.088, NP=8, chunks=0)
+                dtype=_lib.DA_BF16, scale=0.088, NP=8, chunks=0, schedule=0)
     base.update(kw)
     return _lib.DaShape(**base)
 
@@ -65,6 +65,9 @@ def call_micro(lib, sh, **ptrs):
     (dict(shape=dict(chunks=65)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(chunks=4)), _lib.DA_ERR_INVALID_ARG),  # forced chunks, no workspace
     (dict(shape=dict(chunks=4), ptrs=dict(ws=FAKE, ws_bytes=16)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(ws=FAKE + 4, ws_bytes=64)), _lib.DA_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(shape=dict(schedule=3)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(schedule=2)), _lib.DA_ERR_INVALID_ARG),  # persistent, no workspace
     (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
     (dict(shape=dict(P=24)), _lib.DA_ERR_UNSUPPORTED),
     (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
@@ -84,16 +87,16 @@ def test_workspace_size(lib):
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
     chunks = 2  # 128 items -> 2048 / 128 = 16 chunks (capped at 16)
     assert n.value > 0
-    # many items: no chunks, no workspace
+    # many items: no chunks; only the 16-byte work-queue counter
     sh = good_shape(S=64, Hq=40, Hkv=40, max_pages=2048, max_splits=16, P=16)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
-    assert n.value == 0
-    # forced chunks: exactly the three chunk arrays, 16-byte aligned each
+    assert n.value == 16
+    # forced chunks: the counter and the three chunk arrays, 16-byte aligned each
     sh = good_shape(S=2, Hq=8, Hkv=2, D=128, max_splits=3, chunks=5)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
     rows = 2 * 8 * 3 * 5
     align = lambda x: (x + 15) // 16 * 16
-    assert n.value == align(rows * 128 * 4) + 2 * align(rows * 4)
+    assert n.value == 16 + align(rows * 128 * 4) + 2 * align(rows * 4)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), None) == _lib.DA_ERR_INVALID_ARG
     del chunks
 

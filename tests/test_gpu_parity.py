@@ -74,6 +74,55 @@ def test_forced_chunks_parity(cfg, chunks):
                      f"{cfg} chunks={chunks} partials")
 
 
+@pytest.mark.parametrize("chunks", [0, 3])
+@pytest.mark.parametrize("cfg", sorted(REDUCED))
+def test_persistent_schedule_parity(cfg, chunks):
+    """Persistent workgroups claiming items from the work queue (forced)."""
+    spec = REDUCED[cfg]
+    announce("persistent", cfg, chunks)
+    b = wl.build(spec, 9, DEV)
+    out, MA, m, e = run_gpu(b, chunks=chunks, schedule=2)
+    inp = host_inputs(b)
+    tol = TOL_OUT[spec.dtype]
+    compare_out(out.cpu().numpy(), oracle_out(inp, b.scale), tol, f"{cfg} persistent")
+    oMA, om, oe = oracle_micro(inp, b.scale)
+    compare_partials(MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy(), oMA, om, oe, tol,
+                     f"{cfg} persistent partials")
+
+
+@pytest.mark.parametrize("cfg", sorted(REDUCED))
+def test_one_workgroup_per_item_parity(cfg):
+    """Without a workspace the launch is one workgroup per item (no work
+    queue, no chunks): same results within tolerance."""
+    spec = REDUCED[cfg]
+    announce("no-workspace", cfg)
+    b = wl.build(spec, 6, DEV)
+    out, MA, m, e = run_gpu(b, workspace=False)
+    inp = host_inputs(b)
+    tol = TOL_OUT[spec.dtype]
+    compare_out(out.cpu().numpy(), oracle_out(inp, b.scale), tol, f"{cfg} no workspace")
+    oMA, om, oe = oracle_micro(inp, b.scale)
+    compare_partials(MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy(), oMA, om, oe, tol,
+                     f"{cfg} no workspace partials")
+
+
+def test_work_queue_reused_across_calls():
+    """The persistent launch's counter is reset on the stream before every
+    call: repeated calls on one workspace, with shapes that change between
+    them, keep giving the same results."""
+    announce("queue-reuse")
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    batches = [wl.build(REDUCED[c], 8, DEV) for c in ("C3", "C5", "C2")]
+    first = []
+    for b in batches:
+        first.append(run_gpu(b, workspace=ws, schedule=2)[0].clone())
+    for _ in range(2):
+        for b, ref in zip(batches, first):
+            assert torch.equal(run_gpu(b, workspace=ws, schedule=2)[0], ref)
+    ref3 = oracle_out(host_inputs(batches[0]), batches[0].scale)
+    compare_out(first[0].cpu().numpy(), ref3, 2e-3, "queue reuse C3")
+
+
 # Full-size workloads: outputs sampled at (request, KV-head range) units the
 # oracle computes one by one.
 FULL_SAMPLES = {
@@ -151,21 +200,22 @@ def _fill_pool_from_logical(b: wl.Batch, values: np.ndarray, target: torch.Tenso
     target.copy_(host.to(target.dtype))
 
 
+@pytest.mark.parametrize("schedule", [1, 2])
 @pytest.mark.parametrize("chunks", [0, 5])
 @pytest.mark.parametrize("cfg", ["C1", "C3", "C5"])
-def test_fingerprint_counts_bit_exact(cfg, chunks):
+def test_fingerprint_counts_bit_exact(cfg, chunks, schedule):
     """q = 0 makes every weight exp(0) = 1: m_j = 0, e_j = kept-token count and
     MA_j[c] = number of kept tokens whose fingerprint has bit c set -- exact
     integers, compared bitwise with numpy counts."""
     spec = REDUCED[cfg].replace(S=min(REDUCED[cfg].S, 3))
-    announce("fingerprint", cfg, chunks)
+    announce("fingerprint", cfg, chunks, schedule)
     b = wl.build(spec, 5, DEV)
     b.q.zero_()
     sp = b.spec
     L = int(b.seq_lens.max().item())
     bits = fingerprint(sp.S, sp.Hkv, L, sp.D)
     _fill_pool_from_logical(b, bits, b.v_pages)
-    _, MA, m, e = run_gpu(b, chunks=chunks)
+    _, MA, m, e = run_gpu(b, chunks=chunks, schedule=schedule)
     MA, m, e = MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy()
     lens = b.seq_lens.cpu().numpy()
     sb = b.split_bounds.cpu().numpy()
