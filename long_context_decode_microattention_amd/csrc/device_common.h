@@ -19,11 +19,18 @@ constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8-lane half row
 constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i inside each 16-lane row
 
+// Every permutation used here reads a lane of the same row, so the "old"
+// operand is never selected; passing the source itself saves a zeroed
+// register per call.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  const int xi = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(xi, xi, CTRL, 0xF, 0xF, false));
 }
+
+// True in every lane if `c` holds in any lane (a scalar, wave-uniform value:
+// branches on it skip code instead of masking it).
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 // Sum over aligned groups of N consecutive lanes (N = 8, 16 or 32); every
 // lane of the group receives the group total.  After the two quad steps each

@@ -214,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
               if (4 * grp + i < G) sp[col * G + 4 * grp + i] = pw[i];
           }
 
-          if (moved) {
+          if (wave_any(moved)) {  // scalar branch: skipped, not masked
   #pragma unroll
             for (int hs = 0; hs < HS; ++hs)
   #pragma unroll
