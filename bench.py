@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-selector", action="store_true",
+                    help="skip the page-selection timing on the block-sparse workload")
     return ap.parse_args()
 
 
@@ -126,6 +128,121 @@ def time_workload(key, steps, warmup, dev):
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
     return b, res
+
+
+def time_selector(b, steps, warmup, dev, logical=16):
+    """Page selection on a block-sparse workload's own pool: statistics of
+    every (page, KV head) once (the prefill-time cost), then per step the
+    page scores of the KV heads the workload masks and the top-K mask with
+    the workload's own budget (the same kept count as its seeded mask),
+    followed by the attention step over the selected pages."""
+    import numpy as np
+    import torch
+
+    from long_context_decode_microattention_amd import _lib
+
+    sp = b.spec
+    _, keep_first, keep_last, frac = sp.mask
+    Hkv, P, D = sp.Hkv, sp.P, sp.D
+    flags = torch.tensor([1 if h >= Hkv // 2 else 0 for h in range(Hkv)], dtype=torch.uint8,
+                         device=dev)
+    n_sel = int(flags.sum().item())
+    npg = sp.max_pages
+    budget = int(frac * (npg - keep_first - keep_last))
+    esize = sp.esize
+    NL = P // logical
+    stats = torch.zeros((b.k_pages.shape[0], Hkv, NL, 2, D), dtype=b.k_pages.dtype, device=dev)
+    scores = torch.empty((sp.S, Hkv, npg), dtype=torch.float32, device=dev)
+    mask = torch.empty((sp.S, Hkv, npg), dtype=torch.uint8, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    # statistics over the whole pool (all KV heads), timed
+    for _ in range(max(1, warmup)):
+        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical, out=stats)
+    reps = max(3, steps // 4)
+    s0, s1 = ev(), ev()
+    s0.record()
+    for _ in range(reps):
+        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical, out=stats)
+    s1.record()
+    torch.cuda.synchronize()
+    us_stats = s0.elapsed_time(s1) * 1e3 / reps
+    kept_tokens = int(b.seq_lens.sum().item()) * Hkv
+    stats_bytes = kept_tokens * D * esize + sp.S * npg * Hkv * NL * 2 * D * esize
+
+    def select():
+        _lib.page_scores(b.q, stats, b.block_table, b.seq_lens, P=P, select_heads=flags, out=scores)
+
+    def topk():
+        _lib.select_pages(scores, b.seq_lens, P=P, budget=budget, keep_first=keep_first,
+                          keep_last=keep_last, select_heads=flags, out=mask)
+
+    for _ in range(warmup):
+        select()
+        topk()
+    torch.cuda.synchronize()
+    evs = [ev() for _ in range(3 * steps)]
+    for i in range(steps):
+        evs[3 * i].record()
+        select()
+        evs[3 * i + 1].record()
+        topk()
+        evs[3 * i + 2].record()
+    torch.cuda.synchronize()
+    us_scores = sum(evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(steps)) * 1e3 / steps
+    us_topk = sum(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(steps)) * 1e3 / steps
+    # bytes the score kernel must move: the statistics of the selected KV
+    # heads' pages below L_s, plus one fp32 score per (request, KV head, page)
+    score_bytes = sp.S * n_sel * npg * NL * 2 * D * esize + sp.S * Hkv * npg * 4
+
+    # attention over the selected pages: splits over each head's kept pages
+    mask_h = mask.cpu().numpy()
+    lens = b.seq_lens.cpu().numpy()
+    nb = b.max_splits
+    sb = np.zeros((sp.S, Hkv, nb + 1), dtype=np.int32)
+    kept = 0
+    for s in range(sp.S):
+        n = -(-int(lens[s]) // P)
+        for h in range(Hkv):
+            kp = np.nonzero(mask_h[s, h, :n])[0]
+            kept += int(np.minimum((kp + 1) * P, lens[s]).sum() - (kp * P).sum())
+            for j in range(1, nb):
+                sb[s, h, j] = int(kp[(j * len(kp)) // nb]) * P
+            sb[s, h, nb] = int(lens[s])
+    sb_t = torch.from_numpy(sb).to(dev)
+    MA = torch.empty((sp.S, sp.Hq, nb, D), dtype=torch.float32, device=dev)
+    m = torch.empty((sp.S, sp.Hq, nb), dtype=torch.float32, device=dev)
+    e = torch.empty_like(m)
+    out = torch.empty((sp.S, sp.Hq, D), dtype=torch.float32, device=dev)
+
+    def step():
+        select()
+        topk()
+        _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, sb_t, mask,
+                             scale=b.scale, out=(MA, m, e))
+        _lib.merge(MA, m, e, out=out)
+
+    for _ in range(warmup):
+        step()
+    t0, t1 = ev(), ev()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    us_step = t0.elapsed_time(t1) * 1e3 / steps
+    kv_bytes = kept * 2 * D * esize
+    return dict(
+        kernel="page_scores_kernel (da_page_scores)", logical_page=logical, selected_kv_heads=n_sel,
+        budget=budget, keep_first=keep_first, keep_last=keep_last,
+        us_page_scores=us_scores, us_select_topk=us_topk,
+        score_bytes=score_bytes, score_GBps=score_bytes / (us_scores * 1e-6) / 1e9,
+        roofline_frac=score_bytes / (us_scores * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        us_page_stats=us_stats, stats_bytes=stats_bytes,
+        stats_GBps=stats_bytes / (us_stats * 1e-6) / 1e9,
+        us_step_with_selection=us_step, kv_bytes_selected=kv_bytes,
+        step_GBps_kv_only=kv_bytes / (us_step * 1e-6) / 1e9,
+    )
 
 
 def read_ceiling(b):
@@ -215,6 +332,8 @@ def main():
         r2["roofline_frac"] = r2["micro_GBps"] / HBM_PEAK_GBPS
         r2["traffic"] = measured_traffic(key)
         secondary[key] = r2
+        if b2.spec.mask is not None and not a.no_selector:
+            secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
         del b2
         torch.cuda.empty_cache()
 

@@ -160,6 +160,57 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
 da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
                           const int32_t* seq_lens, int32_t* err, hipStream_t stream);
 
+/*
+ * Hierarchical page selection for retrieval heads (LServe blog page, section
+ * 2.2.2 "解码阶段创新": a physical page of P tokens holds logical pages of
+ * `logical` tokens, each with per-dimension key statistics k_max / k_min,
+ * and the important physical pages are picked from the query; section 3.1.2
+ * "动态稀疏的层次化选择": statistics per logical page, a score per physical
+ * page as the maximum over its logical pages, the top-K pages kept).  The
+ * result is the block mask da_micro_attention consumes.
+ *
+ * Supported: dtype F32 or BF16 (q, K and the statistics share it), D 64 or
+ * 128, G = Hq / Hkv in {1, 2, 4, 8}, logical in {8, 16, 32, 64} with
+ * P / logical a power of two; anything else returns DA_ERR_UNSUPPORTED.
+ * The calls read sh->S, Hq, Hkv, D, P, NP, max_pages and dtype only.
+ *
+ * da_page_stats: stats [NP, Hkv, P / logical, 2, D] (dtype, 16-byte
+ *   aligned, caller-owned): for every physical page that block_table names
+ *   below ceil(L_s / P), and every KV head and logical sub-page, index 0 =
+ *   the per-dimension maximum and index 1 = the per-dimension minimum of the
+ *   keys of the sub-page's tokens below L_s (exact: the stored values
+ *   themselves).  A sub-page with no token below L_s gets zeros.  Pages no
+ *   table row names are not written.  k_pages as for da_micro_attention.
+ *
+ * da_page_scores: scores [S, Hkv, max_pages] fp32 (4-byte aligned): for
+ *   page lp < ceil(L_s / P) of request s and KV head kvh, the maximum over
+ *   the group's query heads h (h / G == kvh) and over the logical sub-pages
+ *   holding a token below L_s of the bound
+ *       sum_d max(q_h[d] * kmax[d], q_h[d] * kmin[d])   (>= q_h . k for
+ *   every key k of the sub-page), accumulated in fp32; -inf for pages at or
+ *   beyond ceil(L_s / P), and for every page of a KV head whose entry in
+ *   select_heads (device uint8 [Hkv], nullable = all heads) is 0.  The
+ *   scores are raw bounds: no attention scale (it does not change the order).
+ *
+ * da_select_pages: block_mask [S, Hkv, max_pages] uint8 (caller-owned,
+ *   every entry written): for a KV head with select_heads[kvh] != 0 (or
+ *   select_heads NULL) the first keep_first and the last keep_last pages
+ *   below ceil(L_s / P) are 1, and of the pages between them the `budget`
+ *   with the highest score are 1 (equal scores: lower page index first;
+ *   -0.0 equals 0.0); a KV head with select_heads[kvh] == 0 keeps every page
+ *   below ceil(L_s / P); pages at or beyond it are 0.  budget, keep_first
+ *   and keep_last must be >= 0.  Scores must not be NaN.
+ */
+da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t logical, void* stats,
+                        hipStream_t stream);
+da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t logical,
+                         const uint8_t* select_heads, float* scores, hipStream_t stream);
+da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t* seq_lens,
+                          int32_t budget, int32_t keep_first, int32_t keep_last,
+                          const uint8_t* select_heads, uint8_t* block_mask, hipStream_t stream);
+
 /* Message for the last non-OK status returned on the calling thread
  * (thread-local; never NULL; empty if none). */
 const char* da_last_error(void);

@@ -76,6 +76,13 @@ def load() -> ctypes.CDLL:
     lib.da_check_inputs.restype = ctypes.c_int
     lib.da_last_error.argtypes = []
     lib.da_last_error.restype = ctypes.c_char_p
+    lib.da_page_stats.argtypes = [sp, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    lib.da_page_stats.restype = ctypes.c_int
+    lib.da_page_scores.argtypes = [sp, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP]
+    lib.da_page_scores.restype = ctypes.c_int
+    lib.da_select_pages.argtypes = [sp, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _VP, _VP, _VP]
+    lib.da_select_pages.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
     lib.da_stream_read_sink_words.argtypes = []
@@ -229,6 +236,94 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
     MA, m, e = micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds,
                                block_mask, scale=scale, chunks=chunks)
     return merge(MA, m, e)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DA_F32
+    if t.dtype == torch.bfloat16:
+        return DA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, dtype) -> DaShape:
+    return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=max_pages, max_splits=1,
+                   bounds_per_head=0, dtype=dtype, scale=1.0, NP=NP)
+
+
+def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, out=None):
+    """Per-logical-page key maxima and minima [NP, Hkv, P // logical, 2, D]
+    (dtype of k_pages) via da_page_stats.  Pages that no table row names
+    below L_s are left as they are in ``out`` (zeros when it is allocated
+    here)."""
+    dev = k_pages.device
+    _need(k_pages, "k_pages", None, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    NP, Hkv, P, D = k_pages.shape
+    if P % logical:
+        raise ValueError(f"logical={logical} does not divide P={P}")
+    if out is None:
+        out = torch.zeros((NP, Hkv, P // logical, 2, D), dtype=k_pages.dtype, device=dev)
+    else:
+        _need(out, "out", k_pages.dtype, dev, 5)
+        if tuple(out.shape) != (NP, Hkv, P // logical, 2, D):
+            raise ValueError("out must be [NP, Hkv, P // logical, 2, D]")
+    sh = _selector_shape(block_table.shape[0], Hkv, Hkv, D, P, NP, block_table.shape[1],
+                         _dtype_code(k_pages))
+    _check(load().da_page_stats(ctypes.byref(sh), _ptr(k_pages), _ptr(block_table), _ptr(seq_lens),
+                                int(logical), _ptr(out), _stream(dev)))
+    return out
+
+
+def page_scores(q, stats, block_table, seq_lens, *, P: int, select_heads=None, out=None):
+    """Physical-page scores [S, Hkv, max_pages] float32 via da_page_scores:
+    the largest statistics bound over the group's query heads and the
+    page's logical pages; -inf past L_s and for unselected KV heads."""
+    dev = q.device
+    _need(q, "q", None, dev, 3)
+    _need(stats, "stats", q.dtype, dev, 5)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    if select_heads is not None:
+        _need(select_heads, "select_heads", torch.uint8, dev, 1)
+    S, Hq, D = q.shape
+    NP, Hkv, NL, two, D2 = stats.shape
+    if two != 2 or D2 != D or P % NL:
+        raise ValueError("stats must be [NP, Hkv, P // logical, 2, D]")
+    if select_heads is not None and select_heads.shape[0] != Hkv:
+        raise ValueError("select_heads must have Hkv entries")
+    max_pages = block_table.shape[1]
+    if out is None:
+        out = torch.empty((S, Hkv, max_pages), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, 3)
+    sh = _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, _dtype_code(q))
+    _check(load().da_page_scores(ctypes.byref(sh), _ptr(q), _ptr(stats), _ptr(block_table),
+                                 _ptr(seq_lens), int(P // NL), _ptr(select_heads), _ptr(out),
+                                 _stream(dev)))
+    return out
+
+
+def select_pages(scores, seq_lens, *, P: int, budget: int, keep_first: int = 0,
+                 keep_last: int = 0, select_heads=None, out=None):
+    """Block mask [S, Hkv, max_pages] uint8 via da_select_pages: forced first
+    and last pages plus the ``budget`` best-scoring others."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev, 3)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    if select_heads is not None:
+        _need(select_heads, "select_heads", torch.uint8, dev, 1)
+    S, Hkv, max_pages = scores.shape
+    if out is None:
+        out = torch.empty((S, Hkv, max_pages), dtype=torch.uint8, device=dev)
+    else:
+        _need(out, "out", torch.uint8, dev, 3)
+    sh = _selector_shape(S, Hkv, Hkv, 1, P, 1, max_pages, DA_F32)
+    _check(load().da_select_pages(ctypes.byref(sh), _ptr(scores), _ptr(seq_lens), int(budget),
+                                  int(keep_first), int(keep_last), _ptr(select_heads), _ptr(out),
+                                  _stream(dev)))
+    return out
 
 
 def check_inputs(block_table, seq_lens, NP: int, P: int) -> int:

@@ -98,6 +98,42 @@ WsLayout ws_layout(const da_shape* sh, int chunks) {
   return w;
 }
 
+// Shape checks of the page-selection entry points.
+da_status check_selector(const da_shape* sh, int logical) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 ||
+      sh->NP < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hq=%d Hkv=%d D=%d P=%d max_pages=%d NP=%lld)",
+                sh->S, sh->Hq, sh->Hkv, sh->D, sh->P, sh->max_pages, (long long)sh->NP);
+  if (sh->Hq % sh->Hkv != 0)
+    return fail(DA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", sh->Hq, sh->Hkv);
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
+    return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if (sh->NP > (long long)INT_MAX + 1)
+    return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
+  if ((long long)sh->S * sh->max_pages > INT_MAX ||
+      da::score_launch_items(sh->S, sh->Hkv, sh->max_pages) > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * max_pages exceeds the launch range");
+  if (!da::selector_supported(sh->dtype, sh->D, sh->Hq / sh->Hkv, sh->P, logical))
+    return fail(DA_ERR_UNSUPPORTED,
+                "page selection not built for dtype=%d D=%d G=%d P=%d logical=%d", sh->dtype,
+                sh->D, sh->Hq / sh->Hkv, sh->P, logical);
+  return DA_OK;
+}
+
+da::SelectorParams selector_params(const da_shape* sh, int logical) {
+  da::SelectorParams p{};
+  p.S = sh->S;
+  p.Hq = sh->Hq;
+  p.Hkv = sh->Hkv;
+  p.P = sh->P;
+  p.max_pages = sh->max_pages;
+  p.logical = logical;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,6 +256,79 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
   const hipError_t e2 = da::launch_check_inputs(block_table, seq_lens, sh->S, sh->P, sh->max_pages,
                                                 sh->NP, err, stream);
   if (e2 != hipSuccess) return fail(DA_ERR_HIP, "check launch failed: %s", hipGetErrorString(e2));
+  return DA_OK;
+}
+
+da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t logical, void* stats,
+                        hipStream_t stream) {
+  da_status st = check_selector(sh, logical);
+  if (st != DA_OK) return st;
+  if (!k_pages || !block_table || !seq_lens || !stats)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_pages, 16) || !aligned(stats, 16))
+    return fail(DA_ERR_INVALID_ARG, "k_pages and stats must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  da::SelectorParams p = selector_params(sh, logical);
+  p.k = k_pages;
+  p.stats = stats;
+  p.table = block_table;
+  p.lens = seq_lens;
+  const hipError_t err = da::launch_page_stats(p, sh->dtype, sh->D, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "page-stats launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t logical,
+                         const uint8_t* select_heads, float* scores, hipStream_t stream) {
+  da_status st = check_selector(sh, logical);
+  if (st != DA_OK) return st;
+  if (!q || !stats || !block_table || !seq_lens || !scores)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(stats, 16))
+    return fail(DA_ERR_INVALID_ARG, "q and stats must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(scores, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
+  da::SelectorParams p = selector_params(sh, logical);
+  p.q = q;
+  p.stats = const_cast<void*>(stats);
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.select = select_heads;
+  p.scores = scores;
+  const hipError_t err = da::launch_page_scores(p, sh->dtype, sh->D, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "page-score launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t* seq_lens,
+                          int32_t budget, int32_t keep_first, int32_t keep_last,
+                          const uint8_t* select_heads, uint8_t* block_mask, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d)", sh->S,
+                sh->Hkv, sh->P, sh->max_pages);
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->S * sh->Hkv > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
+  if (budget < 0 || keep_first < 0 || keep_last < 0)
+    return fail(DA_ERR_INVALID_ARG, "budget, keep_first and keep_last must be >= 0");
+  if (!scores || !seq_lens || !block_mask) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(scores, 4) || !aligned(seq_lens, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
+  da::SelectorParams p = selector_params(sh, 0);
+  p.scores = const_cast<float*>(scores);
+  p.lens = seq_lens;
+  p.select = select_heads;
+  p.mask = block_mask;
+  p.budget = budget;
+  p.keep_first = keep_first;
+  p.keep_last = keep_last;
+  const hipError_t err = da::launch_select_pages(p, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "page-select launch failed: %s", hipGetErrorString(err));
   return DA_OK;
 }
 

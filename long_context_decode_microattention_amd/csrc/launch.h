@@ -56,6 +56,25 @@ hipError_t launch_merge(const float* MA, const float* m, const float* e, float* 
 hipError_t launch_check_inputs(const int32_t* table, const int32_t* lens, int S, int P,
                                int max_pages, int64_t NP, int32_t* err, hipStream_t stream);
 
+// Page selection (selector.hip).
+struct SelectorParams {
+  const void* q;      // [S, Hq, D]
+  const void* k;      // [NP, Hkv, P, D]
+  void* stats;        // [NP, Hkv, P / logical, 2, D]
+  const int32_t* table;
+  const int32_t* lens;
+  const uint8_t* select;  // [Hkv] or null
+  float* scores;      // [S, Hkv, max_pages]
+  uint8_t* mask;      // [S, Hkv, max_pages]
+  int S, Hq, Hkv, P, max_pages, logical;
+  int budget, keep_first, keep_last;
+};
+bool selector_supported(int dtype, int D, int G, int P, int logical);
+hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStream_t stream);
+hipError_t launch_page_scores(const SelectorParams& p, int dtype, int D, hipStream_t stream);
+hipError_t launch_select_pages(const SelectorParams& p, hipStream_t stream);
+long long score_launch_items(int S, int Hkv, int max_pages);
+
 int stream_read_grid();
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 

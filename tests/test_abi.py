@@ -127,3 +127,63 @@ def test_binding_refuses_cpu_tensors():
         _lib.micro_attention(q, torch.zeros(2, 4, 16, 64), torch.zeros(2, 4, 16, 64),
                              torch.zeros(1, 2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
                              torch.zeros(1, 1, 2, dtype=torch.int64))
+
+
+def _vp(x):
+    return None if x is None else ctypes.c_void_p(x)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(S=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(Hq=6, Hkv=4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(dtype=5)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),  # G = 3
+    (dict(logical=12), _lib.DA_ERR_UNSUPPORTED),
+    (dict(logical=32), _lib.DA_ERR_UNSUPPORTED),  # larger than P = 16
+    (dict(shape=dict(P=48), logical=16), _lib.DA_ERR_UNSUPPORTED),  # P / logical = 3
+    (dict(ptrs=dict(k=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(stats=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_page_stats_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(k=FAKE, table=FAKE, lens=FAKE, stats=FAKE)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_page_stats(ctypes.byref(sh), _vp(p["k"]), _vp(p["table"]), _vp(p["lens"]),
+                            case.get("logical", 16), _vp(p["stats"]), None)
+    assert got == status, _lib.load().da_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(NP=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(logical=4), _lib.DA_ERR_UNSUPPORTED),
+    (dict(ptrs=dict(q=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(q=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(scores=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_page_scores_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(q=FAKE, stats=FAKE, table=FAKE, lens=FAKE, sel=None, scores=FAKE)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_page_scores(ctypes.byref(sh), _vp(p["q"]), _vp(p["stats"]), _vp(p["table"]),
+                             _vp(p["lens"]), case.get("logical", 16), _vp(p["sel"]),
+                             _vp(p["scores"]), None)
+    assert got == status, _lib.load().da_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(Hkv=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(-1, 0, 0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(4, -2, 0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(4, 0, -1)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(mask=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(scores=FAKE + 1)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_select_pages_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(scores=FAKE, lens=FAKE, sel=None, mask=FAKE)
+    p.update(case.get("ptrs", {}))
+    budget, kf, kl = case.get("args", (4, 1, 1))
+    got = lib.da_select_pages(ctypes.byref(sh), _vp(p["scores"]), _vp(p["lens"]), budget, kf, kl,
+                              _vp(p["sel"]), _vp(p["mask"]), None)
+    assert got == status, _lib.load().da_last_error()
