@@ -132,7 +132,7 @@ def time_workload(key, steps, warmup, dev):
 
 def time_selector(b, steps, warmup, dev, logical=16):
     """Page selection on a block-sparse workload's own pool: statistics of
-    every (page, KV head) once (the prefill-time cost), then per step the
+    every page of the KV heads it masks, once (the prefill-time cost), then per step the
     page scores of the KV heads the workload masks and the top-K mask with
     the workload's own budget (the same kept count as its seeded mask),
     followed by the attention step over the selected pages."""
@@ -156,19 +156,22 @@ def time_selector(b, steps, warmup, dev, logical=16):
     mask = torch.empty((sp.S, Hkv, npg), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    # statistics over the whole pool (all KV heads), timed
+    # statistics of the selected KV heads over the whole pool, timed
     for _ in range(max(1, warmup)):
-        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical, out=stats)
+        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
+                        select_heads=flags, out=stats)
     reps = max(3, steps // 4)
     s0, s1 = ev(), ev()
     s0.record()
     for _ in range(reps):
-        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical, out=stats)
+        _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
+                        select_heads=flags, out=stats)
     s1.record()
     torch.cuda.synchronize()
     us_stats = s0.elapsed_time(s1) * 1e3 / reps
-    kept_tokens = int(b.seq_lens.sum().item()) * Hkv
-    stats_bytes = kept_tokens * D * esize + sp.S * npg * Hkv * NL * 2 * D * esize
+    # every key row of a selected head read once, its statistics written once
+    key_rows = int(b.seq_lens.sum().item()) * n_sel
+    stats_bytes = key_rows * D * esize + sp.S * npg * n_sel * NL * 2 * D * esize
 
     def select():
         _lib.page_scores(b.q, stats, b.block_table, b.seq_lens, P=P, select_heads=flags, out=scores)

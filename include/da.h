@@ -171,8 +171,10 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  *
  * Supported: dtype F32 or BF16 (q, K and the statistics share it), D 64 or
  * 128, G = Hq / Hkv in {1, 2, 4, 8}, logical in {8, 16, 32, 64} with
- * P / logical a power of two; anything else returns DA_ERR_UNSUPPORTED.
- * The calls read sh->S, Hq, Hkv, D, P, NP, max_pages and dtype only.
+ * P / logical a power of two no larger than 256; da_select_pages also needs
+ * max_pages <= 65536.  Anything else returns DA_ERR_UNSUPPORTED.  The calls
+ * read sh->S, Hq, Hkv, D, P, NP, max_pages and dtype only.  select_heads is
+ * a device uint8 [Hkv] array of retrieval-head flags, nullable = every head.
  *
  * da_page_stats: stats [NP, Hkv, P / logical, 2, D] (dtype, 16-byte
  *   aligned, caller-owned): for every physical page that block_table names
@@ -180,7 +182,10 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  *   the per-dimension maximum and index 1 = the per-dimension minimum of the
  *   keys of the sub-page's tokens below L_s (exact: the stored values
  *   themselves).  A sub-page with no token below L_s gets zeros.  Pages no
- *   table row names are not written.  k_pages as for da_micro_attention.
+ *   table row names, and KV heads whose select_heads entry is 0, are not
+ *   written.  k_pages as for da_micro_attention.  A physical page named by
+ *   two table rows with different token counts on it gets either row's
+ *   statistics.
  *
  * da_page_scores: scores [S, Hkv, max_pages] fp32 (4-byte aligned): for
  *   page lp < ceil(L_s / P) of request s and KV head kvh, the maximum over
@@ -189,7 +194,7 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  *       sum_d max(q_h[d] * kmax[d], q_h[d] * kmin[d])   (>= q_h . k for
  *   every key k of the sub-page), accumulated in fp32; -inf for pages at or
  *   beyond ceil(L_s / P), and for every page of a KV head whose entry in
- *   select_heads (device uint8 [Hkv], nullable = all heads) is 0.  The
+ *   select_heads is 0.  The
  *   scores are raw bounds: no attention scale (it does not change the order).
  *
  * da_select_pages: block_mask [S, Hkv, max_pages] uint8 (caller-owned,
@@ -202,8 +207,8 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  *   and keep_last must be >= 0.  Scores must not be NaN.
  */
 da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
-                        const int32_t* seq_lens, int32_t logical, void* stats,
-                        hipStream_t stream);
+                        const int32_t* seq_lens, int32_t logical, const uint8_t* select_heads,
+                        void* stats, hipStream_t stream);
 da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t logical,
                          const uint8_t* select_heads, float* scores, hipStream_t stream);

@@ -76,7 +76,7 @@ def load() -> ctypes.CDLL:
     lib.da_check_inputs.restype = ctypes.c_int
     lib.da_last_error.argtypes = []
     lib.da_last_error.restype = ctypes.c_char_p
-    lib.da_page_stats.argtypes = [sp, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    lib.da_page_stats.argtypes = [sp, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP]
     lib.da_page_stats.restype = ctypes.c_int
     lib.da_page_scores.argtypes = [sp, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP]
     lib.da_page_scores.restype = ctypes.c_int
@@ -251,16 +251,21 @@ def _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, dtype) -> DaShape:
                    bounds_per_head=0, dtype=dtype, scale=1.0, NP=NP)
 
 
-def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, out=None):
+def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_heads=None,
+               out=None):
     """Per-logical-page key maxima and minima [NP, Hkv, P // logical, 2, D]
     (dtype of k_pages) via da_page_stats.  Pages that no table row names
-    below L_s are left as they are in ``out`` (zeros when it is allocated
-    here)."""
+    below L_s, and KV heads whose select_heads flag is 0, are left as they
+    are in ``out`` (zeros when it is allocated here)."""
     dev = k_pages.device
     _need(k_pages, "k_pages", None, dev, 4)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     NP, Hkv, P, D = k_pages.shape
+    if select_heads is not None:
+        _need(select_heads, "select_heads", torch.uint8, dev, 1)
+        if select_heads.shape[0] != Hkv:
+            raise ValueError("select_heads must have Hkv entries")
     if P % logical:
         raise ValueError(f"logical={logical} does not divide P={P}")
     if out is None:
@@ -272,7 +277,7 @@ def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, out=None):
     sh = _selector_shape(block_table.shape[0], Hkv, Hkv, D, P, NP, block_table.shape[1],
                          _dtype_code(k_pages))
     _check(load().da_page_stats(ctypes.byref(sh), _ptr(k_pages), _ptr(block_table), _ptr(seq_lens),
-                                int(logical), _ptr(out), _stream(dev)))
+                                int(logical), _ptr(select_heads), _ptr(out), _stream(dev)))
     return out
 
 
@@ -315,6 +320,8 @@ def select_pages(scores, seq_lens, *, P: int, budget: int, keep_first: int = 0,
     if select_heads is not None:
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
     S, Hkv, max_pages = scores.shape
+    if select_heads is not None and select_heads.shape[0] != Hkv:
+        raise ValueError("select_heads must have Hkv entries")
     if out is None:
         out = torch.empty((S, Hkv, max_pages), dtype=torch.uint8, device=dev)
     else:

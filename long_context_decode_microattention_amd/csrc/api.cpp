@@ -113,13 +113,13 @@ da_status check_selector(const da_shape* sh, int logical) {
     return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
   if (sh->NP > (long long)INT_MAX + 1)
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
-  if ((long long)sh->S * sh->max_pages > INT_MAX ||
-      da::score_launch_items(sh->S, sh->Hkv, sh->max_pages) > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "S * max_pages exceeds the launch range");
   if (!da::selector_supported(sh->dtype, sh->D, sh->Hq / sh->Hkv, sh->P, logical))
     return fail(DA_ERR_UNSUPPORTED,
                 "page selection not built for dtype=%d D=%d G=%d P=%d logical=%d", sh->dtype,
                 sh->D, sh->Hq / sh->Hkv, sh->P, logical);
+  if ((long long)sh->S * sh->max_pages > INT_MAX ||
+      da::score_launch_items(sh->S, sh->Hkv, sh->max_pages, sh->P, logical) > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * max_pages exceeds the launch range");
   return DA_OK;
 }
 
@@ -260,8 +260,8 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
 }
 
 da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
-                        const int32_t* seq_lens, int32_t logical, void* stats,
-                        hipStream_t stream) {
+                        const int32_t* seq_lens, int32_t logical, const uint8_t* select_heads,
+                        void* stats, hipStream_t stream) {
   da_status st = check_selector(sh, logical);
   if (st != DA_OK) return st;
   if (!k_pages || !block_table || !seq_lens || !stats)
@@ -275,6 +275,7 @@ da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* 
   p.stats = stats;
   p.table = block_table;
   p.lens = seq_lens;
+  p.select = select_heads;
   const hipError_t err = da::launch_page_stats(p, sh->dtype, sh->D, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "page-stats launch failed: %s", hipGetErrorString(err));
   return DA_OK;
@@ -314,6 +315,9 @@ da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t
     return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
+  if (sh->max_pages > da::select_max_pages())
+    return fail(DA_ERR_UNSUPPORTED, "top-K selection is built for max_pages <= %d (got %d)",
+                da::select_max_pages(), sh->max_pages);
   if (budget < 0 || keep_first < 0 || keep_last < 0)
     return fail(DA_ERR_INVALID_ARG, "budget, keep_first and keep_last must be >= 0");
   if (!scores || !seq_lens || !block_mask) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");

@@ -73,7 +73,8 @@ bool selector_supported(int dtype, int D, int G, int P, int logical);
 hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_page_scores(const SelectorParams& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_select_pages(const SelectorParams& p, hipStream_t stream);
-long long score_launch_items(int S, int Hkv, int max_pages);
+long long score_launch_items(int S, int Hkv, int max_pages, int P, int logical);
+int select_max_pages();
 
 int stream_read_grid();
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -6,20 +6,27 @@
 // pages, of the bound those statistics put on q . k; the top-K physical pages
 // become the block mask the MicroAttention kernels consume.
 //
-// Three kernels:
+// Three kernels, all streaming (HBM-bound or latency-bound, no dense
+// contraction):
 //   page_stats_kernel   K pool -> statistics pool [NP, Hkv, P/logical, 2, D]
 //                       (same element type as K; max/min of stored values are
-//                       stored values, so bf16 statistics are exact).
+//                       stored values, so bf16 statistics are exact).  A lane
+//                       owns 16 bytes of one (KV head, logical page) column
+//                       and folds every row of it, 16 rows in flight, so no
+//                       cross-lane reduction is needed.
 //   page_scores_kernel  statistics + q -> score per (request, KV head, page).
 //                       Per dimension the bound picks kmax where q_d >= 0 and
 //                       kmin where q_d < 0 (one bit-select per element), then
 //                       a dot product: sum_d max(q_d kmax_d, q_d kmin_d); the
-//                       maximum over the group's query heads and over the
-//                       valid logical pages of the physical page.
+//                       maximum over the group's query heads, then (through
+//                       LDS) over the valid logical pages of a physical page.
 //   select_pages_kernel scores -> uint8 mask: forced first/last pages plus the
-//                       `budget` best others, by a most-significant-digit-first
-//                       radix select over order-preserving integer keys, equal
-//                       keys going to the lower page index.
+//                       `budget` best others.  Keys (order-preserving integer
+//                       images of the scores) stay in registers; the K-th
+//                       largest key is found one bit at a time from the top
+//                       by counting keys at or above a candidate (ballots,
+//                       one barrier per bit); equal keys go to the lower page
+//                       index through one block-wide prefix count.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,9 +35,11 @@ namespace {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kScorePagesPerItem = 64;  // physical pages per score workgroup
+constexpr int kStatsUnroll = 16;           // rows of one column in flight per lane
+constexpr int kScoreLogicalPerItem = 256;  // logical pages per score workgroup
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kTopkMaxKeys = 64;           // keys per thread: up to 65536 candidates
 
 // Element layout of one D-wide row: each lane holds 16 bytes of it.
 template <int DT, int D>
@@ -83,17 +92,24 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int s, int max_tok
   return max(0, min(lens[s], max_tokens));
 }
 
+__device__ __forceinline__ bool head_selected(const uint8_t* select, int kvh) {
+  return select == nullptr || select[kvh] != 0;
+}
+
 // ---------------------------------------------------------------------------
 // statistics
 // ---------------------------------------------------------------------------
 
-// One workgroup per (request, logical page index) of the table; its waves
-// take the (KV head, logical sub-page) pairs of the physical page in turn.
-// A wave folds the sub-page's valid rows per lane (RPW rows per load), then
-// across the rows of the wave; row 0 stores kmax, row 1 kmin.
+// One workgroup per (request, logical page index) of the table.  The page's
+// (KV head, logical sub-page) columns are numbered t = kvh * NL + sub, which
+// is also their order in the pool: column t starts t * logical rows into the
+// physical page, and its statistics t * 2 rows into the page's statistics.
+// A wave job covers TPW consecutive columns (one 16-byte slice per lane), so
+// each of its loads reads TPW contiguous row segments.
 template <int DT, int D>
 __global__ __launch_bounds__(kSelThreads) void page_stats_kernel(SelectorParams p) {
   using R = Row<DT, D>;
+  constexpr int TPW = kWave / R::LPR;
   const int s = blockIdx.x / p.max_pages;
   const int lp = blockIdx.x - s * p.max_pages;
   const int L = clamp_len(p.lens, s, p.max_pages * p.P);
@@ -101,50 +117,56 @@ __global__ __launch_bounds__(kSelThreads) void page_stats_kernel(SelectorParams 
   const long long phys = p.table[(size_t)s * p.max_pages + lp];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int row = lane / R::LPR;
-  const int col = lane - row * R::LPR;
+  const int tsk = lane / R::LPR;
+  const int col = lane - tsk * R::LPR;
   const int NL = p.P / p.logical;
   const int tasks = p.Hkv * NL;
-  for (int t = wave; t < tasks; t += kSelWaves) {
-    const int kvh = t / NL;
-    const int sub = t - kvh * NL;
-    const int slot0 = sub * p.logical;
-    const char* base = static_cast<const char*>(p.k) +
-                       ((size_t)phys * p.Hkv + kvh) * p.P * R::RB + (size_t)col * 16;
+  const char* page = static_cast<const char*>(p.k) + (size_t)phys * p.Hkv * p.P * R::RB +
+                     (size_t)col * 16;
+  char* spage = static_cast<char*>(p.stats) + (size_t)phys * tasks * 2 * R::RB + (size_t)col * 16;
+
+  for (int t0 = wave * TPW; t0 < tasks; t0 += kSelWaves * TPW) {
+    const int t = t0 + tsk;
+    bool write = false;
+    int nv = 0;  // rows of this column below L
+    if (t < tasks) {
+      const int kvh = t / NL;
+      write = head_selected(p.select, kvh);
+      if (write) nv = max(0, min(p.logical, L - (lp * p.P + (t - kvh * NL) * p.logical)));
+    }
+    const char* src = page + (size_t)t * p.logical * R::RB;
     float hi[R::EPL], lo[R::EPL];
 #pragma unroll
     for (int i = 0; i < R::EPL; ++i) {
       hi[i] = neg_inf();
       lo[i] = -neg_inf();
     }
-    for (int r = row; r < p.logical; r += R::RPW) {
-      const int slot = slot0 + r;
-      if (lp * p.P + slot < L) {
-        float x[R::EPL];
-        unpack<DT>(load_stream16(base + (size_t)slot * R::RB), x);
+    for (int r0 = 0; r0 < nv; r0 += kStatsUnroll) {
+      uint4 w[kStatsUnroll];
 #pragma unroll
-        for (int i = 0; i < R::EPL; ++i) {
-          hi[i] = fmaxf(hi[i], x[i]);
-          lo[i] = fminf(lo[i], x[i]);
+      for (int u = 0; u < kStatsUnroll; ++u)
+        w[u] = r0 + u < nv ? load_stream16(src + (size_t)(r0 + u) * R::RB) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kStatsUnroll; ++u) {
+        if (r0 + u < nv) {
+          float x[R::EPL];
+          unpack<DT>(w[u], x);
+#pragma unroll
+          for (int i = 0; i < R::EPL; ++i) {
+            hi[i] = fmaxf(hi[i], x[i]);
+            lo[i] = fminf(lo[i], x[i]);
+          }
         }
       }
     }
+    if (write) {
+      if (nv == 0) {
 #pragma unroll
-    for (int off = R::LPR; off < kWave; off <<= 1) {
-#pragma unroll
-      for (int i = 0; i < R::EPL; ++i) {
-        hi[i] = fmaxf(hi[i], __shfl_xor(hi[i], off, kWave));
-        lo[i] = fminf(lo[i], __shfl_xor(lo[i], off, kWave));
+        for (int i = 0; i < R::EPL; ++i) hi[i] = lo[i] = 0.f;
       }
-    }
-    if (row < 2) {
-      const bool any = lp * p.P + slot0 < L;
-      float v[R::EPL];
-#pragma unroll
-      for (int i = 0; i < R::EPL; ++i) v[i] = any ? (row == 0 ? hi[i] : lo[i]) : 0.f;
-      char* out = static_cast<char*>(p.stats) +
-                  ((((size_t)phys * p.Hkv + kvh) * NL + sub) * 2 + row) * R::RB + (size_t)col * 16;
-      *reinterpret_cast<uint4*>(out) = pack<DT>(v);
+      char* dst = spage + (size_t)t * 2 * R::RB;
+      *reinterpret_cast<uint4*>(dst) = pack<DT>(hi);
+      *reinterpret_cast<uint4*>(dst + R::RB) = pack<DT>(lo);
     }
   }
 }
@@ -187,34 +209,48 @@ __device__ __forceinline__ float bound_part(const uint4& kmax, const uint4& kmin
   return acc;
 }
 
-// One workgroup per (request, KV head, run of kScorePagesPerItem pages).  A
-// wave step covers RPW logical pages (one per row of LPR lanes): PPS whole
-// physical pages when a physical page has fewer logical pages than a wave
-// has rows, else one physical page over SPP steps.
+// Physical pages per score workgroup for NL logical pages per physical page.
+__host__ __device__ __forceinline__ int score_pages_per_item(int NL) {
+  return kScoreLogicalPerItem / NL;
+}
+
+// One workgroup per (request, KV head, run of kScoreLogicalPerItem logical
+// pages).  The run's block-table entries are staged in LDS first; each wave
+// load then covers RPW logical pages (one per row of LPR lanes), U loads of
+// kmax and kmin in flight per lane; the per-logical-page bounds go to LDS and
+// are folded per physical page at the end.
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kSelThreads) void page_scores_kernel(SelectorParams p) {
   using R = Row<DT, D>;
-  const int runs = (p.max_pages + kScorePagesPerItem - 1) / kScorePagesPerItem;
+  constexpr int U = G >= 8 ? 4 : 8;
+  __shared__ int s_phys[kScoreLogicalPerItem];
+  __shared__ float s_bound[kScoreLogicalPerItem];
+  const int NL = p.P / p.logical;
+  const int nl_shift = __builtin_ctz(NL);
+  const int ppi = score_pages_per_item(NL);
+  const int runs = (p.max_pages + ppi - 1) / ppi;
   int x = blockIdx.x;
   const int run = x % runs;
   x /= runs;
   const int kvh = x % p.Hkv;
   const int s = x / p.Hkv;
-  const int lp0 = run * kScorePagesPerItem;
-  const int lp1 = min(lp0 + kScorePagesPerItem, p.max_pages);
+  const int lp0 = run * ppi;
+  const int lp1 = min(lp0 + ppi, p.max_pages);
   float* out = p.scores + ((size_t)s * p.Hkv + kvh) * p.max_pages;
   const int tid = threadIdx.x;
-  if (p.select != nullptr && p.select[kvh] == 0) {
+  const int L = clamp_len(p.lens, s, p.max_pages * p.P);
+  const int lpv = min(lp1, (L + p.P - 1) / p.P);  // end of the run's pages below L
+  if (!head_selected(p.select, kvh) || lpv <= lp0) {
     for (int lp = lp0 + tid; lp < lp1; lp += kSelThreads) out[lp] = neg_inf();
     return;
   }
-  const int L = clamp_len(p.lens, s, p.max_pages * p.P);
-  const int npg = (L + p.P - 1) / p.P;
+  for (int i = tid; i < lpv - lp0; i += kSelThreads)
+    s_phys[i] = p.table[(size_t)s * p.max_pages + lp0 + i];
+
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int row = lane / R::LPR;
   const int col = lane - row * R::LPR;
-
   uint4 qv[G], qm[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -222,38 +258,43 @@ __global__ __launch_bounds__(kSelThreads) void page_scores_kernel(SelectorParams
                    ((size_t)s * p.Hq + (size_t)kvh * G + g) * R::RB + (size_t)col * 16);
     qm[g] = sign_select<DT>(qv[g]);
   }
+  __syncthreads();
 
-  const int NL = p.P / p.logical;
-  const int rows_per_page = min(NL, R::RPW);  // rows of one page within a step
-  const int PPS = R::RPW / rows_per_page;     // physical pages per step
-  const int SPP = NL / rows_per_page;         // steps per physical page
-  const int rowpage = row / rows_per_page;
-  const int rowsub = row - rowpage * rows_per_page;
-  const size_t head_stride = (size_t)NL * 2 * R::RB;  // one (page, KV head) of statistics
-
-  for (int pg = lp0 + wave * PPS; pg < lp1; pg += kSelWaves * PPS) {
-    const int lp = pg + rowpage;
-    const bool pvalid = lp < lp1 && lp < npg;
-    const long long phys = pvalid ? p.table[(size_t)s * p.max_pages + lp] : 0;
-    const char* st = static_cast<const char*>(p.stats) + ((size_t)phys * p.Hkv + kvh) * head_stride +
-                     (size_t)col * 16;
-    float best = neg_inf();
-    for (int step = 0; step < SPP; ++step) {
-      const int sub = rowsub + step * rows_per_page;
-      const bool valid = pvalid && lp * p.P + sub * p.logical < L;
-      uint4 kmax = make_uint4(0, 0, 0, 0), kmin = make_uint4(0, 0, 0, 0);
-      if (valid) {
-        kmax = load16(st + (size_t)sub * 2 * R::RB);
-        kmin = load16(st + (size_t)sub * 2 * R::RB + R::RB);
+  const int nlog = (lpv - lp0) << nl_shift;
+  const char* st = static_cast<const char*>(p.stats) + (size_t)kvh * NL * 2 * R::RB + (size_t)col * 16;
+  const size_t page_stride = (size_t)p.Hkv * NL * 2 * R::RB;
+  for (int base = wave * R::RPW * U; base < nlog; base += kSelWaves * R::RPW * U) {
+    uint4 kmax[U], kmin[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int li = base + u * R::RPW + row;
+      const int pl = li >> nl_shift;
+      const int sub = li & (NL - 1);
+      valid[u] = li < nlog && (lp0 + pl) * p.P + sub * p.logical < L;
+      kmax[u] = kmin[u] = make_uint4(0, 0, 0, 0);
+      if (valid[u]) {
+        const char* src = st + (size_t)s_phys[pl] * page_stride + (size_t)sub * 2 * R::RB;
+        kmax[u] = load_stream16(src);
+        kmin[u] = load_stream16(src + R::RB);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       float h = neg_inf();
 #pragma unroll
-      for (int g = 0; g < G; ++g) h = fmaxf(h, group_sum<R::LPR>(bound_part<DT>(kmax, kmin, qv[g], qm[g])));
-      if (valid) best = fmaxf(best, h);
+      for (int g = 0; g < G; ++g)
+        h = fmaxf(h, group_sum<R::LPR>(bound_part<DT>(kmax[u], kmin[u], qv[g], qm[g])));
+      const int li = base + u * R::RPW + row;
+      if (col == 0 && li < nlog) s_bound[li] = valid[u] ? h : neg_inf();
     }
-    for (int off = R::LPR; off < R::LPR * rows_per_page; off <<= 1)
-      best = fmaxf(best, __shfl_xor(best, off, kWave));
-    if (col == 0 && rowsub == 0 && lp < lp1) out[lp] = best;
+  }
+  __syncthreads();
+  for (int i = tid; i < lp1 - lp0; i += kSelThreads) {
+    float best = neg_inf();
+    if (lp0 + i < lpv)
+      for (int sub = 0; sub < NL; ++sub) best = fmaxf(best, s_bound[(i << nl_shift) + sub]);
+    out[lp0 + i] = best;
   }
 }
 
@@ -262,17 +303,29 @@ __global__ __launch_bounds__(kSelThreads) void page_scores_kernel(SelectorParams
 // ---------------------------------------------------------------------------
 
 // Unsigned key with the order of the float (negative zero taken as zero).
+// Every non-NaN float maps above 0, which therefore marks an empty slot.
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One workgroup per (request, KV head).
+// Number of keys >= c (gt = false) or > c (gt = true) over the wave.
+template <int KPT>
+__device__ __forceinline__ int wave_count(const uint32_t (&key)[KPT], uint32_t c, bool gt) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) n += __popcll(__ballot(gt ? key[j] > c : key[j] >= c));
+  return n;
+}
+
+// One workgroup per (request, KV head).  Thread t owns candidates
+// lo + t*KPT ... lo + t*KPT + KPT - 1, so thread order is page order.
+template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void select_pages_kernel(SelectorParams p) {
-  __shared__ int s_hist[256];
-  __shared__ int s_need, s_digit;
-  __shared__ int s_wcnt[kTopkWaves];
+  __shared__ int s_cnt[2][kTopkWaves];
+  __shared__ int s_eq[kTopkWaves];
+  __shared__ int s_gt[kTopkWaves];
   const int s = blockIdx.x / p.Hkv;
   const int kvh = blockIdx.x - s * p.Hkv;
   const int tid = threadIdx.x;
@@ -283,7 +336,7 @@ __global__ __launch_bounds__(kTopkThreads) void select_pages_kernel(SelectorPara
   const float* sc = p.scores + ((size_t)s * p.Hkv + kvh) * p.max_pages;
   uint8_t* mrow = p.mask + ((size_t)s * p.Hkv + kvh) * p.max_pages;
 
-  const bool selected = p.select == nullptr || p.select[kvh] != 0;
+  const bool selected = head_selected(p.select, kvh);
   const int lo = selected ? min(p.keep_first, npg) : npg;
   const int hi = selected ? max(npg - p.keep_last, lo) : npg;
   // pages outside [lo, hi) are forced (below npg) or zero (at or beyond npg)
@@ -297,50 +350,52 @@ __global__ __launch_bounds__(kTopkThreads) void select_pages_kernel(SelectorPara
     return;
   }
 
-  // the budget-th largest key, one 8-bit digit at a time from the top
-  uint32_t prefix = 0, pmask = 0;
-  int need = p.budget;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTopkThreads) s_hist[i] = 0;
-    __syncthreads();
-    for (int i = lo + tid; i < hi; i += kTopkThreads) {
-      const uint32_t k = order_key(sc[i]);
-      if ((k & pmask) == prefix) atomicAdd(&s_hist[(k >> shift) & 0xFFu], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // keys matching the prefix number at least `need`, so the scan stops
-      int cum = 0, d = 255;
-      while (d > 0 && cum + s_hist[d] < need) cum += s_hist[d--];
-      s_need = need - cum;
-      s_digit = d;
-    }
-    __syncthreads();
-    need = s_need;
-    prefix |= (uint32_t)s_digit << shift;
-    pmask |= 0xFFu << shift;
-    __syncthreads();  // s_hist is cleared again by the next digit
+  const int first = lo + tid * KPT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = first + j < hi ? order_key(sc[first + j]) : 0u;
+
+  // the largest T with #{key >= T} >= budget, i.e. the budget-th largest key
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    const int c = wave_count<KPT>(key, cand, false);
+    if (lane == 0) s_cnt[bit & 1][wave] = c;
+    __syncthreads();  // s_cnt[bit & 1] is written again two bits later, after the next barrier
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) tot += s_cnt[bit & 1][w];
+    if (tot >= p.budget) T = cand;
   }
 
-  // keep keys above the threshold and the first `need` equal ones
-  int base = 0;
-  for (int c0 = lo; c0 < hi; c0 += kTopkThreads) {
-    const int i = c0 + tid;
-    const bool in = i < hi;
-    const uint32_t k = in ? order_key(sc[i]) : 0u;
-    const bool eq = in && k == prefix;
-    const uint64_t bal = __ballot(eq);
-    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = base, tot = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      if (w < wave) off += s_wcnt[w];
-      tot += s_wcnt[w];
+  // keys above T are kept; of the keys equal to T the first `need` in page order
+  int eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) eq += key[j] == T ? 1 : 0;
+  int incl = eq;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  const int gt = wave_count<KPT>(key, T, true);
+  if (lane == kWave - 1) s_eq[wave] = incl;
+  if (lane == 0) s_gt[wave] = gt;
+  __syncthreads();
+  int before = incl - eq, total_gt = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    if (w < wave) before += s_eq[w];
+    total_gt += s_gt[w];
+  }
+  const int need = p.budget - total_gt;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (first + j < hi) {
+      bool keep = key[j] > T;
+      if (key[j] == T) keep = before++ < need;
+      mrow[first + j] = keep ? 1 : 0;
     }
-    if (in) mrow[i] = (k > prefix || (eq && off + pre < need)) ? 1 : 0;
-    base += tot;
-    __syncthreads();
   }
 }
 
@@ -363,8 +418,12 @@ bool selector_supported(int dtype, int D, int G, int P, int logical) {
   if (D != 64 && D != 128) return false;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (logical != 8 && logical != 16 && logical != 32 && logical != 64) return false;
-  return P >= logical && P % logical == 0 && ((P / logical) & (P / logical - 1)) == 0;
+  if (P < logical || P % logical != 0) return false;
+  const int NL = P / logical;
+  return (NL & (NL - 1)) == 0 && NL <= kScoreLogicalPerItem;
 }
+
+int select_max_pages() { return kTopkThreads * kTopkMaxKeys; }
 
 hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStream_t stream) {
   const long long grid = (long long)p.S * p.max_pages;
@@ -378,10 +437,14 @@ hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStrea
   return hipGetLastError();
 }
 
+long long score_launch_items(int S, int Hkv, int max_pages, int P, int logical) {
+  const int ppi = score_pages_per_item(P / logical);
+  return (long long)S * Hkv * ((max_pages + ppi - 1) / ppi);
+}
+
 hipError_t launch_page_scores(const SelectorParams& p, int dtype, int D, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  const long long runs = (p.max_pages + kScorePagesPerItem - 1) / kScorePagesPerItem;
-  const long long grid = (long long)p.S * p.Hkv * runs;
+  const long long grid = score_launch_items(p.S, p.Hkv, p.max_pages, p.P, p.logical);
   if (grid < 1) return hipSuccess;
   const dim3 g((unsigned)grid);
   if (dtype == 0) return D == 64 ? scores_g<0, 64>(G, p, g, stream) : scores_g<0, 128>(G, p, g, stream);
@@ -391,12 +454,17 @@ hipError_t launch_page_scores(const SelectorParams& p, int dtype, int D, hipStre
 hipError_t launch_select_pages(const SelectorParams& p, hipStream_t stream) {
   const long long grid = (long long)p.S * p.Hkv;
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL(select_pages_kernel, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, p);
+  const dim3 g((unsigned)grid), b(kTopkThreads);
+  const int need = (p.max_pages + kTopkThreads - 1) / kTopkThreads;  // keys per thread
+  if (need <= 1) hipLaunchKernelGGL(select_pages_kernel<1>, g, b, 0, stream, p);
+  else if (need <= 2) hipLaunchKernelGGL(select_pages_kernel<2>, g, b, 0, stream, p);
+  else if (need <= 4) hipLaunchKernelGGL(select_pages_kernel<4>, g, b, 0, stream, p);
+  else if (need <= 8) hipLaunchKernelGGL(select_pages_kernel<8>, g, b, 0, stream, p);
+  else if (need <= 16) hipLaunchKernelGGL(select_pages_kernel<16>, g, b, 0, stream, p);
+  else if (need <= 32) hipLaunchKernelGGL(select_pages_kernel<32>, g, b, 0, stream, p);
+  else if (need <= kTopkMaxKeys) hipLaunchKernelGGL(select_pages_kernel<kTopkMaxKeys>, g, b, 0, stream, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
-}
-
-long long score_launch_items(int S, int Hkv, int max_pages) {
-  return (long long)S * Hkv * ((max_pages + kScorePagesPerItem - 1) / kScorePagesPerItem);
 }
 
 }  // namespace da

@@ -142,6 +142,7 @@ def _vp(x):
     (dict(logical=12), _lib.DA_ERR_UNSUPPORTED),
     (dict(logical=32), _lib.DA_ERR_UNSUPPORTED),  # larger than P = 16
     (dict(shape=dict(P=48), logical=16), _lib.DA_ERR_UNSUPPORTED),  # P / logical = 3
+    (dict(shape=dict(P=4096), logical=8), _lib.DA_ERR_UNSUPPORTED),  # P / logical = 512
     (dict(ptrs=dict(k=None)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(stats=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
 ])
@@ -150,7 +151,7 @@ def test_page_stats_rejects(lib, case, status):
     p = dict(k=FAKE, table=FAKE, lens=FAKE, stats=FAKE)
     p.update(case.get("ptrs", {}))
     got = lib.da_page_stats(ctypes.byref(sh), _vp(p["k"]), _vp(p["table"]), _vp(p["lens"]),
-                            case.get("logical", 16), _vp(p["stats"]), None)
+                            case.get("logical", 16), None, _vp(p["stats"]), None)
     assert got == status, _lib.load().da_last_error()
 
 
@@ -178,6 +179,7 @@ def test_page_scores_rejects(lib, case, status):
     (dict(args=(4, 0, -1)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(mask=None)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(scores=FAKE + 1)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(max_pages=65537, P=16)), _lib.DA_ERR_UNSUPPORTED),
 ])
 def test_select_pages_rejects(lib, case, status):
     sh = good_shape(**case.get("shape", {}))

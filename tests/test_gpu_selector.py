@@ -127,10 +127,18 @@ def _run_case(name, spec, logical, seed):
     table, lens = h(b.block_table), h(b.seq_lens)
 
     stats = _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical)
+    upper = _select_flags("upper", Hkv)
+    stats_upper = _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
+                                  select_heads=torch.from_numpy(upper).to(DEV))
     torch.cuda.synchronize()
     want_stats = osel.page_stats(h(b.k_pages), table, lens, logical=logical)
     got_stats = oracle.to_f64(h(stats))
     assert np.array_equal(got_stats, want_stats), f"{name}: statistics differ"
+    # heads with flag 0 are not written (the output was allocated as zeros)
+    got_upper = oracle.to_f64(h(stats_upper))
+    on = upper.astype(bool)
+    assert np.array_equal(got_upper[:, on], want_stats[:, on]), f"{name}: selected-head statistics"
+    assert not np.any(got_upper[:, ~on]), f"{name}: statistics written for an unselected head"
 
     tol = _score_tolerance(h(b.q), want_stats, table, lens, P, logical, D)
     q_host = h(b.q)
@@ -167,7 +175,7 @@ def test_selector_parity(name, seed):
     _run_case(name, spec, logical, seed)
 
 
-@pytest.mark.parametrize("max_pages", [5, 1000, 1024, 1025, 8192 + 77])
+@pytest.mark.parametrize("max_pages", [5, 1000, 1024, 1025, 2049, 8192 + 77, 32768 + 1, 65536])
 @pytest.mark.parametrize("kind", ["ties", "continuous", "signed_zero"])
 def test_select_pages_direct(max_pages, kind):
     """da_select_pages on seeded score arrays: heavy ties, continuous values,
