@@ -151,7 +151,7 @@ def time_selector(b, steps, warmup, dev, logical=16):
     budget = int(frac * (npg - keep_first - keep_last))
     esize = sp.esize
     NL = P // logical
-    stats = torch.zeros((b.k_pages.shape[0], Hkv, NL, 2, D), dtype=b.k_pages.dtype, device=dev)
+    stats = torch.zeros((Hkv, b.k_pages.shape[0], NL, 2, D), dtype=b.k_pages.dtype, device=dev)
     scores = torch.empty((sp.S, Hkv, npg), dtype=torch.float32, device=dev)
     mask = torch.empty((sp.S, Hkv, npg), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -327,6 +327,9 @@ def main():
     b, head = time_workload(a.workload, a.steps, a.warmup, dev)
     ceiling = None if a.no_ceiling else read_ceiling(b)
     cpu = None if a.no_cpu_baseline else cpu_baseline(b, a.cpu_budget)
+    head_selector = None
+    if b.spec.mask is not None and not a.no_selector:
+        head_selector = time_selector(b, a.steps, a.warmup, dev)
     del b
     torch.cuda.empty_cache()
     secondary = {}
@@ -372,6 +375,8 @@ def main():
         "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "frac_of_read_ceiling": None if ceiling is None else round(head["GBps"] / ceiling, 4),
         "cpu_baseline": cpu,
+        "selector": None if head_selector is None else
+        {k: (round(v, 4) if isinstance(v, float) else v) for k, v in head_selector.items()},
         "secondary": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                       for k, r in secondary.items()},
     }

@@ -176,8 +176,9 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  * read sh->S, Hq, Hkv, D, P, NP, max_pages and dtype only.  select_heads is
  * a device uint8 [Hkv] array of retrieval-head flags, nullable = every head.
  *
- * da_page_stats: stats [NP, Hkv, P / logical, 2, D] (dtype, 16-byte
- *   aligned, caller-owned): for every physical page that block_table names
+ * da_page_stats: stats [Hkv, NP, P / logical, 2, D] (dtype, 16-byte
+ *   aligned, caller-owned; head-major, so one KV head's statistics are one
+ *   contiguous run): for every physical page that block_table names
  *   below ceil(L_s / P), and every KV head and logical sub-page, index 0 =
  *   the per-dimension maximum and index 1 = the per-dimension minimum of the
  *   keys of the sub-page's tokens below L_s (exact: the stored values

@@ -253,8 +253,8 @@ def _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, dtype) -> DaShape:
 
 def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_heads=None,
                out=None):
-    """Per-logical-page key maxima and minima [NP, Hkv, P // logical, 2, D]
-    (dtype of k_pages) via da_page_stats.  Pages that no table row names
+    """Per-logical-page key maxima and minima [Hkv, NP, P // logical, 2, D]
+    (dtype of k_pages, head-major) via da_page_stats.  Pages that no table row names
     below L_s, and KV heads whose select_heads flag is 0, are left as they
     are in ``out`` (zeros when it is allocated here)."""
     dev = k_pages.device
@@ -269,11 +269,11 @@ def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_head
     if P % logical:
         raise ValueError(f"logical={logical} does not divide P={P}")
     if out is None:
-        out = torch.zeros((NP, Hkv, P // logical, 2, D), dtype=k_pages.dtype, device=dev)
+        out = torch.zeros((Hkv, NP, P // logical, 2, D), dtype=k_pages.dtype, device=dev)
     else:
         _need(out, "out", k_pages.dtype, dev, 5)
-        if tuple(out.shape) != (NP, Hkv, P // logical, 2, D):
-            raise ValueError("out must be [NP, Hkv, P // logical, 2, D]")
+        if tuple(out.shape) != (Hkv, NP, P // logical, 2, D):
+            raise ValueError("out must be [Hkv, NP, P // logical, 2, D]")
     sh = _selector_shape(block_table.shape[0], Hkv, Hkv, D, P, NP, block_table.shape[1],
                          _dtype_code(k_pages))
     _check(load().da_page_stats(ctypes.byref(sh), _ptr(k_pages), _ptr(block_table), _ptr(seq_lens),
@@ -293,9 +293,9 @@ def page_scores(q, stats, block_table, seq_lens, *, P: int, select_heads=None, o
     if select_heads is not None:
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
     S, Hq, D = q.shape
-    NP, Hkv, NL, two, D2 = stats.shape
+    Hkv, NP, NL, two, D2 = stats.shape
     if two != 2 or D2 != D or P % NL:
-        raise ValueError("stats must be [NP, Hkv, P // logical, 2, D]")
+        raise ValueError("stats must be [Hkv, NP, P // logical, 2, D]")
     if select_heads is not None and select_heads.shape[0] != Hkv:
         raise ValueError("select_heads must have Hkv entries")
     max_pages = block_table.shape[1]

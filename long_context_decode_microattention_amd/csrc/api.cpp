@@ -125,6 +125,7 @@ da_status check_selector(const da_shape* sh, int logical) {
 
 da::SelectorParams selector_params(const da_shape* sh, int logical) {
   da::SelectorParams p{};
+  p.NP = sh->NP;
   p.S = sh->S;
   p.Hq = sh->Hq;
   p.Hkv = sh->Hkv;

@@ -60,12 +60,13 @@ hipError_t launch_check_inputs(const int32_t* table, const int32_t* lens, int S,
 struct SelectorParams {
   const void* q;      // [S, Hq, D]
   const void* k;      // [NP, Hkv, P, D]
-  void* stats;        // [NP, Hkv, P / logical, 2, D]
+  void* stats;        // [Hkv, NP, P / logical, 2, D]
   const int32_t* table;
   const int32_t* lens;
   const uint8_t* select;  // [Hkv] or null
   float* scores;      // [S, Hkv, max_pages]
   uint8_t* mask;      // [S, Hkv, max_pages]
+  long long NP;
   int S, Hq, Hkv, P, max_pages, logical;
   int budget, keep_first, keep_last;
 };

@@ -119,6 +119,12 @@ def _check_mask_valid(mask, want_scores, tol, lens, P, budget, kf, kl, flags):
                 assert gap >= -slack, f"({s},{h}) kept page scores {gap:.3e} below a dropped one"
 
 
+def _page_major(stats):
+    """The library's head-major statistics [Hkv, NP, ...] in the oracle's
+    page-major order [NP, Hkv, ...] (a transpose, no arithmetic)."""
+    return stats.transpose(0, 1).contiguous()
+
+
 def _run_case(name, spec, logical, seed):
     announce("selector", name, "seed", seed)
     b = wl.build(spec, seed, DEV)
@@ -132,10 +138,10 @@ def _run_case(name, spec, logical, seed):
                                   select_heads=torch.from_numpy(upper).to(DEV))
     torch.cuda.synchronize()
     want_stats = osel.page_stats(h(b.k_pages), table, lens, logical=logical)
-    got_stats = oracle.to_f64(h(stats))
+    got_stats = oracle.to_f64(h(_page_major(stats)))
     assert np.array_equal(got_stats, want_stats), f"{name}: statistics differ"
     # heads with flag 0 are not written (the output was allocated as zeros)
-    got_upper = oracle.to_f64(h(stats_upper))
+    got_upper = oracle.to_f64(h(_page_major(stats_upper)))
     on = upper.astype(bool)
     assert np.array_equal(got_upper[:, on], want_stats[:, on]), f"{name}: selected-head statistics"
     assert not np.any(got_upper[:, ~on]), f"{name}: statistics written for an unselected head"
@@ -273,7 +279,7 @@ def test_selector_full_c5_sampled():
         table = np.arange(n, dtype=np.int32)[None, :]
         lens = np.array([L], dtype=np.int32)
         want_stats = osel.page_stats(k, table, lens, logical=logical)
-        got_stats = oracle.to_f64(h(stats[:, kvh:kvh + 1].index_select(0, pages).contiguous()))
+        got_stats = oracle.to_f64(h(_page_major(stats[kvh:kvh + 1].index_select(1, pages))))
         assert np.array_equal(got_stats, want_stats), f"unit ({s},{kvh}): statistics differ"
         fl = flags[kvh:kvh + 1]
         want = osel.page_scores(q, want_stats, table, lens, P, logical, select_heads=fl)
