@@ -37,15 +37,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(key):
-    """HBM bytes per MicroAttention launch from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or
-    None when the kernel sources changed since those counters were taken."""
+def measured_traffic(key, group=None):
+    """HBM bytes per launch of a workload's kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB
+    copy), or None when the kernel sources changed since those counters were
+    taken.  group None = the MicroAttention kernels, "selector" = the page
+    selection kernels."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if group is not None:
+        rec = rec.get(group, {})
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_decode_microattention_amd", "csrc")
     for name in rec.get("files", []):
@@ -128,6 +132,13 @@ def time_workload(key, steps, warmup, dev):
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
     return b, res
+
+
+def sp_key(spec):
+    """Workload key (C1..C5) of a spec."""
+    from long_context_decode_microattention_amd import workloads as wl
+
+    return next(k for k, v in wl.CONFIGS.items() if v.name == spec.name)
 
 
 def time_selector(b, steps, warmup, dev, logical=16):
@@ -237,6 +248,8 @@ def time_selector(b, steps, warmup, dev, logical=16):
     kv_bytes = kept * 2 * D * esize
     return dict(
         kernel="page_scores_kernel (da_page_scores)", logical_page=logical, selected_kv_heads=n_sel,
+        score_traffic=measured_traffic(f"{sp_key(sp)}_page_scores", "selector"),
+        stats_traffic=measured_traffic(f"{sp_key(sp)}_page_stats", "selector"),
         budget=budget, keep_first=keep_first, keep_last=keep_last,
         us_page_scores=us_scores, us_select_topk=us_topk,
         score_bytes=score_bytes, score_GBps=score_bytes / (us_scores * 1e-6) / 1e9,
