@@ -29,7 +29,11 @@ reason in the design notes):
   equal scores are ordered by lower logical page index;
 * KV heads whose selection flag is 0 keep every page below L_s;
 * scores are raw dot-product bounds (a positive attention scale does not
-  change the order, so none is applied).
+  change the order, so none is applied);
+* a selection reused over a chunk of decode steps (section 2.2.2) also keeps
+  the pages that the chunk's appended tokens open (``horizon`` tokens past
+  L_s): they hold the newest tokens, which the forced last pages keep
+  anyway once they exist.
 
 Parity status: every function here is pinned by ``tests/test_selector_oracle.py``
 (brute-force statistics on tiny inputs, the upper-bound property against every
@@ -128,15 +132,18 @@ def page_scores(q, stats, block_table, seq_lens, P: int, logical: int = 16,
 
 
 def select_pages(scores, seq_lens, P: int, budget: int, keep_first: int = 0,
-                 keep_last: int = 0, select_heads=None) -> np.ndarray:
+                 keep_last: int = 0, select_heads=None, horizon: int = 0) -> np.ndarray:
     """Block mask [S, Hkv, max_pages] uint8 from page scores.
 
     For each (request, KV head): pages [0, ceil(L_s / P)) are candidates;
     the first ``keep_first`` and the last ``keep_last`` of them are kept
     unconditionally; of the others the ``budget`` with the highest score are
     kept, equal scores going to the lower page index.  A KV head whose flag
-    in ``select_heads`` is 0 keeps every page below L_s.  Pages at or beyond
-    ceil(L_s / P) are 0.
+    in ``select_heads`` is 0 keeps every page below L_s.  Pages from
+    ceil(L_s / P) up to ceil((L_s + horizon) / P) (at most max_pages) are
+    kept for every head: they receive the tokens appended while the
+    selection is reused (section 2.2.2, reusable page selector).  Pages
+    beyond are 0.
     """
     sc = np.asarray(scores, dtype=np.float64)
     S, Hkv, max_pages = sc.shape
@@ -144,6 +151,8 @@ def select_pages(scores, seq_lens, P: int, budget: int, keep_first: int = 0,
     mask = np.zeros((S, Hkv, max_pages), dtype=np.uint8)
     for s in range(S):
         npg = min(n_pages(int(lens[s]), P), max_pages)
+        npg_h = min(n_pages(int(lens[s]) + int(horizon), P), max_pages)
+        mask[s, :, npg:npg_h] = 1
         for kvh in range(Hkv):
             if select_heads is not None and not select_heads[kvh]:
                 mask[s, kvh, :npg] = 1
