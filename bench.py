@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--chunks", type=int, default=3,
+                    help="timed 16-step chunks of the decode loop with a reused selection")
     ap.add_argument("--no-selector", action="store_true",
                     help="skip the page-selection timing on the block-sparse workload")
     return ap.parse_args()
@@ -158,13 +160,14 @@ def time_selector(b, steps, warmup, dev, logical=16):
     flags = torch.tensor([1 if h >= Hkv // 2 else 0 for h in range(Hkv)], dtype=torch.uint8,
                          device=dev)
     n_sel = int(flags.sum().item())
-    npg = sp.max_pages
+    max_pages = sp.max_pages  # table width (includes spare capacity for appends)
+    npg = -(-sp.max_len // P)  # pages holding each request's tokens (fixed lengths)
     budget = int(frac * (npg - keep_first - keep_last))
     esize = sp.esize
     NL = P // logical
     stats = torch.zeros((Hkv, b.k_pages.shape[0], NL, 2, D), dtype=b.k_pages.dtype, device=dev)
-    scores = torch.empty((sp.S, Hkv, npg), dtype=torch.float32, device=dev)
-    mask = torch.empty((sp.S, Hkv, npg), dtype=torch.uint8, device=dev)
+    scores = torch.empty((sp.S, Hkv, max_pages), dtype=torch.float32, device=dev)
+    mask = torch.empty((sp.S, Hkv, max_pages), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     # statistics of the selected KV heads over the whole pool, timed
@@ -207,7 +210,7 @@ def time_selector(b, steps, warmup, dev, logical=16):
     us_topk = sum(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(steps)) * 1e3 / steps
     # bytes the score kernel must move: the statistics of the selected KV
     # heads' pages below L_s, plus one fp32 score per (request, KV head, page)
-    score_bytes = sp.S * n_sel * npg * NL * 2 * D * esize + sp.S * Hkv * npg * 4
+    score_bytes = sp.S * n_sel * npg * NL * 2 * D * esize + sp.S * Hkv * max_pages * 4
 
     # attention over the selected pages: splits over each head's kept pages
     mask_h = mask.cpu().numpy()
@@ -259,6 +262,93 @@ def time_selector(b, steps, warmup, dev, logical=16):
         us_step_with_selection=us_step, kv_bytes_selected=kv_bytes,
         step_GBps_kv_only=kv_bytes / (us_step * 1e-6) / 1e9,
     )
+
+
+def _kept_tokens(mask_h, lens, P):
+    """Tokens below L_s on pages the mask keeps, summed over (request, KV head)."""
+    import numpy as np
+
+    total = 0
+    for s in range(mask_h.shape[0]):
+        L = int(lens[s])
+        n = -(-L // P)
+        for h in range(mask_h.shape[1]):
+            kp = np.nonzero(mask_h[s, h, :n])[0]
+            total += int((np.minimum((kp + 1) * P, L) - kp * P).sum())
+    return total
+
+
+def time_decode_chunks(b, chunks, dev, logical=16, chunk=16):
+    """The decode loop with a reused selection on a block-sparse workload:
+    per chunk of `chunk` steps, page scores + top-K (horizon = chunk) + split
+    bounds once, then per step: append the new token's K/V (statistics kept
+    current), advance seq_lens, MicroAttention with the reused mask and
+    bounds, merge.  Statistics are computed once before the first chunk.
+    Every chunk starts again from the workload's lengths (the spare capacity
+    of the pool holds one chunk's tokens)."""
+    import numpy as np
+    import torch
+
+    from long_context_decode_microattention_amd import _lib
+    from long_context_decode_microattention_amd import workloads as wl
+
+    sp = b.spec
+    _, keep_first, keep_last, frac = sp.mask
+    Hkv, P, D = sp.Hkv, sp.P, sp.D
+    if sp.reserve < chunk:
+        raise ValueError(f"{sp.name}: the pool needs {chunk} tokens of spare capacity")
+    flags = torch.tensor([1 if h >= Hkv // 2 else 0 for h in range(Hkv)], dtype=torch.uint8,
+                         device=dev)
+    npg = -(-sp.max_len // P)
+    budget = int(frac * (npg - keep_first - keep_last))
+    nb = b.max_splits
+    lens0 = b.seq_lens.clone()
+    lens = lens0.clone()
+    stats = _lib.page_stats(b.k_pages, b.block_table, lens, logical=logical, select_heads=flags)
+    scores = torch.empty((sp.S, Hkv, sp.max_pages), dtype=torch.float32, device=dev)
+    mask = torch.empty((sp.S, Hkv, sp.max_pages), dtype=torch.uint8, device=dev)
+    bounds = torch.empty((sp.S, Hkv, nb + 1), dtype=torch.int32, device=dev)
+    MA = torch.empty((sp.S, sp.Hq, nb, D), dtype=torch.float32, device=dev)
+    m = torch.empty((sp.S, sp.Hq, nb), dtype=torch.float32, device=dev)
+    e = torch.empty_like(m)
+    out = torch.empty((sp.S, sp.Hq, D), dtype=torch.float32, device=dev)
+    new = [wl.new_tokens(sp, 0, i, dev) for i in range(chunk)]
+
+    def run_chunk():
+        _lib.page_scores(b.q, stats, b.block_table, lens, P=P, select_heads=flags, out=scores)
+        _lib.select_pages(scores, lens, P=P, budget=budget, keep_first=keep_first,
+                          keep_last=keep_last, select_heads=flags, horizon=chunk, out=mask)
+        _lib.split_bounds(mask, lens, P=P, b=nb, horizon=chunk, out=bounds)
+        for i in range(chunk):
+            _lib.append_kv(new[i][0], new[i][1], b.block_table, lens, b.k_pages, b.v_pages,
+                           stats=stats, logical=logical, select_heads=flags)
+            lens.add_(1)
+            _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
+                                 scale=b.scale, out=(MA, m, e))
+            _lib.merge(MA, m, e, out=out)
+
+    ms = []
+    for c in range(chunks + 1):  # the first chunk is a warm-up
+        lens.copy_(lens0)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        run_chunk()
+        t1.record()
+        torch.cuda.synchronize()
+        if c:
+            ms.append(t0.elapsed_time(t1))
+    assert torch.isfinite(out).all(), "non-finite output"
+    mask_h = mask.cpu().numpy()
+    L0 = lens0.cpu().numpy().astype(np.int64)
+    kv_bytes = sum(_kept_tokens(mask_h, L0 + i + 1, P) for i in range(chunk)) * 2 * D * sp.esize
+    us_chunk = sum(ms) / len(ms) * 1e3
+    return dict(chunk_steps=chunk, chunks_timed=chunks, us_per_chunk=us_chunk,
+                us_per_step=us_chunk / chunk, kv_bytes_per_chunk=kv_bytes,
+                GBps=kv_bytes / (us_chunk * 1e-6) / 1e9,
+                frac_of_peak=kv_bytes / (us_chunk * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                step="append + micro_attention + merge per step; page scores + top-K + split "
+                     "bounds once per chunk")
 
 
 def read_ceiling(b):
@@ -343,6 +433,7 @@ def main():
     head_selector = None
     if b.spec.mask is not None and not a.no_selector:
         head_selector = time_selector(b, a.steps, a.warmup, dev)
+        head_selector["decode_loop"] = time_decode_chunks(b, a.chunks, dev)
     del b
     torch.cuda.empty_cache()
     secondary = {}
@@ -353,6 +444,7 @@ def main():
         secondary[key] = r2
         if b2.spec.mask is not None and not a.no_selector:
             secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
+            secondary[key + "_selector"]["decode_loop"] = time_decode_chunks(b2, a.chunks, dev)
         del b2
         torch.cuda.empty_cache()
 

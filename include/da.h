@@ -204,8 +204,13 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
  *   below ceil(L_s / P) are 1, and of the pages between them the `budget`
  *   with the highest score are 1 (equal scores: lower page index first;
  *   -0.0 equals 0.0); a KV head with select_heads[kvh] == 0 keeps every page
- *   below ceil(L_s / P); pages at or beyond it are 0.  budget, keep_first
- *   and keep_last must be >= 0.  Scores must not be NaN.
+ *   below ceil(L_s / P).  Pages from ceil(L_s / P) up to
+ *   ceil((L_s + horizon) / P) (at most max_pages) are 1 for every head: a
+ *   selection reused while `horizon` more tokens are appended (section
+ *   2.2.2, reusable page selector: select at the start of a chunk of decode
+ *   steps, reuse inside it) then still covers the pages those tokens open.
+ *   Pages beyond are 0.  budget, keep_first, keep_last and horizon must be
+ *   >= 0.  Scores must not be NaN.
  */
 da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
                         const int32_t* seq_lens, int32_t logical, const uint8_t* select_heads,
@@ -214,8 +219,52 @@ da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t logical,
                          const uint8_t* select_heads, float* scores, hipStream_t stream);
 da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t* seq_lens,
-                          int32_t budget, int32_t keep_first, int32_t keep_last,
+                          int32_t budget, int32_t keep_first, int32_t keep_last, int32_t horizon,
                           const uint8_t* select_heads, uint8_t* block_mask, hipStream_t stream);
+
+/*
+ * Decode-time KV append (the cache write of one decode step).  For every
+ * request s with 0 <= t = seq_lens[s] < max_pages * P and every KV head kvh,
+ * the key row k_new[s, kvh, :] and value row v_new[s, kvh, :] ([S, Hkv, D],
+ * dtype, 16-byte aligned) are written to k_pages / v_pages at page
+ * block_table[s, t / P], slot t % P (the caller assigns that table entry
+ * before the call).  Requests with t outside that range are skipped.  The
+ * call does not change seq_lens: the caller advances it by one afterwards.
+ *
+ * If stats is not NULL ([Hkv, NP, P / logical, 2, D] as for da_page_stats),
+ * the statistics of the logical page receiving the token are kept current at
+ * write time (LServe blog page, section 3.1.2: statistics are computed when
+ * the cache is written): for a KV head whose select_heads entry is not 0 (or
+ * select_heads NULL), the first token of a logical page sets kmax = kmin =
+ * the key, a later one folds in with max / min; the result equals
+ * da_page_stats on the new contents at length t + 1.  logical is read only
+ * when stats is not NULL.
+ *
+ * Reads sh->S, Hkv, D, P, NP, max_pages, dtype.  Supported: dtype F32 or
+ * BF16, D 64 or 128 (statistics: as for da_page_stats).  Two requests must
+ * not append into the same physical page in one call.
+ */
+da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
+                       const int32_t* block_table, const int32_t* seq_lens, void* k_pages,
+                       void* v_pages, int32_t logical, const uint8_t* select_heads, void* stats,
+                       hipStream_t stream);
+
+/*
+ * Split bounds over the kept pages, computed on the device (work planning
+ * for a mask that is reused across decode steps, so no host round trip is
+ * needed).  For request s let E = min(seq_lens[s] + horizon, max_pages * P)
+ * and consider pages below ceil(E / P); for KV head kvh let kept[0] < ... <
+ * kept[K-1] be those with block_mask[s, kvh, page] != 0 (every page when
+ * block_mask is NULL).  With b = sh->max_splits, split_bounds[s, kvh, :]
+ * ([S, Hkv, b + 1] int32, the per-head layout of da_micro_attention) gets
+ *     bound[0] = 0, bound[b] = E,
+ *     bound[j] = P * kept[floor(j K / b)]   (0 < j < b; E when K = 0),
+ * so every split holds floor(K / b) or ceil(K / b) kept pages (the
+ * Infinite-LLM page's sub-blocks, balanced over the pages a mask keeps).
+ * Reads sh->S, Hkv, P, max_pages, max_splits.  horizon must be >= 0.
+ */
+da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
+                          int32_t horizon, int32_t* split_bounds, hipStream_t stream);
 
 /* Message for the last non-OK status returned on the calling thread
  * (thread-local; never NULL; empty if none). */

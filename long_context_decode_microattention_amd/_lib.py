@@ -81,8 +81,12 @@ def load() -> ctypes.CDLL:
     lib.da_page_scores.argtypes = [sp, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP]
     lib.da_page_scores.restype = ctypes.c_int
     lib.da_select_pages.argtypes = [sp, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                    _VP, _VP, _VP]
+                                    ctypes.c_int32, _VP, _VP, _VP]
     lib.da_select_pages.restype = ctypes.c_int
+    lib.da_append_kv.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP]
+    lib.da_append_kv.restype = ctypes.c_int
+    lib.da_split_bounds.argtypes = [sp, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    lib.da_split_bounds.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
     lib.da_stream_read_sink_words.argtypes = []
@@ -311,9 +315,10 @@ def page_scores(q, stats, block_table, seq_lens, *, P: int, select_heads=None, o
 
 
 def select_pages(scores, seq_lens, *, P: int, budget: int, keep_first: int = 0,
-                 keep_last: int = 0, select_heads=None, out=None):
+                 keep_last: int = 0, select_heads=None, horizon: int = 0, out=None):
     """Block mask [S, Hkv, max_pages] uint8 via da_select_pages: forced first
-    and last pages plus the ``budget`` best-scoring others."""
+    and last pages plus the ``budget`` best-scoring others, and the pages the
+    next ``horizon`` appended tokens open."""
     dev = scores.device
     _need(scores, "scores", torch.float32, dev, 3)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
@@ -328,8 +333,70 @@ def select_pages(scores, seq_lens, *, P: int, budget: int, keep_first: int = 0,
         _need(out, "out", torch.uint8, dev, 3)
     sh = _selector_shape(S, Hkv, Hkv, 1, P, 1, max_pages, DA_F32)
     _check(load().da_select_pages(ctypes.byref(sh), _ptr(scores), _ptr(seq_lens), int(budget),
-                                  int(keep_first), int(keep_last), _ptr(select_heads), _ptr(out),
-                                  _stream(dev)))
+                                  int(keep_first), int(keep_last), int(horizon), _ptr(select_heads),
+                                  _ptr(out), _stream(dev)))
+    return out
+
+
+def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=None,
+              logical: int = 16, select_heads=None):
+    """Write each request's new K/V rows ([S, Hkv, D]) at position seq_lens[s]
+    of the paged pools in place via da_append_kv, keeping ``stats`` (head-major
+    statistics, or None) current.  seq_lens is not advanced."""
+    dev = k_pages.device
+    _need(k_pages, "k_pages", None, dev, 4)
+    _need(v_pages, "v_pages", k_pages.dtype, dev, 4)
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages differ in shape")
+    NP, Hkv, P, D = k_pages.shape
+    S = block_table.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, k_pages.dtype, dev, 3)
+        if tuple(t.shape) != (S, Hkv, D):
+            raise ValueError(f"{name} must be [S, Hkv, D] = {(S, Hkv, D)}")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    if seq_lens.shape[0] != S:
+        raise ValueError("seq_lens must have S entries")
+    if stats is not None:
+        _need(stats, "stats", k_pages.dtype, dev, 5)
+        if tuple(stats.shape) != (Hkv, NP, P // logical, 2, D):
+            raise ValueError("stats must be [Hkv, NP, P // logical, 2, D]")
+    if select_heads is not None:
+        _need(select_heads, "select_heads", torch.uint8, dev, 1)
+        if select_heads.shape[0] != Hkv:
+            raise ValueError("select_heads must have Hkv entries")
+    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_pages))
+    _check(load().da_append_kv(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                               _ptr(seq_lens), _ptr(k_pages), _ptr(v_pages), int(logical),
+                               _ptr(select_heads), _ptr(stats), _stream(dev)))
+
+
+def split_bounds(block_mask, seq_lens, *, P: int, b: int, horizon: int = 0, Hkv=None,
+                 max_pages=None, out=None):
+    """Per-head split bounds [S, Hkv, b + 1] int32 over the kept pages via
+    da_split_bounds (block_mask None = every page kept; then Hkv and
+    max_pages are required)."""
+    dev = seq_lens.device
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    S = seq_lens.shape[0]
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+        S2, Hkv, max_pages = block_mask.shape
+        if S2 != S:
+            raise ValueError("block_mask must have S rows")
+    elif Hkv is None or max_pages is None:
+        raise ValueError("Hkv and max_pages are required without a block mask")
+    if out is None:
+        out = torch.empty((S, Hkv, b + 1), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", torch.int32, dev, 3)
+        if tuple(out.shape) != (S, Hkv, b + 1):
+            raise ValueError("out must be [S, Hkv, b + 1]")
+    sh = DaShape(S=S, Hq=Hkv, Hkv=Hkv, D=1, P=P, max_pages=max_pages, max_splits=b,
+                 bounds_per_head=1, dtype=DA_F32, scale=1.0, NP=1)
+    _check(load().da_split_bounds(ctypes.byref(sh), _ptr(block_mask), _ptr(seq_lens), int(horizon),
+                                  _ptr(out), _stream(dev)))
     return out
 
 

@@ -306,7 +306,7 @@ da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
 }
 
 da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t* seq_lens,
-                          int32_t budget, int32_t keep_first, int32_t keep_last,
+                          int32_t budget, int32_t keep_first, int32_t keep_last, int32_t horizon,
                           const uint8_t* select_heads, uint8_t* block_mask, hipStream_t stream) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1)
@@ -319,8 +319,8 @@ da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t
   if (sh->max_pages > da::select_max_pages())
     return fail(DA_ERR_UNSUPPORTED, "top-K selection is built for max_pages <= %d (got %d)",
                 da::select_max_pages(), sh->max_pages);
-  if (budget < 0 || keep_first < 0 || keep_last < 0)
-    return fail(DA_ERR_INVALID_ARG, "budget, keep_first and keep_last must be >= 0");
+  if (budget < 0 || keep_first < 0 || keep_last < 0 || horizon < 0)
+    return fail(DA_ERR_INVALID_ARG, "budget, keep_first, keep_last and horizon must be >= 0");
   if (!scores || !seq_lens || !block_mask) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(scores, 4) || !aligned(seq_lens, 4))
     return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
@@ -332,8 +332,83 @@ da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t
   p.budget = budget;
   p.keep_first = keep_first;
   p.keep_last = keep_last;
+  p.horizon = horizon;
   const hipError_t err = da::launch_select_pages(p, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "page-select launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
+                       const int32_t* block_table, const int32_t* seq_lens, void* k_pages,
+                       void* v_pages, int32_t logical, const uint8_t* select_heads, void* stats,
+                       hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d D=%d P=%d max_pages=%d NP=%lld)",
+                sh->S, sh->Hkv, sh->D, sh->P, sh->max_pages, (long long)sh->NP);
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
+    return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->S * sh->Hkv > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
+  if (!da::append_supported(sh->dtype, sh->D))
+    return fail(DA_ERR_UNSUPPORTED, "KV append not built for dtype=%d D=%d", sh->dtype, sh->D);
+  if (stats != nullptr && !da::selector_supported(sh->dtype, sh->D, 1, sh->P, logical))
+    return fail(DA_ERR_UNSUPPORTED, "statistics not built for P=%d logical=%d", sh->P, logical);
+  if (!k_new || !v_new || !block_table || !seq_lens || !k_pages || !v_pages)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      (stats != nullptr && !aligned(stats, 16)))
+    return fail(DA_ERR_INVALID_ARG, "K/V rows, pools and statistics must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  da::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.k = k_pages;
+  p.v = v_pages;
+  p.stats = stats;
+  p.select = select_heads;
+  p.NP = sh->NP;
+  p.S = sh->S;
+  p.Hkv = sh->Hkv;
+  p.P = sh->P;
+  p.max_pages = sh->max_pages;
+  p.logical = stats != nullptr ? logical : sh->P;
+  const hipError_t err = da::launch_append_kv(p, sh->dtype, sh->D, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "KV append launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
+                          int32_t horizon, int32_t* split_bounds, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1 || sh->max_splits < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d max_splits=%d)",
+                sh->S, sh->Hkv, sh->P, sh->max_pages, sh->max_splits);
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->S * sh->Hkv > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
+  if (horizon < 0) return fail(DA_ERR_INVALID_ARG, "horizon must be >= 0");
+  if (!seq_lens || !split_bounds) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(seq_lens, 4) || !aligned(split_bounds, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  da::BoundsParams p{};
+  p.mask = block_mask;
+  p.lens = seq_lens;
+  p.bounds = split_bounds;
+  p.S = sh->S;
+  p.Hkv = sh->Hkv;
+  p.P = sh->P;
+  p.max_pages = sh->max_pages;
+  p.b = sh->max_splits;
+  p.horizon = horizon;
+  const hipError_t err = da::launch_split_bounds(p, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "split-bounds launch failed: %s", hipGetErrorString(err));
   return DA_OK;
 }
 

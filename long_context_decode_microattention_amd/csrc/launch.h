@@ -68,7 +68,7 @@ struct SelectorParams {
   uint8_t* mask;      // [S, Hkv, max_pages]
   long long NP;
   int S, Hq, Hkv, P, max_pages, logical;
-  int budget, keep_first, keep_last;
+  int budget, keep_first, keep_last, horizon;
 };
 bool selector_supported(int dtype, int D, int G, int P, int logical);
 hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStream_t stream);
@@ -76,6 +76,29 @@ hipError_t launch_page_scores(const SelectorParams& p, int dtype, int D, hipStre
 hipError_t launch_select_pages(const SelectorParams& p, hipStream_t stream);
 long long score_launch_items(int S, int Hkv, int max_pages, int P, int logical);
 int select_max_pages();
+
+// Decode-time cache update and split planning (decode_update.hip).
+struct AppendParams {
+  const void* k_new;  // [S, Hkv, D]
+  const void* v_new;  // [S, Hkv, D]
+  const int32_t* table;
+  const int32_t* lens;
+  void* k;            // [NP, Hkv, P, D]
+  void* v;
+  void* stats;        // [Hkv, NP, P / logical, 2, D] or null
+  const uint8_t* select;
+  long long NP;
+  int S, Hkv, P, max_pages, logical;
+};
+struct BoundsParams {
+  const uint8_t* mask;  // [S, Hkv, max_pages] or null (every page kept)
+  const int32_t* lens;
+  int32_t* bounds;      // [S, Hkv, b + 1]
+  int S, Hkv, P, max_pages, b, horizon;
+};
+bool append_supported(int dtype, int D);
+hipError_t launch_append_kv(const AppendParams& p, int dtype, int D, hipStream_t stream);
+hipError_t launch_split_bounds(const BoundsParams& p, hipStream_t stream);
 
 int stream_read_grid();
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

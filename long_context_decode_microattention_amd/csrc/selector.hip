@@ -347,9 +347,13 @@ __global__ __launch_bounds__(kTopkThreads) void select_pages_kernel(SelectorPara
   const bool selected = head_selected(p.select, kvh);
   const int lo = selected ? min(p.keep_first, npg) : npg;
   const int hi = selected ? max(npg - p.keep_last, lo) : npg;
-  // pages outside [lo, hi) are forced (below npg) or zero (at or beyond npg)
+  // pages the next `horizon` appended tokens open stay kept while the
+  // selection is reused
+  const int npg_h = (int)min((long long)p.max_pages,
+                             ((long long)L + p.horizon + p.P - 1) / p.P);
+  // pages outside [lo, hi) are forced (below npg_h) or zero (at or beyond it)
   for (int i = tid; i < p.max_pages; i += kTopkThreads)
-    if (i < lo || i >= hi) mrow[i] = i < npg ? 1 : 0;
+    if (i < lo || i >= hi) mrow[i] = i < npg_h ? 1 : 0;
   const int n = hi - lo;
   if (n <= 0) return;
   if (p.budget >= n || p.budget <= 0) {

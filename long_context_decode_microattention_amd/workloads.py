@@ -42,6 +42,9 @@ class Spec:
     sink      -- (tokens, cosine) of request-prefix keys aligned to q, or None.
     mask      -- ("lserve", keep_first, keep_last, fraction) applied to the
                  upper half of the KV heads, or None.
+    reserve   -- tokens of spare capacity per request: the block table maps
+                 pages up to ceil((L_s + reserve) / P), so decode steps can
+                 append that many tokens.
     """
 
     name: str
@@ -58,6 +61,7 @@ class Spec:
     sink: Optional[tuple] = None
     mask: Optional[tuple] = None
     extra_pages: int = 0
+    reserve: int = 0
 
     @property
     def G(self) -> int:
@@ -73,7 +77,7 @@ class Spec:
 
     @property
     def max_pages(self) -> int:
-        return -(-self.max_len // self.P)
+        return -(-(self.max_len + self.reserve) // self.P)
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -94,7 +98,7 @@ CONFIGS = {
                sink=(4, 0.9)),
     "C5": Spec("C5 LLaMA-3-8B GQA 32/8, batch 8, 512K, half the KV heads block-sparse, bf16",
                S=8, Hq=32, Hkv=8, D=128, P=64, dtype=BF16, lens=("fixed", 1 << 19),
-               splits=("kept_pages", 16), mask=("lserve", 1, 2, 0.25)),
+               splits=("kept_pages", 16), mask=("lserve", 1, 2, 0.25), reserve=16),
 }
 
 
@@ -180,20 +184,21 @@ def build(spec: Spec, seed: int = 0, device="cpu") -> Batch:
     lens = _lengths(spec, seed)
     n_log = [-(-int(L) // P) for L in lens]
     max_pages = spec.max_pages
+    n_cap = [min(max_pages, -(-(int(L) + spec.reserve) // P)) for L in lens]  # mapped pages
 
     # block table
     table = np.zeros((S, max_pages), dtype=np.int32)
     if spec.table == "identity":
         NP = S * max_pages
         for s in range(S):
-            table[s, :n_log[s]] = s * max_pages + np.arange(n_log[s])
+            table[s, :n_cap[s]] = s * max_pages + np.arange(n_cap[s])
     elif spec.table == "shuffled":
-        NP = int(sum(n_log))
+        NP = int(sum(n_cap))
         perm = _np_rng(seed, spec, "table").permutation(NP + spec.extra_pages)[:NP]
         off = 0
         for s in range(S):
-            table[s, :n_log[s]] = perm[off:off + n_log[s]]
-            off += n_log[s]
+            table[s, :n_cap[s]] = perm[off:off + n_cap[s]]
+            off += n_cap[s]
     else:
         raise ValueError(spec.table)
     NP += spec.extra_pages
@@ -295,6 +300,17 @@ def build(spec: Spec, seed: int = 0, device="cpu") -> Batch:
         block_mask=None if mask_np is None else torch.from_numpy(mask_np).to(device),
         scale=1.0 / math.sqrt(D), kept_pages=kept,
     )
+
+
+def new_tokens(spec: Spec, seed: int, step: int, device="cpu"):
+    """Key and value rows [S, Hkv, D] of the token appended at decode step
+    `step`: i.i.d. N(0, 1) in the workload's dtype, one seeded sub-stream per
+    (seed, workload, step)."""
+    g = _gen(seed, spec, f"new_tokens/{step}", torch.device(device))
+    shape = (spec.S, spec.Hkv, spec.D)
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return k.to(TORCH_DTYPE[spec.dtype]), v.to(TORCH_DTYPE[spec.dtype])
 
 
 def host(t: Optional[torch.Tensor]):

@@ -174,9 +174,10 @@ def test_page_scores_rejects(lib, case, status):
 
 @pytest.mark.parametrize("case,status", [
     (dict(shape=dict(Hkv=0)), _lib.DA_ERR_INVALID_ARG),
-    (dict(args=(-1, 0, 0)), _lib.DA_ERR_INVALID_ARG),
-    (dict(args=(4, -2, 0)), _lib.DA_ERR_INVALID_ARG),
-    (dict(args=(4, 0, -1)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(-1, 0, 0, 0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(4, -2, 0, 0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(4, 0, -1, 0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(args=(4, 0, 0, -1)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(mask=None)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(scores=FAKE + 1)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(max_pages=65537, P=16)), _lib.DA_ERR_UNSUPPORTED),
@@ -185,7 +186,43 @@ def test_select_pages_rejects(lib, case, status):
     sh = good_shape(**case.get("shape", {}))
     p = dict(scores=FAKE, lens=FAKE, sel=None, mask=FAKE)
     p.update(case.get("ptrs", {}))
-    budget, kf, kl = case.get("args", (4, 1, 1))
+    budget, kf, kl, hz = case.get("args", (4, 1, 1, 0))
     got = lib.da_select_pages(ctypes.byref(sh), _vp(p["scores"]), _vp(p["lens"]), budget, kf, kl,
-                              _vp(p["sel"]), _vp(p["mask"]), None)
+                              hz, _vp(p["sel"]), _vp(p["mask"]), None)
+    assert got == status, _lib.load().da_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(S=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(dtype=7)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(logical=12, ptrs=dict(stats=FAKE)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(ptrs=dict(k_new=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(v=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(stats=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(table=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_append_kv_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(k_new=FAKE, v_new=FAKE, table=FAKE, lens=FAKE, k=FAKE, v=FAKE, sel=None, stats=None)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_append_kv(ctypes.byref(sh), _vp(p["k_new"]), _vp(p["v_new"]), _vp(p["table"]),
+                           _vp(p["lens"]), _vp(p["k"]), _vp(p["v"]), case.get("logical", 16),
+                           _vp(p["sel"]), _vp(p["stats"]), None)
+    assert got == status, _lib.load().da_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(max_splits=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(Hkv=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(horizon=-1), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(out=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(lens=FAKE + 1)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_split_bounds_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(mask=None, lens=FAKE, out=FAKE)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_split_bounds(ctypes.byref(sh), _vp(p["mask"]), _vp(p["lens"]),
+                              case.get("horizon", 0), _vp(p["out"]), None)
     assert got == status, _lib.load().da_last_error()

@@ -263,7 +263,7 @@ def test_selector_full_c5_sampled():
     sel_t = torch.from_numpy(flags).to(DEV)
     stats = _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical)
     scores = _lib.page_scores(b.q, stats, b.block_table, b.seq_lens, P=P, select_heads=sel_t)
-    npg = spec.max_pages
+    npg = -(-spec.max_len // P)  # pages holding each request's tokens
     budget = (npg - 3) // 4
     mask = _lib.select_pages(scores, b.seq_lens, P=P, budget=budget, keep_first=1, keep_last=2,
                              select_heads=sel_t)
@@ -284,11 +284,16 @@ def test_selector_full_c5_sampled():
         fl = flags[kvh:kvh + 1]
         want = osel.page_scores(q, want_stats, table, lens, P, logical, select_heads=fl)
         got = scores[s:s + 1, kvh:kvh + 1].cpu().numpy().astype(np.float64)
+        # table columns past the request's pages (spare capacity) score -inf
+        assert np.all(np.isneginf(got[..., n:])), f"unit ({s},{kvh}): spare pages scored"
+        got = got[..., :n]
         assert np.array_equal(np.isneginf(got), np.isneginf(want))
         tol = _score_tolerance(q, want_stats, table, lens, P, logical, spec.D)
         fin = ~np.isneginf(want)
         assert np.all(np.abs(got[fin] - want[fin]) <= tol[fin]), f"unit ({s},{kvh}): scores"
         got_mask = mask[s:s + 1, kvh:kvh + 1].cpu().numpy()
+        assert not np.any(got_mask[..., n:]), f"unit ({s},{kvh}): spare pages kept"
+        got_mask = got_mask[..., :n]
         want_mask = osel.select_pages(got, lens, P, budget, 1, 2, select_heads=fl)
         assert np.array_equal(got_mask, want_mask), f"unit ({s},{kvh}): mask differs"
         _check_mask_valid(got_mask, want, tol, lens, P, budget, 1, 2, fl)
