@@ -58,8 +58,11 @@ typedef enum da_status {
 } da_status;
 
 typedef enum da_dtype {
-  DA_F32 = 0,  /* IEEE binary32                                     */
-  DA_BF16 = 1  /* bfloat16: the upper 16 bits of an IEEE binary32  */
+  DA_F32 = 0,     /* IEEE binary32                                     */
+  DA_BF16 = 1,    /* bfloat16: the upper 16 bits of an IEEE binary32  */
+  DA_FP8_E4M3 = 2 /* 8-bit pages: OCP FP8 E4M3 codes with one fp32     */
+                  /* scale per (page, KV head, slot) row; q is bf16.   */
+                  /* Used by da_micro_attention_fp8 only.              */
 } da_dtype;
 
 /* Problem shape.  Notation: S requests, Hq query heads, Hkv KV heads
@@ -134,6 +137,42 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
 /* Workspace bytes da_micro_attention uses for this shape (0 if it runs
  * unchunked).  Host-only; writes *bytes. */
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes);
+
+/*
+ * MicroAttention over 8-bit KV pages (LServe blog page, section 3.2.1: the
+ * retrieval-head cache is stored with configurable 2-8 bit quantization).
+ * Same partials, splits, mask, workspace and errors as da_micro_attention,
+ * with sh->dtype = DA_FP8_E4M3 and:
+ *   q            [S, Hq, D] bfloat16, 16-byte aligned.
+ *   k_codes      [NP, Hkv, P, D] uint8 OCP FP8 E4M3 codes, 16-byte aligned;
+ *                the key of a token is value(code) * k_scales[page, g, slot]
+ *                (per-row scales as written by da_quantize_rows).
+ *   k_scales     [NP, Hkv, P] float32, 4-byte aligned.
+ *   v_codes, v_scales  likewise for values.
+ * Scores, softmax and value sums are computed in fp32 from the exact code
+ * values; slots outside every split are never read.  Supported: D 64 or 128,
+ * G in {1, 2, 4, 8}.  da_micro_attention_workspace_size with the same shape
+ * gives the workspace size.
+ */
+da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                                 const float* k_scales, const uint8_t* v_codes,
+                                 const float* v_scales, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* split_bounds,
+                                 const uint8_t* block_mask, float* MA, float* m, float* e,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * 8-bit quantization of rows (the write side of 8-bit KV pages): for each of
+ * `rows` rows of D elements of x (dtype DA_F32 or DA_BF16, [rows, D],
+ * 16-byte aligned), s = amax / 448 (amax = the largest |x| of the row, fp32
+ * division) and code = the OCP FP8 E4M3 value nearest to x / s (fp32
+ * division, clamped to [-448, 448], ties to even, sign kept when the
+ * magnitude rounds to zero); an all-zero row gets s = 0 and codes 0.
+ * codes [rows, D] uint8 (8-byte aligned), scales [rows] float32.  A K or V
+ * pool [NP, Hkv, P, D] is rows = NP * Hkv * P.  Supported: D 64 or 128.
+ */
+da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x,
+                           uint8_t* codes, float* scales, hipStream_t stream);
 
 /*
  * Aggregate b partials per (request, query head) into attention output.

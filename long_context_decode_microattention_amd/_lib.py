@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libda.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "da.h")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
-DA_F32, DA_BF16 = 0, 1
+DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "DA_OK", 1: "DA_ERR_INVALID_ARG", 2: "DA_ERR_UNSUPPORTED", 3: "DA_ERR_HIP"}
 
 
@@ -87,6 +87,12 @@ def load() -> ctypes.CDLL:
     lib.da_append_kv.restype = ctypes.c_int
     lib.da_split_bounds.argtypes = [sp, _VP, _VP, ctypes.c_int32, _VP, _VP]
     lib.da_split_bounds.restype = ctypes.c_int
+    lib.da_micro_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.da_micro_attention_fp8.restype = ctypes.c_int
+    lib.da_quantize_rows.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP,
+                                     _VP]
+    lib.da_quantize_rows.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
     lib.da_stream_read_sink_words.argtypes = []
@@ -214,6 +220,78 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
         ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
         _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m), _ptr(e), _ptr(workspace),
         ws_bytes, _stream(dev)))
+    return MA, m, e
+
+
+def quantize_rows(x, *, out=None):
+    """8-bit rows via da_quantize_rows: x [..., D] (bf16 or float32) ->
+    (codes uint8 [..., D], scales float32 [...]), OCP FP8 E4M3 codes with one
+    scale amax / 448 per row."""
+    dev = x.device
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if out is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    else:
+        codes, scales = out
+        _need(codes, "codes", torch.uint8, dev, x.dim())
+        _need(scales, "scales", torch.float32, dev, x.dim() - 1)
+        if codes.shape != x.shape or scales.shape != x.shape[:-1]:
+            raise ValueError("codes must match x, scales x without its last dim")
+    _check(load().da_quantize_rows(_dtype_code(x), rows, D, _ptr(x), _ptr(codes), _ptr(scales),
+                                   _stream(dev)))
+    return codes, scales
+
+
+def micro_attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens,
+                        split_bounds, block_mask=None, *, scale: Optional[float] = None, out=None,
+                        chunks: int = 0, workspace: Optional[torch.Tensor] = None,
+                        schedule: int = 0):
+    """MicroAttention partials over 8-bit pages via da_micro_attention_fp8:
+    q [S, Hq, D] bf16; k_codes / v_codes [NP, Hkv, P, D] uint8 E4M3 codes;
+    k_scales / v_scales [NP, Hkv, P] float32.  Arguments otherwise as
+    micro_attention."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(k_codes, "k_codes", torch.uint8, dev, 4)
+    _need(v_codes, "v_codes", torch.uint8, dev, 4)
+    if v_codes.shape != k_codes.shape:
+        raise ValueError("k_codes and v_codes differ in shape")
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.float32, dev, 3)
+        if tuple(t.shape) != tuple(k_codes.shape[:3]):
+            raise ValueError(f"{name} must be [NP, Hkv, P]")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule)
+    sh.dtype = DA_FP8_E4M3
+    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
+        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
+    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
+        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
+    if out is None:
+        MA = torch.empty((sh.S, sh.Hq, sh.max_splits, sh.D), dtype=torch.float32, device=dev)
+        m = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
+        e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
+    else:
+        MA, m, e = out
+    if workspace is False:
+        workspace = None
+    elif workspace is None:
+        workspace = _cached_workspace(dev, workspace_size(sh))
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().da_micro_attention_fp8(
+        ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(block_table), _ptr(seq_lens), _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m),
+        _ptr(e), _ptr(workspace), ws_bytes, _stream(dev)))
     return MA, m, e
 
 

@@ -29,8 +29,10 @@ da_status fail(da_status st, const char* fmt, ...) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Shape checks shared by the entry points that read the paged cache.
-da_status check_shape(const da_shape* sh) {
+// Shape checks shared by the entry points that read the paged cache.  The
+// 8-bit page type is accepted only where fp8 is true (its own entry point
+// and the workspace query).
+da_status check_shape(const da_shape* sh, bool fp8 = false) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 ||
       sh->max_splits < 1 || sh->NP < 1)
@@ -42,8 +44,9 @@ da_status check_shape(const da_shape* sh) {
     return fail(DA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", sh->Hq, sh->Hkv);
   if (sh->bounds_per_head != 0 && sh->bounds_per_head != 1)
     return fail(DA_ERR_INVALID_ARG, "bounds_per_head must be 0 or 1 (got %d)", sh->bounds_per_head);
-  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
-    return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16 && !(fp8 && sh->dtype == DA_FP8_E4M3))
+    return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype%s", sh->dtype,
+                sh->dtype == DA_FP8_E4M3 ? " for this entry point (8-bit pages: da_micro_attention_fp8)" : "");
   if (!(sh->scale > 0.f) || !isfinite(sh->scale))
     return fail(DA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if ((long long)sh->max_pages * sh->P > INT_MAX)
@@ -139,13 +142,18 @@ da::SelectorParams selector_params(const da_shape* sh, int logical) {
 
 extern "C" {
 
-da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pages,
-                             const void* v_pages, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* split_bounds,
-                             const uint8_t* block_mask, float* MA, float* m, float* e,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  da_status st = check_shape(sh);
-  if (st != DA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Body of both MicroAttention entry points; ks / vs are the per-row scales
+// of 8-bit pages (null otherwise).
+da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_pages,
+                               const void* v_pages, const float* ks, const float* vs,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* split_bounds, const uint8_t* block_mask, float* MA,
+                               float* m, float* e, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds || !MA || !m || !e)
     return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(MA, 16))
@@ -190,6 +198,8 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   p.lens = seq_lens;
   p.bounds = split_bounds;
   p.mask = block_mask;
+  p.ks = ks;
+  p.vs = vs;
   char* wsb = static_cast<char*>(workspace);
   p.MA = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.ma) : MA;
   p.m = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.m) : m;
@@ -219,9 +229,44 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   return DA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* split_bounds,
+                             const uint8_t* block_mask, float* MA, float* m, float* e,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const da_status st = check_shape(sh);
+  if (st != DA_OK) return st;
+  return micro_attention_impl(sh, q, k_pages, v_pages, nullptr, nullptr, block_table, seq_lens,
+                              split_bounds, block_mask, MA, m, e, workspace, workspace_bytes,
+                              stream);
+}
+
+da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                                 const float* k_scales, const uint8_t* v_codes,
+                                 const float* v_scales, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* split_bounds,
+                                 const uint8_t* block_mask, float* MA, float* m, float* e,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const da_status st = check_shape(sh, true);
+  if (st != DA_OK) return st;
+  if (sh->dtype != DA_FP8_E4M3)
+    return fail(DA_ERR_INVALID_ARG, "da_micro_attention_fp8 needs dtype DA_FP8_E4M3 (got %d)",
+                sh->dtype);
+  if (!k_scales || !v_scales) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
+  return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
+                              split_bounds, block_mask, MA, m, e, workspace, workspace_bytes,
+                              stream);
+}
+
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
   if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
-  da_status st = check_shape(sh);
+  da_status st = check_shape(sh, true);
   if (st != DA_OK) return st;
   *bytes = ws_layout(sh, resolve_chunks(sh)).total;
   return DA_OK;
@@ -409,6 +454,24 @@ da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const i
   p.horizon = horizon;
   const hipError_t err = da::launch_split_bounds(p, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "split-bounds launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
+da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x,
+                           uint8_t* codes, float* scales, hipStream_t stream) {
+  if (rows < 0 || D < 1) return fail(DA_ERR_INVALID_ARG, "rows must be >= 0 and D >= 1");
+  if (dtype != DA_F32 && dtype != DA_BF16)
+    return fail(DA_ERR_INVALID_ARG, "dtype %d is not DA_F32 or DA_BF16", dtype);
+  if (!da::quantize_supported(dtype, D))
+    return fail(DA_ERR_UNSUPPORTED, "quantization not built for D=%d (64, 128)", D);
+  if (rows == 0) return DA_OK;
+  if (!x || !codes || !scales) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte and scales 4-byte aligned");
+  if (da::quantize_launch_blocks(D, rows) > UINT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "too many rows for one launch");
+  const hipError_t err = da::launch_quantize_rows(dtype, D, x, codes, scales, rows, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(err));
   return DA_OK;
 }
 

@@ -32,7 +32,7 @@ __device__ __forceinline__ float dpp(float x) {
 // branches on it skip code instead of masking it).
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
-// Sum over aligned groups of N consecutive lanes (N = 8, 16 or 32); every
+// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16 or 32); every
 // lane of the group receives the group total.  After the two quad steps each
 // lane holds its quad's sum; the half-row mirror pairs every lane with a lane
 // of the other quad of its 8-lane half, the row mirror with a lane of the
@@ -40,9 +40,10 @@ __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballo
 // across rows.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
   x += dpp<kDppQuadXor1>(x);
   x += dpp<kDppQuadXor2>(x);
+  if constexpr (N == 4) return x;
   x += dpp<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
   if constexpr (N == 32) x += __shfl_xor(x, 16, kWave);
@@ -60,6 +61,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Four OCP E4M3 codes packed in a word (byte i = element i) -> four floats,
+// exactly (v_cvt_pk_f32_fp8 on gfx950).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = hi.x;
+  out[3] = hi.y;
+}
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 

@@ -16,6 +16,8 @@ struct MicroParams {
   const int32_t* lens;
   const int32_t* bounds;
   const uint8_t* mask;  // may be null
+  const float* ks;      // fp8 pages: per-(page, head, slot) scales of K and V, else null
+  const float* vs;
   float* MA;  // [S, Hq, max_splits, chunks, D]: the split partials when chunks == 1,
   float* m;   // else one partial per chunk (workspace), folded by launch_combine
   float* e;
@@ -99,6 +101,12 @@ struct BoundsParams {
 bool append_supported(int dtype, int D);
 hipError_t launch_append_kv(const AppendParams& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_split_bounds(const BoundsParams& p, hipStream_t stream);
+
+// 8-bit KV rows (quant.hip).
+bool quantize_supported(int dtype, int D);
+hipError_t launch_quantize_rows(int dtype, int D, const void* x, uint8_t* codes, float* scales,
+                                long long rows, hipStream_t stream);
+long long quantize_launch_blocks(int D, long long rows);
 
 int stream_read_grid();
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -20,7 +20,10 @@
 // end of the item.
 //
 // Arithmetic: fp32 accumulation.  bf16 scores use v_dot2 (bf16 pairs, fp32
-// accumulate); bf16 values are widened exactly by bit shifts.  Exponentials
+// accumulate); bf16 values are widened exactly by bit shifts.  fp8 (E4M3)
+// pages are widened exactly by v_cvt_pk_f32_fp8 and multiply a bf16 query
+// held in fp32; a token's K scale multiplies its dot product and its V scale
+// its probability (per-row scales of the quantized pages).  Exponentials
 // run in base 2 on raw dot products: exp(scale*(d - d_max)) =
 // exp2((d - d_max) * scale*log2(e)); the reported m_j is scale * d_max.
 #include <type_traits>
@@ -29,14 +32,15 @@
 
 namespace da {
 
-hipError_t launch_micro_mfma(int D, int G, const MicroParams& p, hipStream_t stream);
+hipError_t launch_micro_mfma(int dtype, int D, int G, const MicroParams& p, hipStream_t stream);
 bool micro_mfma_supported(int dtype, int D, int G);
 
 namespace {
 
+// DT: 0 = fp32, 1 = bf16, 2 = fp8 E4M3 with per-row scales.
 template <int DT, int D>
 struct Layout {
-  static constexpr int ES = DT == 0 ? 4 : 2;  // bytes per element
+  static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);  // bytes per element
   static constexpr int TOKB = D * ES;          // bytes per token row
   static constexpr int LPT = TOKB / 16;        // lanes per token row
   static constexpr int TPI = kWave / LPT;      // token rows per wave load
@@ -50,6 +54,8 @@ template <int DT, int D>
 struct Frag {
   uint4 k[Layout<DT, D>::NI];
   uint4 v[Layout<DT, D>::NI];
+  float ks[Layout<DT, D>::NI];  // fp8: K and V scales of this lane's token rows
+  float vs[Layout<DT, D>::NI];
 };
 
 template <bool B>
@@ -77,13 +83,28 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
     const int P = p.P;
     const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
-    // Query fragment of every head in the group: the lane's 16-byte column.
+    // Query fragment of every head in the group: the lane's 16-byte column
+    // (for fp8 pages: the lane's 16 dims of the bf16 query, widened to fp32).
     uint4 qv[G];
+    float qf[DT == 2 ? G : 1][DT == 2 ? L::EPL : 1];
   #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const char* qp = static_cast<const char*>(p.q) +
-                       ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
-      qv[g] = *reinterpret_cast<const uint4*>(qp);
+      if constexpr (DT == 2) {
+        const uint4* qp = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + g) * D * 2 + (size_t)chunk * 32);
+        const uint4 a = qp[0], b = qp[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qf[g][2 * i] = bf16_lo(w[i]);
+          qf[g][2 * i + 1] = bf16_hi(w[i]);
+        }
+        qv[g] = make_uint4(0, 0, 0, 0);
+      } else {
+        const char* qp = static_cast<const char*>(p.q) +
+                         ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
+        qv[g] = *reinterpret_cast<const uint4*>(qp);
+      }
     }
 
     float m_[G], e_[G], acc[G][L::EPL];
@@ -101,6 +122,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
       const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
       const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
       const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+      const size_t scale_page = (size_t)p.Hkv * P;  // fp8: scales per physical page
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
@@ -113,11 +135,17 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
           const int sub = sl - kp * spp;
           const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
           const int tb = s_lp[kp] * P + sub * kSlab;
+          // fp8: the scales of this lane's token rows (slot sub*kSlab + i*TPI + row)
+          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * kSlab + row;
           if (tb >= t0 && tb + kSlab <= t1) {
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               f.k[i] = load_stream16(kbase + off + i * 1024);
               f.v[i] = load_stream16(vbase + off + i * 1024);
+              if constexpr (DT == 2) {
+                f.ks[i] = p.ks[so + i * L::TPI];
+                f.vs[i] = p.vs[so + i * L::TPI];
+              }
             }
           } else {
   #pragma unroll
@@ -126,9 +154,16 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
               if (t >= t0 && t < t1) {
                 f.k[i] = load_stream16(kbase + off + i * 1024);
                 f.v[i] = load_stream16(vbase + off + i * 1024);
+                if constexpr (DT == 2) {
+                  f.ks[i] = p.ks[so + i * L::TPI];
+                  f.vs[i] = p.vs[so + i * L::TPI];
+                }
               } else {
+                // rows outside the split: zeros, never the (unread) slot's contents
                 f.k[i] = make_uint4(0, 0, 0, 0);
                 f.v[i] = make_uint4(0, 0, 0, 0);
+                f.ks[i] = 0.f;
+                f.vs[i] = 0.f;
               }
             }
           }
@@ -148,7 +183,15 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   #pragma unroll
             for (int g = 0; g < G; ++g) {
               float d;
-              if constexpr (DT == 1) {
+              if constexpr (DT == 2) {
+                const uint32_t w4[4] = {f.k[i].x, f.k[i].y, f.k[i].z, f.k[i].w};
+                float kf[16];
+  #pragma unroll
+                for (int w = 0; w < 4; ++w) fp8x4_to_f32(w4[w], kf + 4 * w);
+                d = qf[g][0] * kf[0];
+  #pragma unroll
+                for (int e = 1; e < 16; ++e) d = fmaf(qf[g][e], kf[e], d);
+              } else if constexpr (DT == 1) {
                 d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
                 d = dot2_bf16(f.k[i].y, qv[g].y, d);
                 d = dot2_bf16(f.k[i].z, qv[g].z, d);
@@ -160,6 +203,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
                 d = fmaf(__builtin_bit_cast(float, f.k[i].w), __builtin_bit_cast(float, qv[g].w), d);
               }
               dot[i][g] = group_sum<L::LPT>(d);
+              if constexpr (DT == 2) dot[i][g] *= f.ks[i];
             }
           }
 
@@ -197,7 +241,11 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   #pragma unroll
           for (int i = 0; i < L::NI; ++i) {
             float vf[L::EPL];
-            if constexpr (DT == 1) {
+            if constexpr (DT == 2) {
+              const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
+  #pragma unroll
+              for (int w = 0; w < 4; ++w) fp8x4_to_f32(w4[w], vf + 4 * w);
+            } else if constexpr (DT == 1) {
               const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
   #pragma unroll
               for (int k = 0; k < 4; ++k) {
@@ -212,8 +260,9 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
             }
   #pragma unroll
             for (int g = 0; g < G; ++g) {
+              const float pv = DT == 2 ? pw[i][g] * f.vs[i] : pw[i][g];
   #pragma unroll
-              for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pw[i][g], vf[k], acc[g][k]);
+              for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pv, vf[k], acc[g][k]);
             }
           }
         };
@@ -289,20 +338,23 @@ hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
 }  // namespace
 
 bool micro_supported(int dtype, int D, int G) {
-  return (dtype == 0 || dtype == 1) && (D == 64 || D == 128) &&
-         (G == 1 || G == 2 || G == 4 || G == 8);
+  if (D != 64 && D != 128) return false;
+  if (dtype == 2) return G == 1 || micro_mfma_supported(dtype, D, G);
+  return (dtype == 0 || dtype == 1) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
 long long micro_target_items(int dtype, int D, int G) {
   return micro_mfma_supported(dtype, D, G) ? 4096 : 1024;
 }
 
-// bf16 with grouped query heads goes to the matrix-core kernel; one query
-// head per KV head and fp32 K/V stay on the vector ALUs.
+// bf16 and fp8 with grouped query heads go to the matrix-core kernel; one
+// query head per KV head and fp32 K/V stay on the vector ALUs.
 hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream_t stream) {
   if (!micro_supported(dtype, D, G)) return hipErrorInvalidValue;
-  if (micro_mfma_supported(dtype, D, G)) return launch_micro_mfma(D, G, p, stream);
+  if (micro_mfma_supported(dtype, D, G)) return launch_micro_mfma(dtype, D, G, p, stream);
   if (dtype == 0) return D == 64 ? dispatch_g<0, 64>(G, p, stream) : dispatch_g<0, 128>(G, p, stream);
+  if (dtype == 2)  // fp8 pages: one query head per KV head here, groups on the matrix cores
+    return D == 64 ? launch_one<2, 64, 1>(p, stream) : launch_one<2, 128, 1>(p, stream);
   return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
 }
 

@@ -28,6 +28,13 @@
 //            dims x 4 heads, all four block rows useful for G >= 4.  The
 //            probabilities move from the score layout to that operand
 //            layout through a 16 x G float scratch in LDS per wave.
+//
+// fp8 (E4M3) pages with per-row scales take the same path: a lane's key codes
+// (8 dims per score step, the steps of a lane now contiguous: dims
+// grp*D/4 + 8*step, q in the same order) are widened exactly to bf16 for the
+// score MFMA and the score column is multiplied by its token's K scale; the
+// value codes (8 per lane, 8-byte loads in the same row layout) are widened
+// exactly to fp32 and a token's V scale multiplies its probability operand.
 #include "micro_common.h"
 
 namespace da {
@@ -36,21 +43,48 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+// DT: 1 = bf16 pages, 2 = fp8 E4M3 pages with per-row scales.  Either way a
+// value lane holds 8 dims of one token row (LPT lanes per row).
+template <int DT, int D>
 struct MLayout {
-  static constexpr int TOKB = D * 2;       // bf16 token row bytes
-  static constexpr int LPT = TOKB / 16;    // value lanes per token row
-  static constexpr int TPI = kWave / LPT;  // token rows per value load
-  static constexpr int NI = kSlab / TPI;   // value loads per slab
-  static constexpr int KS = D / 32;        // score k-steps
-  static constexpr int EPL = 8;            // bf16 elements per lane
+  static constexpr int TOKB = DT == 1 ? D * 2 : D;  // token row bytes
+  static constexpr int LPT = D / 8;                // value lanes per token row
+  static constexpr int TPI = kWave / LPT;          // token rows per value load
+  static constexpr int NI = kSlab / TPI;           // value loads per slab
+  static constexpr int KS = D / 32;                // score k-steps
+  static constexpr int KL = DT == 1 ? KS : KS / 2; // 16-byte key loads per lane
+  static constexpr int VB = 8 * (TOKB / D);        // value bytes per lane per load
+  static constexpr int EPL = 8;                    // elements per lane
 };
 
-template <int D>
+template <int DT, int D>
 struct MFrag {
-  uint4 k[MLayout<D>::KS];
-  uint4 v[MLayout<D>::NI];
+  uint4 k[MLayout<DT, D>::KL];
+  uint4 v[DT == 1 ? MLayout<DT, D>::NI : 1];  // bf16 values
+  uint2 v8[DT == 2 ? MLayout<DT, D>::NI : 1];  // fp8 values
+  float ksc;                                   // fp8: K scale of token `col`
+  float vsc[MLayout<DT, D>::NI];               // fp8: V scales of the value rows
 };
+
+// Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly:
+// every E4M3 value is a bf16 value, so the fp32 result's upper half is it.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  fp8x4_to_f32(w0, f);
+  fp8x4_to_f32(w1, f + 4);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (__builtin_bit_cast(uint32_t, f[2 * i]) >> 16) |
+           (__builtin_bit_cast(uint32_t, f[2 * i + 1]) & 0xFFFF0000u);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t.x, t.y);
+}
 
 template <bool B>
 using Bool = std::integral_constant<bool, B>;
@@ -70,10 +104,10 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // Two waves per SIMD: the register budget that holds the prefetched slab, the
 // query operand and the accumulators without spilling (measured faster than
 // three waves with spills).
-template <int D, int G>
+template <int DT, int D, int G>
 __global__ __launch_bounds__(kMicroThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
-  using L = MLayout<D>;
+  using L = MLayout<DT, D>;
   constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
   static_assert(G == 2 || G == 4 || G == 8, "group size");
   __shared__ int s_phys[kPageCap];
@@ -98,14 +132,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
     const int P = p.P;
     const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
-    // score operand A: lane l -> head l%16 (zero beyond G), dims chunk 4*step + l/16
+    // score operand A: lane l -> head l%16 (zero beyond G), 8 bf16 dims per
+    // step: chunk 4*step + l/16 (bf16 pages) or chunk KS*(l/16) + step (fp8)
     uint4 qa[L::KS];
   #pragma unroll
     for (int st = 0; st < L::KS; ++st) {
       qa[st] = make_uint4(0, 0, 0, 0);
       if (col < G) {
-        const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * L::TOKB +
-                         (size_t)(4 * st + grp) * 16;
+        const int chunk8 = DT == 1 ? 4 * st + grp : L::KS * grp + st;
+        const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * D * 2 +
+                         (size_t)chunk8 * 16;
         qa[st] = *reinterpret_cast<const uint4*>(qp);
       }
     }
@@ -126,40 +162,61 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       const int spp = P / kSlab;
       const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+      // key lane: token col; bf16: 16 bytes per step at 64*step + 16*grp;
+      // fp8: 8*KS contiguous bytes at 8*KS*grp
       const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB +
-                          (size_t)col * L::TOKB + (size_t)grp * 16;
-      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
+                          (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
+      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * L::VB;
+      const size_t scale_page = (size_t)p.Hkv * P;  // fp8: scales per physical page
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
         const int nslab = nk * spp;
 
-        auto load = [&](int sl, MFrag<D>& f) {
+        // key load j of a lane: bf16 64*j (one score step), fp8 16*j (two steps)
+        constexpr int KSTRIDE = DT == 1 ? 64 : 16;
+        constexpr int VSTRIDE = L::TPI * L::TOKB;  // bytes per value load
+        auto load = [&](int sl, MFrag<DT, D>& f) {
           const int kp = sl / spp;
           const int sub = sl - kp * spp;
           const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
+          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * kSlab;
           const int tb = s_lp[kp] * P + sub * kSlab;
-          if (tb >= t0 && tb + kSlab <= t1) {
+          if (tb >= t0 && tb + kSlab <= t1) {  // whole slab inside the split
   #pragma unroll
-            for (int st = 0; st < L::KS; ++st) f.k[st] = load_stream16(kbase + off + st * 64);
+            for (int j = 0; j < L::KL; ++j) f.k[j] = load_stream16(kbase + off + j * KSTRIDE);
+            if constexpr (DT == 2) f.ksc = p.ks[so + col];
   #pragma unroll
-            for (int i = 0; i < L::NI; ++i) f.v[i] = load_stream16(vbase + off + i * 1024);
-          } else {
+            for (int i = 0; i < L::NI; ++i) {
+              if constexpr (DT == 1) {
+                f.v[i] = load_stream16(vbase + off + i * VSTRIDE);
+              } else {
+                f.v8[i] = load_stream8(vbase + off + i * VSTRIDE);
+                f.vsc[i] = p.vs[so + i * L::TPI + vrow];
+              }
+            }
+          } else {  // tokens outside the split read as zeros (and zero scales)
             const int tk = tb + col;
             const bool kok = tk >= t0 && tk < t1;
   #pragma unroll
-            for (int st = 0; st < L::KS; ++st)
-              f.k[st] = kok ? load_stream16(kbase + off + st * 64) : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < L::KL; ++j)
+              f.k[j] = kok ? load_stream16(kbase + off + j * KSTRIDE) : make_uint4(0, 0, 0, 0);
+            if constexpr (DT == 2) f.ksc = kok ? p.ks[so + col] : 0.f;
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               const int tv = tb + i * L::TPI + vrow;
-              f.v[i] = (tv >= t0 && tv < t1) ? load_stream16(vbase + off + i * 1024)
-                                             : make_uint4(0, 0, 0, 0);
+              const bool vok = tv >= t0 && tv < t1;
+              if constexpr (DT == 1) {
+                f.v[i] = vok ? load_stream16(vbase + off + i * VSTRIDE) : make_uint4(0, 0, 0, 0);
+              } else {
+                f.v8[i] = vok ? load_stream8(vbase + off + i * VSTRIDE) : make_uint2(0, 0);
+                f.vsc[i] = vok ? p.vs[so + i * L::TPI + vrow] : 0.f;
+              }
             }
           }
         };
 
-        auto compute = [&](int sl, const MFrag<D>& f, auto full_tag) {
+        auto compute = [&](int sl, const MFrag<DT, D>& f, auto full_tag) {
           constexpr bool FULL = decltype(full_tag)::value;
           const int kp = sl / spp;
           const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
@@ -167,10 +224,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
           f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
   #pragma unroll
-          for (int st = 0; st < L::KS; ++st)
+          for (int st = 0; st < L::KS; ++st) {
+            uint4 kb;
+            if constexpr (DT == 1) {
+              kb = f.k[st];
+            } else {
+              const uint4& w = f.k[st / 2];
+              kb = (st & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+            }
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
-                                                        __builtin_bit_cast(bf16x8_t, f.k[st]), sc,
-                                                        0, 0, 0);
+                                                        __builtin_bit_cast(bf16x8_t, kb), sc, 0, 0, 0);
+          }
+          if constexpr (DT == 2) sc *= f.ksc;
           const bool kvalid = FULL || (tb + col >= t0 && tb + col < t1);
 
           // slab maxima per head, then the running maxima (wave-uniform)
@@ -229,24 +294,32 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           for (int j = 0; j < L::NI; ++j) {
             float pa[HS];
   #pragma unroll
-            for (int hs = 0; hs < HS; ++hs)
+            for (int hs = 0; hs < HS; ++hs) {
               pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
-            const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
+              if constexpr (DT == 2) pa[hs] *= f.vsc[j];
+            }
+            float vf[8];
+            if constexpr (DT == 1) {
+              const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
   #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float lo = bf16_lo(w4[k]);
-              const float hi = bf16_hi(w4[k]);
-  #pragma unroll
-              for (int hs = 0; hs < HS; ++hs) {
-                acc[hs][2 * k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], lo, acc[hs][2 * k], 0, 0, 0);
-                acc[hs][2 * k + 1] =
-                    __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], hi, acc[hs][2 * k + 1], 0, 0, 0);
+              for (int k = 0; k < 4; ++k) {
+                vf[2 * k] = bf16_lo(w4[k]);
+                vf[2 * k + 1] = bf16_hi(w4[k]);
               }
+            } else {
+              fp8x4_to_f32(f.v8[j].x, vf);
+              fp8x4_to_f32(f.v8[j].y, vf + 4);
+            }
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+  #pragma unroll
+              for (int hs = 0; hs < HS; ++hs)
+                acc[hs][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], vf[k], acc[hs][k], 0, 0, 0);
             }
           }
         };
 
-        auto step = [&](int sl, const MFrag<D>& f) {
+        auto step = [&](int sl, const MFrag<DT, D>& f) {
           const int kp = sl / spp;
           const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
           if (tb >= t0 && tb + kSlab <= t1)
@@ -255,7 +328,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             compute(sl, f, Bool<false>{});
         };
 
-        MFrag<D> fa, fb;
+        MFrag<DT, D> fa, fb;
         int sl = wave;
         if (sl < nslab) load(sl, fa);
         while (sl < nslab) {
@@ -303,17 +376,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 // Resident workgroups per CU (measured best for the grouped-query workload).
 constexpr int kMfmaWorkgroupsPerCU = 2;
 
-template <int D, int G>
+template <int DT, int D, int G>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_kernel(micro_mfma_kernel<D, G>, kMfmaWorkgroupsPerCU, p, stream);
+  return launch_micro_kernel(micro_mfma_kernel<DT, D, G>, kMfmaWorkgroupsPerCU, p, stream);
 }
 
-template <int D>
+template <int DT, int D>
 hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
   switch (G) {
-    case 2: return launch_one<D, 2>(p, stream);
-    case 4: return launch_one<D, 4>(p, stream);
-    case 8: return launch_one<D, 8>(p, stream);
+    case 2: return launch_one<DT, D, 2>(p, stream);
+    case 4: return launch_one<DT, D, 4>(p, stream);
+    case 8: return launch_one<DT, D, 8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -321,11 +394,12 @@ hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
 }  // namespace
 
 bool micro_mfma_supported(int dtype, int D, int G) {
-  return dtype == 1 && (D == 64 || D == 128) && (G == 2 || G == 4 || G == 8);
+  return (dtype == 1 || dtype == 2) && (D == 64 || D == 128) && (G == 2 || G == 4 || G == 8);
 }
 
-hipError_t launch_micro_mfma(int D, int G, const MicroParams& p, hipStream_t stream) {
-  return D == 64 ? dispatch_g<64>(G, p, stream) : dispatch_g<128>(G, p, stream);
+hipError_t launch_micro_mfma(int dtype, int D, int G, const MicroParams& p, hipStream_t stream) {
+  if (dtype == 2) return D == 64 ? dispatch_g<2, 64>(G, p, stream) : dispatch_g<2, 128>(G, p, stream);
+  return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
 }
 
 }  // namespace da

@@ -226,3 +226,50 @@ def test_split_bounds_rejects(lib, case, status):
     got = lib.da_split_bounds(ctypes.byref(sh), _vp(p["mask"]), _vp(p["lens"]),
                               case.get("horizon", 0), _vp(p["out"]), None)
     assert got == status, _lib.load().da_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(dtype=_lib.DA_BF16)), _lib.DA_ERR_INVALID_ARG),  # needs DA_FP8_E4M3
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),  # G = 3
+    (dict(ptrs=dict(ks=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(vs=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(k=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_micro_attention_fp8_rejects(lib, case, status):
+    sh = good_shape(**{"dtype": _lib.DA_FP8_E4M3, **case.get("shape", {})})
+    p = dict(q=FAKE, k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, table=FAKE, lens=FAKE, bounds=FAKE,
+             mask=None, MA=FAKE, m=FAKE, e=FAKE, ws=None)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_micro_attention_fp8(ctypes.byref(sh), *[_vp(p[k]) for k in
+                                                         ("q", "k", "ks", "v", "vs", "table", "lens",
+                                                          "bounds", "mask", "MA", "m", "e", "ws")],
+                                     0, None)
+    assert got == status, _lib.load().da_last_error()
+
+
+def test_fp8_dtype_refused_by_the_bf16_entry_point(lib):
+    sh = good_shape(dtype=_lib.DA_FP8_E4M3)
+    assert call_micro(lib, sh) == _lib.DA_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((2, 10, 96), _lib.DA_ERR_UNSUPPORTED),
+    ((1, -1, 128), _lib.DA_ERR_INVALID_ARG),
+    ((5, 10, 128), _lib.DA_ERR_INVALID_ARG),
+    ((1, 0, 128), _lib.DA_OK),  # nothing to do
+])
+def test_quantize_rows_rejects(lib, args, status):
+    dtype, rows, D = args
+    dtype = _lib.DA_F32 if dtype == 2 else dtype
+    got = lib.da_quantize_rows(dtype, rows, D, _vp(FAKE), _vp(FAKE), _vp(FAKE), None)
+    assert got == status, _lib.load().da_last_error()
+
+
+def test_quantize_rows_misaligned(lib):
+    got = lib.da_quantize_rows(_lib.DA_BF16, 4, 128, _vp(FAKE + 8), _vp(FAKE), _vp(FAKE), None)
+    assert got == _lib.DA_ERR_INVALID_ARG
+    got = lib.da_quantize_rows(_lib.DA_BF16, 4, 128, _vp(FAKE), _vp(FAKE + 4), _vp(FAKE), None)
+    assert got == _lib.DA_ERR_INVALID_ARG
