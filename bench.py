@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C4", help="headline workload (C2, C3, C4, C5)")
-    ap.add_argument("--secondary", default="C5", help="comma list reported beside it, or ''")
+    ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8",
+                    help="comma list reported beside it ('_fp8': over 8-bit pages), or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
@@ -79,23 +80,39 @@ def parse():
 
 
 def time_workload(key, steps, warmup, dev):
+    """Times the decode step of workload `key`; a "_fp8" suffix runs it over
+    8-bit pages made from the workload's bf16 pools by da_quantize_rows
+    (quantization is untimed: it belongs to the cache write)."""
     import torch
 
     from long_context_decode_microattention_amd import _lib
     from long_context_decode_microattention_amd import workloads as wl
 
-    spec = wl.CONFIGS[key]
+    fp8 = key.endswith("_fp8")
+    spec = wl.CONFIGS[key[:-4] if fp8 else key]
     t0 = time.time()
     b = wl.build(spec, 0, dev)
     torch.cuda.synchronize()
     log(f"[bench] built {key} in {time.time() - t0:.1f}s: NP={b.k_pages.shape[0]}")
-    kv_bytes = b.kv_bytes()
     S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
+    kept = int(b.kept_tokens().sum())
+    if fp8:
+        kc, ks = _lib.quantize_rows(b.k_pages)
+        vc, vs = _lib.quantize_rows(b.v_pages)
+        torch.cuda.synchronize()
+        b.k_pages = b.v_pages = None  # the bf16 pools are not needed any more
+        torch.cuda.empty_cache()
+        kv_bytes = kept * 2 * (D + 4)  # an 8-bit row of D codes plus its fp32 scale, K and V
+        micro = _lib.micro_attention_fp8
+        args = (b.q, kc, ks, vc, vs, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
+    else:
+        kv_bytes = b.kv_bytes()
+        micro = _lib.micro_attention
+        args = (b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
     MA = torch.empty((S, Hq, B, D), dtype=torch.float32, device=dev)
     m = torch.empty((S, Hq, B), dtype=torch.float32, device=dev)
     e = torch.empty((S, Hq, B), dtype=torch.float32, device=dev)
     out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
-    args = (b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
 
     # a plain copy of known size (1 GiB): the yardstick for the HBM byte counters
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -104,7 +121,7 @@ def time_workload(key, steps, warmup, dev):
     del src, dst
 
     for _ in range(warmup):
-        _lib.micro_attention(*args, scale=b.scale, out=(MA, m, e))
+        micro(*args, scale=b.scale, out=(MA, m, e))
         _lib.merge(MA, m, e, out=out)
     torch.cuda.synchronize()
 
@@ -112,7 +129,7 @@ def time_workload(key, steps, warmup, dev):
     torch.cuda.synchronize()
     for i in range(steps):
         ev[3 * i].record()
-        _lib.micro_attention(*args, scale=b.scale, out=(MA, m, e))
+        micro(*args, scale=b.scale, out=(MA, m, e))
         ev[3 * i + 1].record()
         _lib.merge(MA, m, e, out=out)
         ev[3 * i + 2].record()
@@ -129,8 +146,11 @@ def time_workload(key, steps, warmup, dev):
         us_per_step=ms_step * 1e3, us_micro=avg_micro * 1e3, us_merge=avg_merge * 1e3,
         us_micro_min=min(micro_ms) * 1e3, merge_share=avg_merge / (avg_micro + avg_merge),
         GBps=kv_bytes / (ms_step * 1e-3) / 1e9, micro_GBps=kv_bytes / (avg_micro * 1e-3) / 1e9,
-        shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B, kv_dtype=spec.dtype,
+        shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B,
+                   kv_dtype="fp8_e4m3+f32 row scale" if fp8 else spec.dtype,
                    max_len=spec.max_len, block_mask=spec.mask is not None),
+        kept_tokens=kept,
+        tokens_per_s=kept / (ms_step * 1e-3),
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
     return b, res
@@ -428,10 +448,11 @@ def main():
     _lib.load()
 
     b, head = time_workload(a.workload, a.steps, a.warmup, dev)
-    ceiling = None if a.no_ceiling else read_ceiling(b)
-    cpu = None if a.no_cpu_baseline else cpu_baseline(b, a.cpu_budget)
+    bf16_pools = b.k_pages is not None  # an "_fp8" headline keeps only the 8-bit pools
+    ceiling = None if a.no_ceiling or not bf16_pools else read_ceiling(b)
+    cpu = None if a.no_cpu_baseline or not bf16_pools else cpu_baseline(b, a.cpu_budget)
     head_selector = None
-    if b.spec.mask is not None and not a.no_selector:
+    if b.spec.mask is not None and not a.no_selector and bf16_pools:
         head_selector = time_selector(b, a.steps, a.warmup, dev)
         head_selector["decode_loop"] = time_decode_chunks(b, a.chunks, dev)
     del b
@@ -442,7 +463,7 @@ def main():
         r2["roofline_frac"] = r2["micro_GBps"] / HBM_PEAK_GBPS
         r2["traffic"] = measured_traffic(key)
         secondary[key] = r2
-        if b2.spec.mask is not None and not a.no_selector:
+        if b2.spec.mask is not None and not a.no_selector and b2.k_pages is not None:
             secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
             secondary[key + "_selector"]["decode_loop"] = time_decode_chunks(b2, a.chunks, dev)
         del b2

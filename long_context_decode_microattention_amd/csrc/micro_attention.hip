@@ -37,33 +37,35 @@ bool micro_mfma_supported(int dtype, int D, int G);
 
 namespace {
 
-// DT: 0 = fp32, 1 = bf16, 2 = fp8 E4M3 with per-row scales.
-template <int DT, int D>
+// DT: 0 = fp32, 1 = bf16, 2 = fp8 E4M3 with per-row scales.  SL: tokens per
+// slab (16; 32 for fp8 pages when the page size allows, so a slab moves as
+// many bytes as a 16-token bf16 slab and as many stay in flight).
+template <int DT, int D, int SL>
 struct Layout {
   static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);  // bytes per element
   static constexpr int TOKB = D * ES;          // bytes per token row
   static constexpr int LPT = TOKB / 16;        // lanes per token row
   static constexpr int TPI = kWave / LPT;      // token rows per wave load
   static constexpr int EPL = 16 / ES;          // elements per lane
-  static constexpr int NI = kSlab / TPI;       // wave loads per slab per tensor
+  static constexpr int NI = SL / TPI;          // wave loads per slab per tensor
   static_assert(TPI * TOKB == kWave * 16, "wave load covers whole rows");
-  static_assert(NI >= 1 && kSlab % TPI == 0, "slab covers whole wave loads");
+  static_assert(NI >= 1 && SL % TPI == 0, "slab covers whole wave loads");
 };
 
-template <int DT, int D>
+template <int DT, int D, int SL>
 struct Frag {
-  uint4 k[Layout<DT, D>::NI];
-  uint4 v[Layout<DT, D>::NI];
-  float ks[Layout<DT, D>::NI];  // fp8: K and V scales of this lane's token rows
-  float vs[Layout<DT, D>::NI];
+  uint4 k[Layout<DT, D, SL>::NI];
+  uint4 v[Layout<DT, D, SL>::NI];
+  float ks[Layout<DT, D, SL>::NI];  // fp8: K and V scales of this lane's token rows
+  float vs[Layout<DT, D, SL>::NI];
 };
 
 template <bool B>
 using Bool = std::integral_constant<bool, B>;
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int SL>
 __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
-  using L = Layout<DT, D>;
+  using L = Layout<DT, D, SL>;
   __shared__ int s_phys[kPageCap];
   __shared__ int s_lp[kPageCap];
   __shared__ int s_cnt[kMicroWaves];
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
 
     if (it.scan0 < it.scan1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
-      const int spp = P / kSlab;  // slabs per page
+      const int spp = P / SL;  // slabs per page
       const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
       const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
       const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
@@ -130,14 +132,14 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
         // ---- stream the piece's slabs: wave w takes slabs w, w+4, ... ----
         const int nslab = nk * spp;
 
-        auto load = [&](int sl, Frag<DT, D>& f) {
+        auto load = [&](int sl, Frag<DT, D, SL>& f) {
           const int kp = sl / spp;
           const int sub = sl - kp * spp;
-          const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
-          const int tb = s_lp[kp] * P + sub * kSlab;
-          // fp8: the scales of this lane's token rows (slot sub*kSlab + i*TPI + row)
-          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * kSlab + row;
-          if (tb >= t0 && tb + kSlab <= t1) {
+          const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (SL * L::TOKB);
+          const int tb = s_lp[kp] * P + sub * SL;
+          // fp8: the scales of this lane's token rows (slot sub*SL + i*TPI + row)
+          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * SL + row;
+          if (tb >= t0 && tb + SL <= t1) {
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               f.k[i] = load_stream16(kbase + off + i * 1024);
@@ -170,11 +172,11 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
         };
 
         // FULL: every token of the slab lies inside [t0, t1)
-        auto compute = [&](int sl, const Frag<DT, D>& f, auto full_tag) {
+        auto compute = [&](int sl, const Frag<DT, D, SL>& f, auto full_tag) {
           constexpr bool FULL = decltype(full_tag)::value;
           const int kp = sl / spp;
           const int sub = sl - kp * spp;
-          const int tb = s_lp[kp] * P + sub * kSlab;
+          const int tb = s_lp[kp] * P + sub * SL;
 
           // scores: dot[i][g] for this row's token of wave load i
           float dot[L::NI][G];
@@ -267,26 +269,40 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
           }
         };
 
-        auto step = [&](int sl, const Frag<DT, D>& f) {
+        auto step = [&](int sl, const Frag<DT, D, SL>& f) {
           const int kp = sl / spp;
-          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
-          if (tb >= t0 && tb + kSlab <= t1)
+          const int tb = s_lp[kp] * P + (sl - kp * spp) * SL;
+          if (tb >= t0 && tb + SL <= t1)
             compute(sl, f, Bool<true>{});
           else
             compute(sl, f, Bool<false>{});
         };
 
-        // two slabs in flight ahead of the one being computed
-        Frag<DT, D> f0, f1, f2;
-        int sl = wave;
-        if (sl < nslab) load(sl, f0);
-        if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
-        while (sl < nslab) {
-          if (sl + 2 * kMicroWaves < nslab) load(sl + 2 * kMicroWaves, f2);
-          step(sl, f0);
-          f0 = f1;
-          f1 = f2;
-          sl += kMicroWaves;
+        if constexpr (SL == kSlab) {
+          // two slabs in flight ahead of the one being computed
+          Frag<DT, D, SL> f0, f1, f2;
+          int sl = wave;
+          if (sl < nslab) load(sl, f0);
+          if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
+          while (sl < nslab) {
+            if (sl + 2 * kMicroWaves < nslab) load(sl + 2 * kMicroWaves, f2);
+            step(sl, f0);
+            f0 = f1;
+            f1 = f2;
+            sl += kMicroWaves;
+          }
+        } else {
+          // double-length fp8 slabs: one in flight ahead keeps the register
+          // budget of two waves per SIMD
+          Frag<DT, D, SL> f0, f1;
+          int sl = wave;
+          if (sl < nslab) load(sl, f0);
+          while (sl < nslab) {
+            if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
+            step(sl, f0);
+            f0 = f1;
+            sl += kMicroWaves;
+          }
         }
         __syncthreads();  // the page list is rewritten by the next batch
       }
@@ -319,9 +335,9 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
 // Resident workgroups per CU (0: as many as registers allow).
 constexpr int kValuWorkgroupsPerCU = 0;
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int SL = kSlab>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_kernel(micro_kernel<DT, D, G>, kValuWorkgroupsPerCU, p, stream);
+  return launch_micro_kernel(micro_kernel<DT, D, G, SL>, kValuWorkgroupsPerCU, p, stream);
 }
 
 template <int DT, int D>
@@ -353,8 +369,11 @@ hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream
   if (!micro_supported(dtype, D, G)) return hipErrorInvalidValue;
   if (micro_mfma_supported(dtype, D, G)) return launch_micro_mfma(dtype, D, G, p, stream);
   if (dtype == 0) return D == 64 ? dispatch_g<0, 64>(G, p, stream) : dispatch_g<0, 128>(G, p, stream);
-  if (dtype == 2)  // fp8 pages: one query head per KV head here, groups on the matrix cores
+  if (dtype == 2) {  // fp8 pages: one query head per KV head here, groups on the matrix cores
+    if (p.P % 32 == 0)
+      return D == 64 ? launch_one<2, 64, 1, 32>(p, stream) : launch_one<2, 128, 1, 32>(p, stream);
     return D == 64 ? launch_one<2, 64, 1>(p, stream) : launch_one<2, 128, 1>(p, stream);
+  }
   return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
 }
 

@@ -328,19 +328,36 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             compute(sl, f, Bool<false>{});
         };
 
-        MFrag<DT, D> fa, fb;
-        int sl = wave;
-        if (sl < nslab) load(sl, fa);
-        while (sl < nslab) {
-          int sn = sl + kMicroWaves;
-          if (sn < nslab) load(sn, fb);
-          step(sl, fa);
-          sl = sn;
-          if (sl >= nslab) break;
-          sn = sl + kMicroWaves;
-          if (sn < nslab) load(sn, fa);
-          step(sl, fb);
-          sl = sn;
+        if constexpr (DT == 1) {
+          // bf16: one slab in flight while the other is computed
+          MFrag<DT, D> fa, fb;
+          int sl = wave;
+          if (sl < nslab) load(sl, fa);
+          while (sl < nslab) {
+            int sn = sl + kMicroWaves;
+            if (sn < nslab) load(sn, fb);
+            step(sl, fa);
+            sl = sn;
+            if (sl >= nslab) break;
+            sn = sl + kMicroWaves;
+            if (sn < nslab) load(sn, fa);
+            step(sl, fb);
+            sl = sn;
+          }
+        } else {
+          // fp8: a slab carries half the bytes, so two are kept in flight
+          // (the 8-bit fragments fit the same register budget)
+          MFrag<DT, D> f0, f1, f2;
+          int sl = wave;
+          if (sl < nslab) load(sl, f0);
+          if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
+          while (sl < nslab) {
+            if (sl + 2 * kMicroWaves < nslab) load(sl + 2 * kMicroWaves, f2);
+            step(sl, f0);
+            f0 = f1;
+            f1 = f2;
+            sl += kMicroWaves;
+          }
         }
         __syncthreads();  // the page list is rewritten by the next batch
       }
