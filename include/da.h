@@ -175,6 +175,21 @@ da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x
                            uint8_t* codes, float* scales, hipStream_t stream);
 
 /*
+ * Decode-time append into 8-bit pages: the write of da_append_kv (token
+ * t = seq_lens[s] of every request with 0 <= t < max_pages * P, through the
+ * block table; seq_lens is not advanced) for pools of OCP FP8 E4M3 codes
+ * with per-row scales.  The new rows k_new, v_new ([S, Hkv, D] of sh->dtype,
+ * DA_F32 or DA_BF16, 16-byte aligned) are quantized exactly as
+ * da_quantize_rows does, and their codes and scales are written to
+ * k_codes / v_codes ([NP, Hkv, P, D] uint8, 8-byte aligned) and k_scales /
+ * v_scales ([NP, Hkv, P] float32) at the token's slot.  Reads sh->S, Hkv,
+ * D, P, NP, max_pages, dtype.  Supported: D 64 or 128.
+ */
+da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
+                           float* k_scales, uint8_t* v_codes, float* v_scales, hipStream_t stream);
+
+/*
  * Aggregate b partials per (request, query head) into attention output.
  *
  *   MA [S, Hq, b, D], m [S, Hq, b], e [S, Hq, b] float32 as written by

@@ -93,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.da_quantize_rows.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP,
                                      _VP]
     lib.da_quantize_rows.restype = ctypes.c_int
+    lib.da_append_kv_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.da_append_kv_fp8.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
     lib.da_stream_read_sink_words.argtypes = []
@@ -448,6 +450,33 @@ def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=No
     _check(load().da_append_kv(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                _ptr(seq_lens), _ptr(k_pages), _ptr(v_pages), int(logical),
                                _ptr(select_heads), _ptr(stats), _stream(dev)))
+
+
+def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales):
+    """Quantize each request's new K/V rows ([S, Hkv, D], bf16 or float32)
+    and write their codes and scales at position seq_lens[s] of the 8-bit
+    pools in place via da_append_kv_fp8.  seq_lens is not advanced."""
+    dev = k_codes.device
+    _need(k_codes, "k_codes", torch.uint8, dev, 4)
+    _need(v_codes, "v_codes", torch.uint8, dev, 4)
+    if v_codes.shape != k_codes.shape:
+        raise ValueError("k_codes and v_codes differ in shape")
+    NP, Hkv, P, D = k_codes.shape
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.float32, dev, 3)
+        if tuple(t.shape) != (NP, Hkv, P):
+            raise ValueError(f"{name} must be [NP, Hkv, P]")
+    S = block_table.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, k_new.dtype, dev, 3)
+        if tuple(t.shape) != (S, Hkv, D):
+            raise ValueError(f"{name} must be [S, Hkv, D] = {(S, Hkv, D)}")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_new))
+    _check(load().da_append_kv_fp8(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                                   _ptr(seq_lens), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                   _ptr(v_scales), _stream(dev)))
 
 
 def split_bounds(block_mask, seq_lens, *, P: int, b: int, horizon: int = 0, Hkv=None,

@@ -428,6 +428,45 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
   return DA_OK;
 }
 
+da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
+                           float* k_scales, uint8_t* v_codes, float* v_scales, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d D=%d P=%d max_pages=%d NP=%lld)",
+                sh->S, sh->Hkv, sh->D, sh->P, sh->max_pages, (long long)sh->NP);
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
+    return fail(DA_ERR_INVALID_ARG, "dtype of the new rows must be DA_F32 or DA_BF16 (got %d)", sh->dtype);
+  if ((long long)sh->max_pages * sh->P > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->S * sh->Hkv > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
+  if (!da::quantize_supported(sh->dtype, sh->D))
+    return fail(DA_ERR_UNSUPPORTED, "8-bit append not built for D=%d (64, 128)", sh->D);
+  if (!k_new || !v_new || !block_table || !seq_lens || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_codes, 8) || !aligned(v_codes, 8))
+    return fail(DA_ERR_INVALID_ARG, "new rows must be 16-byte and code pools 8-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
+  da::AppendFp8Params p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.table = block_table;
+  p.lens = seq_lens;
+  p.k_codes = k_codes;
+  p.k_scales = k_scales;
+  p.v_codes = v_codes;
+  p.v_scales = v_scales;
+  p.S = sh->S;
+  p.Hkv = sh->Hkv;
+  p.P = sh->P;
+  p.max_pages = sh->max_pages;
+  const hipError_t err = da::launch_append_kv_fp8(p, sh->dtype, sh->D, stream);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "8-bit append launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
 da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
                           int32_t horizon, int32_t* split_bounds, hipStream_t stream) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");

@@ -8,6 +8,9 @@
 //                      written, adding no decode latency): the first token of
 //                      a logical page sets kmax = kmin = k, later tokens fold
 //                      into them with max / min (exact: stored values).
+// append_kv_fp8_kernel the same write for 8-bit pages: the new rows are
+//                      quantized (one scale per row, fp8_rows.h) and their
+//                      codes and scales stored at the token's slot.
 // split_bounds_kernel  split bounds over a head's kept pages (b splits, split
 //                      j starting at the kept page of ordinal floor(j K / b)),
 //                      computed on the device from the mask so a selection
@@ -15,10 +18,10 @@
 //                      page, section 2.2.2, reusable page selector) never
 //                      waits on the host.
 //
-// Both are tiny next to the attention step (one row per head, one mask row
-// per head); they are written for latency: one wave per (request, KV head)
-// for the append, one workgroup per mask row for the bounds.
-#include "device_common.h"
+// All three are tiny next to the attention step (one row per head, one mask
+// row per head); they are written for latency: one wave per (request, KV
+// head) for the appends, one workgroup per mask row for the bounds.
+#include "fp8_rows.h"
 #include "launch.h"
 
 namespace da {
@@ -91,6 +94,40 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_kernel(AppendP
   }
 }
 
+// One wave per (request, KV head) for 8-bit pages: lanes [0, LPR) quantize
+// the new key row, lanes [LPR, 2 LPR) the value row (each group sits inside
+// one DPP row, so its maximum is a DPP reduction); the other lanes idle.
+template <int DT, int D>
+__global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(AppendFp8Params p) {
+  constexpr int LPR = D / 8;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  const int item = blockIdx.x * kAppendWaves + threadIdx.x / kWave;
+  if (item >= p.S * p.Hkv) return;  // wave-uniform
+  const int s = item / p.Hkv;
+  const int kvh = item - s * p.Hkv;
+  const int t = p.lens[s];
+  if (t < 0 || t >= p.max_pages * p.P) return;  // full cache: nothing is written
+  const int lp = t / p.P;
+  const int slot = t - lp * p.P;
+  const long long phys = p.table[(size_t)s * p.max_pages + lp];
+  const int lane = threadIdx.x % kWave;
+  const int part = lane / LPR;  // 0 = key row, 1 = value row, else idle
+  const int col = lane % LPR;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (part < 2) {
+    const void* src = part == 0 ? p.k_new : p.v_new;
+    load8<DT>(static_cast<const char*>(src) + (((size_t)s * p.Hkv + kvh) * D + col * 8) * ES, v);
+  }
+  float sc;
+  const uint2 c = quantize8<LPR>(v, sc);
+  if (part < 2) {
+    const size_t row = ((size_t)phys * p.Hkv + kvh) * p.P + slot;
+    uint8_t* codes = part == 0 ? p.k_codes : p.v_codes;
+    *reinterpret_cast<uint2*>(codes + row * D + col * 8) = c;
+    if (col == 0) (part == 0 ? p.k_scales : p.v_scales)[row] = sc;
+  }
+}
+
 // One workgroup per (request, KV head).  Pages [0, n) with n = ceil(E / P),
 // E = min(L + horizon, capacity), are split into contiguous per-thread
 // chunks (thread order = page order); a block-wide exclusive scan of the
@@ -159,6 +196,18 @@ hipError_t launch_append_kv(const AppendParams& p, int dtype, int D, hipStream_t
   else if (dtype == 0 && D == 128) hipLaunchKernelGGL((append_kv_kernel<0, 128>), g, b, 0, stream, p);
   else if (dtype == 1 && D == 64) hipLaunchKernelGGL((append_kv_kernel<1, 64>), g, b, 0, stream, p);
   else if (dtype == 1 && D == 128) hipLaunchKernelGGL((append_kv_kernel<1, 128>), g, b, 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv_fp8(const AppendFp8Params& p, int dtype, int D, hipStream_t stream) {
+  const long long items = (long long)p.S * p.Hkv;
+  if (items < 1) return hipSuccess;
+  const dim3 g((unsigned)((items + kAppendWaves - 1) / kAppendWaves)), b(kAppendWaves * kWave);
+  if (dtype == 0 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 64>), g, b, 0, stream, p);
+  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 128>), g, b, 0, stream, p);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 64>), g, b, 0, stream, p);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 128>), g, b, 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

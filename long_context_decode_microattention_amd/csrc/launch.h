@@ -92,6 +92,17 @@ struct AppendParams {
   long long NP;
   int S, Hkv, P, max_pages, logical;
 };
+struct AppendFp8Params {
+  const void* k_new;  // [S, Hkv, D], bf16 or fp32
+  const void* v_new;
+  const int32_t* table;
+  const int32_t* lens;
+  uint8_t* k_codes;   // [NP, Hkv, P, D]
+  float* k_scales;    // [NP, Hkv, P]
+  uint8_t* v_codes;
+  float* v_scales;
+  int S, Hkv, P, max_pages;
+};
 struct BoundsParams {
   const uint8_t* mask;  // [S, Hkv, max_pages] or null (every page kept)
   const int32_t* lens;
@@ -100,6 +111,7 @@ struct BoundsParams {
 };
 bool append_supported(int dtype, int D);
 hipError_t launch_append_kv(const AppendParams& p, int dtype, int D, hipStream_t stream);
+hipError_t launch_append_kv_fp8(const AppendFp8Params& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_split_bounds(const BoundsParams& p, hipStream_t stream);
 
 // 8-bit KV rows (quant.hip).

@@ -273,3 +273,22 @@ def test_quantize_rows_misaligned(lib):
     assert got == _lib.DA_ERR_INVALID_ARG
     got = lib.da_quantize_rows(_lib.DA_BF16, 4, 128, _vp(FAKE), _vp(FAKE + 4), _vp(FAKE), None)
     assert got == _lib.DA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(S=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(dtype=_lib.DA_FP8_E4M3)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(ptrs=dict(ks=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(k_new=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(kc=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(vs=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+])
+def test_append_kv_fp8_rejects(lib, case, status):
+    sh = good_shape(**case.get("shape", {}))
+    p = dict(k_new=FAKE, v_new=FAKE, table=FAKE, lens=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_append_kv_fp8(ctypes.byref(sh), *[_vp(p[k]) for k in
+                                                   ("k_new", "v_new", "table", "lens", "kc", "ks",
+                                                    "vc", "vs")], None)
+    assert got == status, _lib.load().da_last_error()

@@ -214,3 +214,72 @@ def test_fp8_full_size_sampled(cfg):
                                 block_mask=mask, scale=b.scale)
         got = out[s:s + 1, kvh * G:(kvh + 1) * G].cpu().numpy()
         compare_out(got, want, TOL, f"unit ({s},{kvh})")
+
+
+def _host_append_fp8(codes, scales, table, lens, new_rows):
+    """Oracle of an 8-bit append: quantize the new rows, then write codes and
+    scales through the table (scales as one-element rows)."""
+    import oracle.decode as odec
+    c_new, s_new = oq.quantize_rows(new_rows)
+    c2, s2 = odec.append_kv(codes, scales[..., None], table, lens, c_new, s_new[..., None])
+    return c2, s2[..., 0]
+
+
+@pytest.mark.parametrize("cfg", ["C4", "C5", "C5_G2_D64"])
+def test_append_fp8_matches_oracle(cfg):
+    """Consecutive 8-bit appends across a page boundary: after every step the
+    code and scale pools equal the oracle's (quantize the new rows, write them
+    through the table) bit for bit."""
+    spec = CASES[cfg].replace(reserve=24, table="shuffled", extra_pages=2)
+    announce("fp8 append", cfg)
+    b = wl.build(spec, 4, DEV)
+    (kc, ks, vc, vs), _ = _quantized(b)
+    h = wl.host
+    table = h(b.block_table)
+    okc, oks, ovc, ovs = h(kc), h(ks), h(vc), h(vs)
+    lens = b.seq_lens.clone()
+    for step in range(20):
+        kn, vn = wl.new_tokens(spec, 4, step, DEV)
+        _lib.append_kv_fp8(kn, vn, b.block_table, lens, kc, ks, vc, vs)
+        L = h(lens)
+        okc, oks = _host_append_fp8(okc, oks, table, L, h(kn))
+        ovc, ovs = _host_append_fp8(ovc, ovs, table, L, h(vn))
+        lens += 1
+        torch.cuda.synchronize()
+        assert np.array_equal(h(kc), okc) and np.array_equal(h(vc), ovc), f"{cfg} step {step}: codes"
+        assert np.array_equal(h(ks), oks) and np.array_equal(h(vs), ovs), f"{cfg} step {step}: scales"
+
+
+def test_fp8_decode_chunk():
+    """16 decode steps over 8-bit pages with a reused mask: split bounds once
+    (horizon 16), then per step an 8-bit append and the attention step; every
+    step's output matches the oracle's attention over the oracle's pools."""
+    import oracle.decode as odec
+    chunk = 16
+    spec = CASES["C5"].replace(lens=("fixed", 64 * 40 + 57), reserve=chunk)
+    announce("fp8 decode chunk")
+    b = wl.build(spec, 5, DEV)
+    (kc, ks, vc, vs), _ = _quantized(b)
+    h = wl.host
+    table = h(b.block_table)
+    mask = b.block_mask.clone()
+    # keep the pages the chunk's tokens open (the horizon of a reused selection)
+    L0 = int(b.seq_lens[0].item())
+    mask[:, :, L0 // spec.P:-(-(L0 + chunk) // spec.P)] = 1
+    lens = b.seq_lens.clone()
+    bounds = _lib.split_bounds(mask, lens, P=spec.P, b=8, horizon=chunk)
+    okc, oks, ovc, ovs = h(kc), h(ks), h(vc), h(vs)
+    mask_h = h(mask)
+    for step in range(chunk):
+        kn, vn = wl.new_tokens(spec, 5, step, DEV)
+        _lib.append_kv_fp8(kn, vn, b.block_table, lens, kc, ks, vc, vs)
+        okc, oks = _host_append_fp8(okc, oks, table, h(lens), h(kn))
+        ovc, ovs = _host_append_fp8(ovc, ovs, table, h(lens), h(vn))
+        lens += 1
+        MA, m, e = _lib.micro_attention_fp8(b.q, kc, ks, vc, vs, b.block_table, lens, bounds, mask,
+                                            scale=b.scale)
+        out = _lib.merge(MA, m, e)
+        torch.cuda.synchronize()
+        want = oracle.attention(h(b.q), oq.dequantize(okc, oks), oq.dequantize(ovc, ovs), table,
+                                h(lens), block_mask=mask_h, scale=b.scale)
+        compare_out(out.cpu().numpy(), want, TOL, f"fp8 chunk step {step}")
