@@ -182,12 +182,17 @@ da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x
  * DA_F32 or DA_BF16, 16-byte aligned) are quantized exactly as
  * da_quantize_rows does, and their codes and scales are written to
  * k_codes / v_codes ([NP, Hkv, P, D] uint8, 8-byte aligned) and k_scales /
- * v_scales ([NP, Hkv, P] float32) at the token's slot.  Reads sh->S, Hkv,
- * D, P, NP, max_pages, dtype.  Supported: D 64 or 128.
+ * v_scales ([NP, Hkv, P] float32) at the token's slot.  If stats is not
+ * NULL ([Hkv, NP, P / logical, 2, D] of sh->dtype, as for da_page_stats),
+ * the statistics of the receiving logical page are kept current from the
+ * full-precision key row exactly as da_append_kv does (select_heads and
+ * logical as there), so page selection keeps working on 8-bit pools.  Reads
+ * sh->S, Hkv, D, P, NP, max_pages, dtype.  Supported: D 64 or 128.
  */
 da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
-                           float* k_scales, uint8_t* v_codes, float* v_scales, hipStream_t stream);
+                           float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
+                           const uint8_t* select_heads, void* stats, hipStream_t stream);
 
 /*
  * Aggregate b partials per (request, query head) into attention output.

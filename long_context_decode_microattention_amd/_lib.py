@@ -93,7 +93,8 @@ def load() -> ctypes.CDLL:
     lib.da_quantize_rows.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP,
                                      _VP]
     lib.da_quantize_rows.restype = ctypes.c_int
-    lib.da_append_kv_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.da_append_kv_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32,
+                                     _VP, _VP, _VP]
     lib.da_append_kv_fp8.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
@@ -452,10 +453,13 @@ def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=No
                                _ptr(select_heads), _ptr(stats), _stream(dev)))
 
 
-def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales):
+def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales, *,
+                  stats=None, logical: int = 16, select_heads=None):
     """Quantize each request's new K/V rows ([S, Hkv, D], bf16 or float32)
     and write their codes and scales at position seq_lens[s] of the 8-bit
-    pools in place via da_append_kv_fp8.  seq_lens is not advanced."""
+    pools in place via da_append_kv_fp8, keeping ``stats`` (head-major
+    statistics in the rows' dtype, or None) current from the full-precision
+    key rows.  seq_lens is not advanced."""
     dev = k_codes.device
     _need(k_codes, "k_codes", torch.uint8, dev, 4)
     _need(v_codes, "v_codes", torch.uint8, dev, 4)
@@ -473,10 +477,17 @@ def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_code
             raise ValueError(f"{name} must be [S, Hkv, D] = {(S, Hkv, D)}")
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    if stats is not None:
+        _need(stats, "stats", k_new.dtype, dev, 5)
+        if tuple(stats.shape) != (Hkv, NP, P // logical, 2, D):
+            raise ValueError("stats must be [Hkv, NP, P // logical, 2, D]")
+    if select_heads is not None:
+        _need(select_heads, "select_heads", torch.uint8, dev, 1)
     sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_new))
     _check(load().da_append_kv_fp8(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                    _ptr(seq_lens), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
-                                   _ptr(v_scales), _stream(dev)))
+                                   _ptr(v_scales), int(logical), _ptr(select_heads), _ptr(stats),
+                                   _stream(dev)))
 
 
 def split_bounds(block_mask, seq_lens, *, P: int, b: int, horizon: int = 0, Hkv=None,

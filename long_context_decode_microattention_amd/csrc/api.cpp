@@ -430,7 +430,8 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
 
 da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
-                           float* k_scales, uint8_t* v_codes, float* v_scales, hipStream_t stream) {
+                           float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
+                           const uint8_t* select_heads, void* stats, hipStream_t stream) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d D=%d P=%d max_pages=%d NP=%lld)",
@@ -443,6 +444,10 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (!da::quantize_supported(sh->dtype, sh->D))
     return fail(DA_ERR_UNSUPPORTED, "8-bit append not built for D=%d (64, 128)", sh->D);
+  if (stats != nullptr && !da::selector_supported(sh->dtype, sh->D, 1, sh->P, logical))
+    return fail(DA_ERR_UNSUPPORTED, "statistics not built for P=%d logical=%d", sh->P, logical);
+  if (stats != nullptr && !aligned(stats, 16))
+    return fail(DA_ERR_INVALID_ARG, "statistics must be 16-byte aligned");
   if (!k_new || !v_new || !block_table || !seq_lens || !k_codes || !k_scales || !v_codes || !v_scales)
     return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_codes, 8) || !aligned(v_codes, 8))
@@ -458,10 +463,14 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
   p.k_scales = k_scales;
   p.v_codes = v_codes;
   p.v_scales = v_scales;
+  p.stats = stats;
+  p.select = select_heads;
+  p.NP = sh->NP;
   p.S = sh->S;
   p.Hkv = sh->Hkv;
   p.P = sh->P;
   p.max_pages = sh->max_pages;
+  p.logical = stats != nullptr ? logical : sh->P;
   const hipError_t err = da::launch_append_kv_fp8(p, sh->dtype, sh->D, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "8-bit append launch failed: %s", hipGetErrorString(err));
   return DA_OK;

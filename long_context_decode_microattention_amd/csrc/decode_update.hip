@@ -126,6 +126,23 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
     *reinterpret_cast<uint2*>(codes + row * D + col * 8) = c;
     if (col == 0) (part == 0 ? p.k_scales : p.v_scales)[row] = sc;
   }
+  // statistics of the logical page, folded from the full-precision key row
+  // (as append_kv_kernel does for bf16 / fp32 pools)
+  if (p.stats != nullptr && (p.select == nullptr || p.select[kvh] != 0)) {
+    constexpr int RB = D * ES;
+    constexpr int SL = RB / 16;  // 16-byte chunks per row
+    const int NL = p.P / p.logical;
+    const int sub = slot / p.logical;
+    const char* k = static_cast<const char*>(p.k_new) + ((size_t)s * p.Hkv + kvh) * RB;
+    char* base = static_cast<char*>(p.stats) + ((((size_t)kvh * p.NP + phys) * NL + sub) * 2) * RB;
+    for (int cc = lane; cc < 2 * SL; cc += kWave) {
+      const int which = cc / SL;  // 0 = kmax, 1 = kmin
+      const size_t col16 = (size_t)(cc - which * SL) * 16;
+      const uint4 kx = ld16(k + col16);
+      char* dst = base + which * RB + col16;
+      st16(dst, slot % p.logical == 0 ? kx : fold16<DT>(ld16(dst), kx, which == 0));
+    }
+  }
 }
 
 // One workgroup per (request, KV head).  Pages [0, n) with n = ceil(E / P),

@@ -101,7 +101,10 @@ struct AppendFp8Params {
   float* k_scales;    // [NP, Hkv, P]
   uint8_t* v_codes;
   float* v_scales;
-  int S, Hkv, P, max_pages;
+  void* stats;        // [Hkv, NP, P / logical, 2, D] of the new rows' dtype, or null
+  const uint8_t* select;
+  long long NP;
+  int S, Hkv, P, max_pages, logical;
 };
 struct BoundsParams {
   const uint8_t* mask;  // [S, Hkv, max_pages] or null (every page kept)

@@ -283,6 +283,8 @@ def test_quantize_rows_misaligned(lib):
     (dict(ptrs=dict(k_new=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(kc=FAKE + 4)), _lib.DA_ERR_INVALID_ARG),
     (dict(ptrs=dict(vs=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(stats=FAKE), logical=12), _lib.DA_ERR_UNSUPPORTED),
+    (dict(ptrs=dict(stats=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),
 ])
 def test_append_kv_fp8_rejects(lib, case, status):
     sh = good_shape(**case.get("shape", {}))
@@ -290,5 +292,6 @@ def test_append_kv_fp8_rejects(lib, case, status):
     p.update(case.get("ptrs", {}))
     got = lib.da_append_kv_fp8(ctypes.byref(sh), *[_vp(p[k]) for k in
                                                    ("k_new", "v_new", "table", "lens", "kc", "ks",
-                                                    "vc", "vs")], None)
+                                                    "vc", "vs")], case.get("logical", 16), None,
+                               _vp(p.get("stats")), None)
     assert got == status, _lib.load().da_last_error()

@@ -229,7 +229,11 @@ def _host_append_fp8(codes, scales, table, lens, new_rows):
 def test_append_fp8_matches_oracle(cfg):
     """Consecutive 8-bit appends across a page boundary: after every step the
     code and scale pools equal the oracle's (quantize the new rows, write them
-    through the table) bit for bit."""
+    through the table) bit for bit; the statistics kept from the bf16 key rows
+    (upper half of the KV heads) equal the oracle's statistics of the bf16
+    cache with the same rows appended."""
+    import oracle.decode as odec
+    import oracle.selector as osel
     spec = CASES[cfg].replace(reserve=24, table="shuffled", extra_pages=2)
     announce("fp8 append", cfg)
     b = wl.build(spec, 4, DEV)
@@ -237,17 +241,29 @@ def test_append_fp8_matches_oracle(cfg):
     h = wl.host
     table = h(b.block_table)
     okc, oks, ovc, ovs = h(kc), h(ks), h(vc), h(vs)
+    ok_bf16 = h(b.k_pages)  # the full-precision keys the statistics follow
     lens = b.seq_lens.clone()
+    logical = 16
+    flags = np.array([1 if i >= spec.Hkv // 2 else 0 for i in range(spec.Hkv)], dtype=np.uint8)
+    sel_t = torch.from_numpy(flags).to(DEV)
+    stats = _lib.page_stats(b.k_pages, b.block_table, lens, logical=logical, select_heads=sel_t)
+    on = flags.astype(bool)
     for step in range(20):
         kn, vn = wl.new_tokens(spec, 4, step, DEV)
-        _lib.append_kv_fp8(kn, vn, b.block_table, lens, kc, ks, vc, vs)
+        _lib.append_kv_fp8(kn, vn, b.block_table, lens, kc, ks, vc, vs, stats=stats,
+                           logical=logical, select_heads=sel_t)
         L = h(lens)
         okc, oks = _host_append_fp8(okc, oks, table, L, h(kn))
         ovc, ovs = _host_append_fp8(ovc, ovs, table, L, h(vn))
+        ok_bf16, _ = odec.append_kv(ok_bf16, ok_bf16, table, L, h(kn), h(kn))
         lens += 1
         torch.cuda.synchronize()
         assert np.array_equal(h(kc), okc) and np.array_equal(h(vc), ovc), f"{cfg} step {step}: codes"
         assert np.array_equal(h(ks), oks) and np.array_equal(h(vs), ovs), f"{cfg} step {step}: scales"
+        if step % 7 == 6 or step == 19:
+            want = osel.page_stats(ok_bf16, table, h(lens), logical=logical)
+            got = oracle.to_f64(h(stats.transpose(0, 1).contiguous()))
+            assert np.array_equal(got[:, on], want[:, on]), f"{cfg} step {step}: statistics"
 
 
 def test_fp8_decode_chunk():
