@@ -64,6 +64,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Two OCP E4M3 codes of a word (bytes 0-1, or 2-3 when HI) -> a bf16 pair
+// in one word, exactly (every E4M3 value is a bf16 value): the scaled
+// conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Its packed result is
+// read as one 32-bit word (checked on gfx950 for all 256 codes).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
 // Four OCP E4M3 codes packed in a word (byte i = element i) -> four floats,
 // exactly (v_cvt_pk_f32_fp8 on gfx950).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {

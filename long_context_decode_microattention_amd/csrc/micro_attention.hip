@@ -21,9 +21,10 @@
 //
 // Arithmetic: fp32 accumulation.  bf16 scores use v_dot2 (bf16 pairs, fp32
 // accumulate); bf16 values are widened exactly by bit shifts.  fp8 (E4M3)
-// pages are widened exactly by v_cvt_pk_f32_fp8 and multiply a bf16 query
-// held in fp32; a token's K scale multiplies its dot product and its V scale
-// its probability (per-row scales of the quantized pages).  Exponentials
+// keys are widened exactly to bf16 pairs for the same v_dot2 with the bf16
+// query, fp8 values to fp32 by v_cvt_pk_f32_fp8; a token's K scale
+// multiplies its dot product and its V scale its probability (per-row scales
+// of the quantized pages).  Exponentials
 // run in base 2 on raw dot products: exp(scale*(d - d_max)) =
 // exp2((d - d_max) * scale*log2(e)); the reported m_j is scale * d_max.
 #include <type_traits>
@@ -86,22 +87,16 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
     const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
     // Query fragment of every head in the group: the lane's 16-byte column
-    // (for fp8 pages: the lane's 16 dims of the bf16 query, widened to fp32).
+    // (for fp8 pages: the lane's 16 dims of the bf16 query, 32 bytes).
     uint4 qv[G];
-    float qf[DT == 2 ? G : 1][DT == 2 ? L::EPL : 1];
+    uint4 qv2[DT == 2 ? G : 1];
   #pragma unroll
     for (int g = 0; g < G; ++g) {
       if constexpr (DT == 2) {
         const uint4* qp = reinterpret_cast<const uint4*>(
             static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + g) * D * 2 + (size_t)chunk * 32);
-        const uint4 a = qp[0], b = qp[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          qf[g][2 * i] = bf16_lo(w[i]);
-          qf[g][2 * i + 1] = bf16_hi(w[i]);
-        }
-        qv[g] = make_uint4(0, 0, 0, 0);
+        qv[g] = qp[0];
+        qv2[g] = qp[1];
       } else {
         const char* qp = static_cast<const char*>(p.q) +
                          ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
@@ -186,13 +181,16 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
             for (int g = 0; g < G; ++g) {
               float d;
               if constexpr (DT == 2) {
+                // codes widened to bf16 pairs, then bf16 dot products with q
                 const uint32_t w4[4] = {f.k[i].x, f.k[i].y, f.k[i].z, f.k[i].w};
-                float kf[16];
+                const uint32_t qw[8] = {qv[g].x, qv[g].y, qv[g].z, qv[g].w,
+                                        qv2[g].x, qv2[g].y, qv2[g].z, qv2[g].w};
+                d = 0.f;
   #pragma unroll
-                for (int w = 0; w < 4; ++w) fp8x4_to_f32(w4[w], kf + 4 * w);
-                d = qf[g][0] * kf[0];
-  #pragma unroll
-                for (int e = 1; e < 16; ++e) d = fmaf(qf[g][e], kf[e], d);
+                for (int w = 0; w < 4; ++w) {
+                  d = dot2_bf16(fp8x2_to_bf16x2<false>(w4[w]), qw[2 * w], d);
+                  d = dot2_bf16(fp8x2_to_bf16x2<true>(w4[w]), qw[2 * w + 1], d);
+                }
               } else if constexpr (DT == 1) {
                 d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
                 d = dot2_bf16(f.k[i].y, qv[g].y, d);

@@ -66,18 +66,10 @@ struct MFrag {
   float vsc[MLayout<DT, D>::NI];               // fp8: V scales of the value rows
 };
 
-// Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly:
-// every E4M3 value is a bf16 value, so the fp32 result's upper half is it.
+// Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly.
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  float f[8];
-  fp8x4_to_f32(w0, f);
-  fp8x4_to_f32(w1, f + 4);
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = (__builtin_bit_cast(uint32_t, f[2 * i]) >> 16) |
-           (__builtin_bit_cast(uint32_t, f[2 * i + 1]) & 0xFFFF0000u);
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                    fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
 }
 
 __device__ __forceinline__ uint2 load_stream8(const void* p) {
