@@ -89,11 +89,12 @@ def time_workload(key, steps, warmup, dev):
     from long_context_decode_microattention_amd import workloads as wl
 
     fp8 = key.endswith("_fp8")
-    spec = wl.CONFIGS[key[:-4] if fp8 else key]
+    base = key[:-4] if fp8 else key
+    spec = wl.CONFIGS[base].replace(layout=wl.PREFERRED_LAYOUT.get(base, "page"))
     t0 = time.time()
     b = wl.build(spec, 0, dev)
     torch.cuda.synchronize()
-    log(f"[bench] built {key} in {time.time() - t0:.1f}s: NP={b.k_pages.shape[0]}")
+    log(f"[bench] built {key} in {time.time() - t0:.1f}s: NP={b.k_pm.shape[0]}")
     S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
     kept = int(b.kept_tokens().sum())
     if fp8:
@@ -121,7 +122,7 @@ def time_workload(key, steps, warmup, dev):
     del src, dst
 
     for _ in range(warmup):
-        micro(*args, scale=b.scale, out=(MA, m, e))
+        micro(*args, scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
         _lib.merge(MA, m, e, out=out)
     torch.cuda.synchronize()
 
@@ -129,7 +130,7 @@ def time_workload(key, steps, warmup, dev):
     torch.cuda.synchronize()
     for i in range(steps):
         ev[3 * i].record()
-        micro(*args, scale=b.scale, out=(MA, m, e))
+        micro(*args, scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
         ev[3 * i + 1].record()
         _lib.merge(MA, m, e, out=out)
         ev[3 * i + 2].record()
@@ -148,6 +149,7 @@ def time_workload(key, steps, warmup, dev):
         GBps=kv_bytes / (ms_step * 1e-3) / 1e9, micro_GBps=kv_bytes / (avg_micro * 1e-3) / 1e9,
         shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B,
                    kv_dtype="fp8_e4m3+f32 row scale" if fp8 else spec.dtype,
+                   pool_layout="[Hkv, NP, P, D]" if spec.layout == "head" else "[NP, Hkv, P, D]",
                    max_len=spec.max_len, block_mask=spec.mask is not None),
         kept_tokens=kept,
         tokens_per_s=kept / (ms_step * 1e-3),
@@ -185,7 +187,7 @@ def time_selector(b, steps, warmup, dev, logical=16):
     budget = int(frac * (npg - keep_first - keep_last))
     esize = sp.esize
     NL = P // logical
-    stats = torch.zeros((Hkv, b.k_pages.shape[0], NL, 2, D), dtype=b.k_pages.dtype, device=dev)
+    stats = torch.zeros((Hkv, b.k_pm.shape[0], NL, 2, D), dtype=b.k_pages.dtype, device=dev)
     scores = torch.empty((sp.S, Hkv, max_pages), dtype=torch.float32, device=dev)
     mask = torch.empty((sp.S, Hkv, max_pages), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -193,13 +195,13 @@ def time_selector(b, steps, warmup, dev, logical=16):
     # statistics of the selected KV heads over the whole pool, timed
     for _ in range(max(1, warmup)):
         _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
-                        select_heads=flags, out=stats)
+                        select_heads=flags, out=stats, pool_layout=b.layout)
     reps = max(3, steps // 4)
     s0, s1 = ev(), ev()
     s0.record()
     for _ in range(reps):
         _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
-                        select_heads=flags, out=stats)
+                        select_heads=flags, out=stats, pool_layout=b.layout)
     s1.record()
     torch.cuda.synchronize()
     us_stats = s0.elapsed_time(s1) * 1e3 / reps
@@ -256,7 +258,7 @@ def time_selector(b, steps, warmup, dev, logical=16):
         select()
         topk()
         _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, sb_t, mask,
-                             scale=b.scale, out=(MA, m, e))
+                             scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
         _lib.merge(MA, m, e, out=out)
 
     for _ in range(warmup):
@@ -324,7 +326,8 @@ def time_decode_chunks(b, chunks, dev, logical=16, chunk=16):
     nb = b.max_splits
     lens0 = b.seq_lens.clone()
     lens = lens0.clone()
-    stats = _lib.page_stats(b.k_pages, b.block_table, lens, logical=logical, select_heads=flags)
+    stats = _lib.page_stats(b.k_pages, b.block_table, lens, logical=logical, select_heads=flags,
+                            pool_layout=b.layout)
     scores = torch.empty((sp.S, Hkv, sp.max_pages), dtype=torch.float32, device=dev)
     mask = torch.empty((sp.S, Hkv, sp.max_pages), dtype=torch.uint8, device=dev)
     bounds = torch.empty((sp.S, Hkv, nb + 1), dtype=torch.int32, device=dev)
@@ -341,10 +344,10 @@ def time_decode_chunks(b, chunks, dev, logical=16, chunk=16):
         _lib.split_bounds(mask, lens, P=P, b=nb, horizon=chunk, out=bounds)
         for i in range(chunk):
             _lib.append_kv(new[i][0], new[i][1], b.block_table, lens, b.k_pages, b.v_pages,
-                           stats=stats, logical=logical, select_heads=flags)
+                           stats=stats, logical=logical, select_heads=flags, pool_layout=b.layout)
             lens.add_(1)
             _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
-                                 scale=b.scale, out=(MA, m, e))
+                                 scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
             _lib.merge(MA, m, e, out=out)
 
     ms = []
@@ -414,8 +417,8 @@ def cpu_baseline(b, budget_s):
             npg = -(-L // sp.P)
             pages = b.block_table[s, :npg].long()
             h = wl.host
-            k = h(b.k_pages[:, kvh:kvh + 1].index_select(0, pages).contiguous())
-            v = h(b.v_pages[:, kvh:kvh + 1].index_select(0, pages).contiguous())
+            k = h(b.k_pm[:, kvh:kvh + 1].index_select(0, pages).contiguous())
+            v = h(b.v_pm[:, kvh:kvh + 1].index_select(0, pages).contiguous())
             q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
             mask = None
             if b.block_mask is not None:

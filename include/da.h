@@ -65,6 +65,16 @@ typedef enum da_dtype {
                   /* Used by da_micro_attention_fp8 only.              */
 } da_dtype;
 
+/* Order of the dimensions of the K / V pools.  Page-major: [NP, Hkv, P, D]
+ * (a physical page holds every KV head).  Head-major: [Hkv, NP, P, D] (one
+ * KV head's pages form one contiguous run: the per-head view
+ * K:[num_pages, page_size, head_dim] of the LServe blog page, section 3.1.2,
+ * stacked over heads); the fp8 scale arrays follow the same order. */
+typedef enum da_pool_layout {
+  DA_POOL_PAGE_MAJOR = 0,
+  DA_POOL_HEAD_MAJOR = 1
+} da_pool_layout;
+
 /* Problem shape.  Notation: S requests, Hq query heads, Hkv KV heads
  * (G = Hq / Hkv query heads share one KV head: query head h reads KV head
  * h / G), D head dimension, P tokens per page, NP pages in the pool. */
@@ -86,6 +96,8 @@ typedef struct da_shape {
   int32_t schedule;        /* 0: library choice; 1: one workgroup per item;     */
                            /* 2: persistent workgroups claiming items from a   */
                            /* work queue in the workspace                      */
+  int32_t pool_layout;     /* da_pool_layout of the K / V pools (and fp8 scale  */
+                           /* arrays); read by every call that takes them      */
 } da_shape;
 
 /*
@@ -95,7 +107,11 @@ typedef struct da_shape {
  *   q            [S, Hq, D] of sh->dtype, 16-byte aligned.
  *   k_pages      [NP, Hkv, P, D] of sh->dtype, 16-byte aligned: the key of
  *                logical token t of request s for KV head g is
- *                k_pages[block_table[s, t / P], g, t % P, :].
+ *                k_pages[block_table[s, t / P], g, t % P, :]; with
+ *                sh->pool_layout = DA_POOL_HEAD_MAJOR the pool is
+ *                [Hkv, NP, P, D] and the key is k_pages[g, block_table[s, t / P],
+ *                t % P, :] (every call that takes pools reads this field, and
+ *                8-bit scale arrays [NP, Hkv, P] become [Hkv, NP, P]).
  *   v_pages      same layout as k_pages, for values.
  *   block_table  [S, max_pages] int32: logical page -> physical page.  Only
  *                entries of pages that hold tokens of some split are read.

@@ -41,6 +41,7 @@ class DaShape(ctypes.Structure):
         ("NP", ctypes.c_int64),
         ("chunks", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
+        ("pool_layout", ctypes.c_int32),
     ]
 
 
@@ -137,10 +138,20 @@ def _need(t: torch.Tensor, name: str, dtype, device, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+POOL_LAYOUTS = {"page": 0, "head": 1}
+
+
 def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None,
-             chunks: int = 0, schedule: int = 0) -> DaShape:
+             chunks: int = 0, schedule: int = 0, pool_layout: str = "page") -> DaShape:
+    """da_shape of a call; pool_layout "page" = pools [NP, Hkv, P, D],
+    "head" = [Hkv, NP, P, D]."""
     S, Hq, D = q.shape
-    NP, Hkv, P, D2 = k_pages.shape
+    if pool_layout not in POOL_LAYOUTS:
+        raise ValueError(f"pool_layout must be one of {sorted(POOL_LAYOUTS)}")
+    if pool_layout == "head":
+        Hkv, NP, P, D2 = k_pages.shape
+    else:
+        NP, Hkv, P, D2 = k_pages.shape
     if D2 != D:
         raise ValueError(f"head dim of q ({D}) and k_pages ({D2}) differ")
     nbh = split_bounds.shape[1]
@@ -155,7 +166,8 @@ def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = Non
     return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=block_table.shape[1],
                    max_splits=split_bounds.shape[2] - 1, bounds_per_head=int(nbh == Hkv and Hkv > 1),
                    dtype=dt, scale=(1.0 / math.sqrt(D)) if scale is None else float(scale), NP=NP,
-                   chunks=int(chunks), schedule=int(schedule))
+                   chunks=int(chunks), schedule=int(schedule),
+                   pool_layout=POOL_LAYOUTS[pool_layout])
 
 
 _WORKSPACE = {}
@@ -182,7 +194,8 @@ def _cached_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tenso
 
 def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
                     *, scale: Optional[float] = None, out=None, chunks: int = 0,
-                    workspace: Optional[torch.Tensor] = None, schedule: int = 0):
+                    workspace: Optional[torch.Tensor] = None, schedule: int = 0,
+                    pool_layout: str = "page"):
     """MicroAttention partials (MA [S,Hq,b,D], m [S,Hq,b], e [S,Hq,b]) via da_micro_attention.
 
     chunks: 0 lets the library cut splits into page ranges when that balances
@@ -201,7 +214,7 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
     _need(split_bounds, "split_bounds", torch.int32, dev, 3)
     if block_mask is not None:
         _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule)
+    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule, pool_layout)
     if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
         raise ValueError("block_table, seq_lens and split_bounds must have S rows")
     if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
@@ -252,7 +265,7 @@ def quantize_rows(x, *, out=None):
 def micro_attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens,
                         split_bounds, block_mask=None, *, scale: Optional[float] = None, out=None,
                         chunks: int = 0, workspace: Optional[torch.Tensor] = None,
-                        schedule: int = 0):
+                        schedule: int = 0, pool_layout: str = "page"):
     """MicroAttention partials over 8-bit pages via da_micro_attention_fp8:
     q [S, Hq, D] bf16; k_codes / v_codes [NP, Hkv, P, D] uint8 E4M3 codes;
     k_scales / v_scales [NP, Hkv, P] float32.  Arguments otherwise as
@@ -266,13 +279,13 @@ def micro_attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, se
     for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
         _need(t, name, torch.float32, dev, 3)
         if tuple(t.shape) != tuple(k_codes.shape[:3]):
-            raise ValueError(f"{name} must be [NP, Hkv, P]")
+            raise ValueError(f"{name} must match the first three dims of the code pools")
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     _need(split_bounds, "split_bounds", torch.int32, dev, 3)
     if block_mask is not None:
         _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule)
+    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule, pool_layout)
     sh.dtype = DA_FP8_E4M3
     if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
         raise ValueError("block_table, seq_lens and split_bounds must have S rows")
@@ -316,10 +329,10 @@ def merge(MA, m, e, *, out=None):
 
 
 def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
-              *, scale: Optional[float] = None, chunks: int = 0):
+              *, scale: Optional[float] = None, chunks: int = 0, pool_layout: str = "page"):
     """One decode step: micro_attention then merge."""
     MA, m, e = micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds,
-                               block_mask, scale=scale, chunks=chunks)
+                               block_mask, scale=scale, chunks=chunks, pool_layout=pool_layout)
     return merge(MA, m, e)
 
 
@@ -331,13 +344,22 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, dtype) -> DaShape:
+def _selector_shape(S, Hq, Hkv, D, P, NP, max_pages, dtype, pool_layout: str = "page") -> DaShape:
     return DaShape(S=S, Hq=Hq, Hkv=Hkv, D=D, P=P, max_pages=max_pages, max_splits=1,
-                   bounds_per_head=0, dtype=dtype, scale=1.0, NP=NP)
+                   bounds_per_head=0, dtype=dtype, scale=1.0, NP=NP,
+                   pool_layout=POOL_LAYOUTS[pool_layout])
+
+
+def _pool_dims(pool, pool_layout: str):
+    """(NP, Hkv, P, D) of a pool in the given layout."""
+    if pool_layout not in POOL_LAYOUTS:
+        raise ValueError(f"pool_layout must be one of {sorted(POOL_LAYOUTS)}")
+    a, b, P, D = pool.shape
+    return (b, a, P, D) if pool_layout == "head" else (a, b, P, D)
 
 
 def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_heads=None,
-               out=None):
+               out=None, pool_layout: str = "page"):
     """Per-logical-page key maxima and minima [Hkv, NP, P // logical, 2, D]
     (dtype of k_pages, head-major) via da_page_stats.  Pages that no table row names
     below L_s, and KV heads whose select_heads flag is 0, are left as they
@@ -346,7 +368,7 @@ def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_head
     _need(k_pages, "k_pages", None, dev, 4)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
-    NP, Hkv, P, D = k_pages.shape
+    NP, Hkv, P, D = _pool_dims(k_pages, pool_layout)
     if select_heads is not None:
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
         if select_heads.shape[0] != Hkv:
@@ -360,7 +382,7 @@ def page_stats(k_pages, block_table, seq_lens, *, logical: int = 16, select_head
         if tuple(out.shape) != (Hkv, NP, P // logical, 2, D):
             raise ValueError("out must be [Hkv, NP, P // logical, 2, D]")
     sh = _selector_shape(block_table.shape[0], Hkv, Hkv, D, P, NP, block_table.shape[1],
-                         _dtype_code(k_pages))
+                         _dtype_code(k_pages), pool_layout)
     _check(load().da_page_stats(ctypes.byref(sh), _ptr(k_pages), _ptr(block_table), _ptr(seq_lens),
                                 int(logical), _ptr(select_heads), _ptr(out), _stream(dev)))
     return out
@@ -420,7 +442,7 @@ def select_pages(scores, seq_lens, *, P: int, budget: int, keep_first: int = 0,
 
 
 def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=None,
-              logical: int = 16, select_heads=None):
+              logical: int = 16, select_heads=None, pool_layout: str = "page"):
     """Write each request's new K/V rows ([S, Hkv, D]) at position seq_lens[s]
     of the paged pools in place via da_append_kv, keeping ``stats`` (head-major
     statistics, or None) current.  seq_lens is not advanced."""
@@ -429,7 +451,7 @@ def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=No
     _need(v_pages, "v_pages", k_pages.dtype, dev, 4)
     if v_pages.shape != k_pages.shape:
         raise ValueError("k_pages and v_pages differ in shape")
-    NP, Hkv, P, D = k_pages.shape
+    NP, Hkv, P, D = _pool_dims(k_pages, pool_layout)
     S = block_table.shape[0]
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         _need(t, name, k_pages.dtype, dev, 3)
@@ -447,14 +469,15 @@ def append_kv(k_new, v_new, block_table, seq_lens, k_pages, v_pages, *, stats=No
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
         if select_heads.shape[0] != Hkv:
             raise ValueError("select_heads must have Hkv entries")
-    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_pages))
+    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_pages),
+                         pool_layout)
     _check(load().da_append_kv(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                _ptr(seq_lens), _ptr(k_pages), _ptr(v_pages), int(logical),
                                _ptr(select_heads), _ptr(stats), _stream(dev)))
 
 
 def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales, *,
-                  stats=None, logical: int = 16, select_heads=None):
+                  stats=None, logical: int = 16, select_heads=None, pool_layout: str = "page"):
     """Quantize each request's new K/V rows ([S, Hkv, D], bf16 or float32)
     and write their codes and scales at position seq_lens[s] of the 8-bit
     pools in place via da_append_kv_fp8, keeping ``stats`` (head-major
@@ -465,11 +488,11 @@ def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_code
     _need(v_codes, "v_codes", torch.uint8, dev, 4)
     if v_codes.shape != k_codes.shape:
         raise ValueError("k_codes and v_codes differ in shape")
-    NP, Hkv, P, D = k_codes.shape
+    NP, Hkv, P, D = _pool_dims(k_codes, pool_layout)
     for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
         _need(t, name, torch.float32, dev, 3)
-        if tuple(t.shape) != (NP, Hkv, P):
-            raise ValueError(f"{name} must be [NP, Hkv, P]")
+        if tuple(t.shape) != tuple(k_codes.shape[:3]):
+            raise ValueError(f"{name} must match the first three dims of the code pools")
     S = block_table.shape[0]
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         _need(t, name, k_new.dtype, dev, 3)
@@ -483,7 +506,8 @@ def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_code
             raise ValueError("stats must be [Hkv, NP, P // logical, 2, D]")
     if select_heads is not None:
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
-    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_new))
+    sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_new),
+                         pool_layout)
     _check(load().da_append_kv_fp8(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                    _ptr(seq_lens), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                    _ptr(v_scales), int(logical), _ptr(select_heads), _ptr(stats),

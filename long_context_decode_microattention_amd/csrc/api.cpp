@@ -57,6 +57,9 @@ da_status check_shape(const da_shape* sh, bool fp8 = false) {
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
   if (sh->schedule < 0 || sh->schedule > 2)
     return fail(DA_ERR_INVALID_ARG, "schedule must be 0, 1 or 2 (got %d)", sh->schedule);
+  if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
+    return fail(DA_ERR_INVALID_ARG, "pool_layout must be DA_POOL_PAGE_MAJOR or DA_POOL_HEAD_MAJOR (got %d)",
+                sh->pool_layout);
   if (sh->chunks < 0 || sh->chunks > kMaxChunks)
     return fail(DA_ERR_INVALID_ARG, "chunks must be 0 (library choice) or 1..%d (got %d)",
                 kMaxChunks, sh->chunks);
@@ -112,6 +115,8 @@ da_status check_selector(const da_shape* sh, int logical) {
     return fail(DA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", sh->Hq, sh->Hkv);
   if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
+    return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
   if ((long long)sh->max_pages * sh->P > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
   if (sh->NP > (long long)INT_MAX + 1)
@@ -135,6 +140,7 @@ da::SelectorParams selector_params(const da_shape* sh, int logical) {
   p.P = sh->P;
   p.max_pages = sh->max_pages;
   p.logical = logical;
+  p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
   return p;
 }
 
@@ -217,6 +223,8 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.max_splits = sh->max_splits;
   p.bounds_per_head = sh->bounds_per_head;
   p.scale = sh->scale;
+  p.NP = sh->NP;
+  p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
   hipError_t err = da::launch_micro(sh->dtype, sh->D, G, p, stream);
   if (err != hipSuccess)
     return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
@@ -393,6 +401,8 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
                 sh->S, sh->Hkv, sh->D, sh->P, sh->max_pages, (long long)sh->NP);
   if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
+  if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
+    return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
   if ((long long)sh->max_pages * sh->P > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
@@ -423,6 +433,7 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
   p.P = sh->P;
   p.max_pages = sh->max_pages;
   p.logical = stats != nullptr ? logical : sh->P;
+  p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
   const hipError_t err = da::launch_append_kv(p, sh->dtype, sh->D, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "KV append launch failed: %s", hipGetErrorString(err));
   return DA_OK;
@@ -438,6 +449,8 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
                 sh->S, sh->Hkv, sh->D, sh->P, sh->max_pages, (long long)sh->NP);
   if (sh->dtype != DA_F32 && sh->dtype != DA_BF16)
     return fail(DA_ERR_INVALID_ARG, "dtype of the new rows must be DA_F32 or DA_BF16 (got %d)", sh->dtype);
+  if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
+    return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
   if ((long long)sh->max_pages * sh->P > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
@@ -471,6 +484,7 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
   p.P = sh->P;
   p.max_pages = sh->max_pages;
   p.logical = stats != nullptr ? logical : sh->P;
+  p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
   const hipError_t err = da::launch_append_kv_fp8(p, sh->dtype, sh->D, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "8-bit append launch failed: %s", hipGetErrorString(err));
   return DA_OK;

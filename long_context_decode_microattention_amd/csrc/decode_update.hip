@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_kernel(AppendP
   const bool stats = p.stats != nullptr && (p.select == nullptr || p.select[kvh] != 0);
   const int parts = stats ? 4 : 2;
   const size_t new_off = ((size_t)s * p.Hkv + kvh) * RB;
-  const size_t row_off = (((size_t)phys * p.Hkv + kvh) * p.P + slot) * RB;
+  const size_t tile_id = p.head_major ? (size_t)kvh * p.NP + phys : (size_t)phys * p.Hkv + kvh;
+  const size_t row_off = (tile_id * p.P + slot) * RB;
   for (int c = threadIdx.x % kWave; c < parts * LPR; c += kWave) {
     const int part = c / LPR;
     const size_t col = (size_t)(c - part * LPR) * 16;
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
   float sc;
   const uint2 c = quantize8<LPR>(v, sc);
   if (part < 2) {
-    const size_t row = ((size_t)phys * p.Hkv + kvh) * p.P + slot;
+    const size_t tile_id = p.head_major ? (size_t)kvh * p.NP + phys : (size_t)phys * p.Hkv + kvh;
+    const size_t row = tile_id * p.P + slot;
     uint8_t* codes = part == 0 ? p.k_codes : p.v_codes;
     *reinterpret_cast<uint2*>(codes + row * D + col * 8) = c;
     if (col == 0) (part == 0 ? p.k_scales : p.v_scales)[row] = sc;

@@ -24,6 +24,8 @@ struct MicroParams {
   int S, Hq, Hkv, P, max_pages, max_splits, bounds_per_head;
   int chunks;  // page-range pieces per split, >= 1
   float scale;
+  long long NP;     // pages in the pools
+  int head_major;   // 0: pools [NP, Hkv, P, D] (scales [NP, Hkv, P]); 1: [Hkv, NP, P, D] ([Hkv, NP, P])
   // Persistent launch: `queue` is a device counter that is zero when the
   // kernel starts; each workgroup claims `grab` consecutive items at a time
   // until all n_items = S*Hkv*max_splits*chunks are taken.  queue == null:
@@ -71,6 +73,7 @@ struct SelectorParams {
   long long NP;
   int S, Hq, Hkv, P, max_pages, logical;
   int budget, keep_first, keep_last, horizon;
+  int head_major;     // K pool [Hkv, NP, P, D] instead of [NP, Hkv, P, D]
 };
 bool selector_supported(int dtype, int D, int G, int P, int logical);
 hipError_t launch_page_stats(const SelectorParams& p, int dtype, int D, hipStream_t stream);
@@ -91,6 +94,7 @@ struct AppendParams {
   const uint8_t* select;
   long long NP;
   int S, Hkv, P, max_pages, logical;
+  int head_major;     // pools [Hkv, NP, P, D] instead of [NP, Hkv, P, D]
 };
 struct AppendFp8Params {
   const void* k_new;  // [S, Hkv, D], bf16 or fp32
@@ -105,6 +109,7 @@ struct AppendFp8Params {
   const uint8_t* select;
   long long NP;
   int S, Hkv, P, max_pages, logical;
+  int head_major;     // pools and scales [Hkv, NP, P(, D)] instead of [NP, Hkv, P(, D)]
 };
 struct BoundsParams {
   const uint8_t* mask;  // [S, Hkv, max_pages] or null (every page kept)

@@ -116,10 +116,13 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
     if (it.scan0 < it.scan1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       const int spp = P / SL;  // slabs per page
-      const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
-      const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB + lane * 16;
-      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * 16;
-      const size_t scale_page = (size_t)p.Hkv * P;  // fp8: scales per physical page
+      // page-major pool [NP, Hkv, P, D] or head-major pool [Hkv, NP, P, D]
+      const size_t page_stride = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P * L::TOKB;
+      const size_t head_off = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P * L::TOKB;
+      const char* kbase = static_cast<const char*>(p.k) + head_off + lane * 16;
+      const char* vbase = static_cast<const char*>(p.v) + head_off + lane * 16;
+      const size_t scale_page = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P;  // fp8 scales
+      const size_t scale_head = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
           const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (SL * L::TOKB);
           const int tb = s_lp[kp] * P + sub * SL;
           // fp8: the scales of this lane's token rows (slot sub*SL + i*TPI + row)
-          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * SL + row;
+          const size_t so = (size_t)s_phys[kp] * scale_page + scale_head + sub * SL + row;
           if (tb >= t0 && tb + SL <= t1) {
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {

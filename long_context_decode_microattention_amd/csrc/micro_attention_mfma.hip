@@ -153,13 +153,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
     if (it.scan0 < it.scan1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       const int spp = P / kSlab;
-      const size_t page_stride = (size_t)p.Hkv * P * L::TOKB;
+      // page-major pool [NP, Hkv, P, D] or head-major pool [Hkv, NP, P, D]
+      const size_t page_stride = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P * L::TOKB;
+      const size_t head_off = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P * L::TOKB;
       // key lane: token col; bf16: 16 bytes per step at 64*step + 16*grp;
       // fp8: 8*KS contiguous bytes at 8*KS*grp
-      const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * P * L::TOKB +
+      const char* kbase = static_cast<const char*>(p.k) + head_off +
                           (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
-      const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * P * L::TOKB + lane * L::VB;
-      const size_t scale_page = (size_t)p.Hkv * P;  // fp8: scales per physical page
+      const char* vbase = static_cast<const char*>(p.v) + head_off + lane * L::VB;
+      const size_t scale_page = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P;  // fp8 scales
+      const size_t scale_head = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
@@ -172,7 +175,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           const int kp = sl / spp;
           const int sub = sl - kp * spp;
           const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
-          const size_t so = (size_t)s_phys[kp] * scale_page + (size_t)kvh * P + sub * kSlab;
+          const size_t so = (size_t)s_phys[kp] * scale_page + scale_head + sub * kSlab;
           const int tb = s_lp[kp] * P + sub * kSlab;
           if (tb >= t0 && tb + kSlab <= t1) {  // whole slab inside the split
   #pragma unroll

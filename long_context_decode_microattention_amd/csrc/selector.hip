@@ -125,8 +125,10 @@ __global__ __launch_bounds__(kSelThreads) void page_stats_kernel(SelectorParams 
   const int col = lane - tsk * R::LPR;
   const int NL = p.P / p.logical;
   const int tasks = p.Hkv * NL;
-  const char* page = static_cast<const char*>(p.k) + (size_t)phys * p.Hkv * p.P * R::RB +
-                     (size_t)col * 16;
+  // the (page, KV head) tile: [phys][kvh] of a page-major pool or [kvh][phys]
+  // of a head-major one; column t = kvh * NL + sub starts sub * logical rows in
+  const char* kpool = static_cast<const char*>(p.k) + (size_t)col * 16;
+  const size_t tile = (size_t)p.P * R::RB;
   const size_t head_stride = (size_t)p.NP * NL * 2 * R::RB;
   char* spage = static_cast<char*>(p.stats) + (size_t)phys * NL * 2 * R::RB + (size_t)col * 16;
 
@@ -141,7 +143,8 @@ __global__ __launch_bounds__(kSelThreads) void page_stats_kernel(SelectorParams 
       write = head_selected(p.select, kvh);
       if (write) nv = max(0, min(p.logical, L - (lp * p.P + sub * p.logical)));
     }
-    const char* src = page + (size_t)t * p.logical * R::RB;
+    const size_t tile_id = p.head_major ? (size_t)kvh * p.NP + phys : (size_t)phys * p.Hkv + kvh;
+    const char* src = kpool + tile_id * tile + (size_t)sub * p.logical * R::RB;
     float hi[R::EPL], lo[R::EPL];
 #pragma unroll
     for (int i = 0; i < R::EPL; ++i) {

@@ -23,7 +23,7 @@ def run_gpu(batch: wl.Batch, chunks: int = 0, workspace=None, schedule: int = 0)
     MA, m, e = _lib.micro_attention(batch.q, batch.k_pages, batch.v_pages, batch.block_table,
                                     batch.seq_lens, batch.split_bounds, batch.block_mask,
                                     scale=batch.scale, chunks=chunks, workspace=workspace,
-                                    schedule=schedule)
+                                    schedule=schedule, pool_layout=batch.layout)
     out = _lib.merge(MA, m, e)
     torch.cuda.synchronize()
     return out, MA, m, e
@@ -31,7 +31,7 @@ def run_gpu(batch: wl.Batch, chunks: int = 0, workspace=None, schedule: int = 0)
 
 def host_inputs(batch: wl.Batch):
     h = wl.host
-    return dict(q=h(batch.q), k_pool=h(batch.k_pages), v_pool=h(batch.v_pages),
+    return dict(q=h(batch.q), k_pool=h(batch.k_pm), v_pool=h(batch.v_pm),
                 block_table=h(batch.block_table), seq_lens=h(batch.seq_lens),
                 split_bounds=h(batch.split_bounds),
                 block_mask=None if batch.block_mask is None else h(batch.block_mask))
@@ -46,8 +46,8 @@ def sub_inputs(batch: wl.Batch, s: int, kv_lo: int, kv_hi: int):
     L = int(batch.seq_lens[s].item())
     n = -(-L // sp.P)
     pages = batch.block_table[s, :n].long()
-    k = batch.k_pages[:, kv_lo:kv_hi].index_select(0, pages).contiguous()
-    v = batch.v_pages[:, kv_lo:kv_hi].index_select(0, pages).contiguous()
+    k = batch.k_pm[:, kv_lo:kv_hi].index_select(0, pages).contiguous()
+    v = batch.v_pm[:, kv_lo:kv_hi].index_select(0, pages).contiguous()
     q = batch.q[s:s + 1, kv_lo * G:kv_hi * G].contiguous()
     sb = batch.split_bounds[s:s + 1]
     if batch.bounds_per_head:

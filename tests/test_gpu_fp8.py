@@ -108,7 +108,7 @@ def _run(b, dev_q, chunks=0, workspace=None):
     kc, ks, vc, vs = dev_q
     MA, m, e = _lib.micro_attention_fp8(b.q, kc, ks, vc, vs, b.block_table, b.seq_lens,
                                         b.split_bounds, b.block_mask, scale=b.scale, chunks=chunks,
-                                        workspace=workspace)
+                                        workspace=workspace, pool_layout=b.layout)
     out = _lib.merge(MA, m, e)
     torch.cuda.synchronize()
     return out, MA, m, e
@@ -186,12 +186,14 @@ def test_fp8_full_size_sampled(cfg):
     """Full-size workload quantized on the GPU and run in the launch
     configuration the benchmark times; sampled (request, KV head) units
     against the oracle on those units alone."""
-    spec = wl.CONFIGS[cfg]
-    announce("fp8 full", cfg)
+    spec = wl.CONFIGS[cfg].replace(layout=wl.PREFERRED_LAYOUT.get(cfg, "page"))
+    announce("fp8 full", cfg, spec.layout)
     b = wl.build(spec, 0, DEV)
     kc, ks = _lib.quantize_rows(b.k_pages)
     vc, vs = _lib.quantize_rows(b.v_pages)
     out, *_ = _run(b, (kc, ks, vc, vs))
+    if b.layout == "head":  # page-major views for the host-side selection below
+        kc, ks, vc, vs = (t.transpose(0, 1) for t in (kc, ks, vc, vs))
     h = wl.host
     G, P = spec.G, spec.P
     units = [(0, 0), (0, spec.Hkv - 1)] if spec.S == 1 else [(0, 5), (spec.S - 1, 2)]
@@ -203,7 +205,7 @@ def test_fp8_full_size_sampled(cfg):
         sub = lambda t: h(t[:, kvh:kvh + 1].index_select(0, pages).contiguous())  # noqa: E731
         kc_u, vc_u = sub(kc), sub(vc)
         ks_u, vs_u = sub(ks), sub(vs)
-        okc, oks = oq.quantize_rows(sub(b.k_pages))
+        okc, oks = oq.quantize_rows(sub(b.k_pm))
         assert np.array_equal(kc_u, okc) and np.array_equal(ks_u, oks), f"unit ({s},{kvh}) codes"
         q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
         mask = None

@@ -136,8 +136,8 @@ FULL_SAMPLES = {
 @pytest.mark.slow
 @pytest.mark.parametrize("cfg", ["C2", "C3", "C4", "C5"])
 def test_full_size_sampled(cfg):
-    spec = wl.CONFIGS[cfg]
-    announce("full", cfg)
+    spec = wl.CONFIGS[cfg].replace(layout=wl.PREFERRED_LAYOUT.get(cfg, "page"))
+    announce("full", cfg, spec.layout)
     b = wl.build(spec, 0, DEV)
     out, MA, m, e = run_gpu(b)
     samples = FULL_SAMPLES[cfg]
@@ -245,7 +245,7 @@ def test_shuffled_table_bitwise_equal_identity():
     spec = REDUCED["C4"].replace(Hq=4, Hkv=4, lens=("fixed", 16384 + 37))
     announce("shuffle-bitwise")
     a = wl.build(spec, 3, DEV)
-    n = a.k_pages.shape[0]
+    n = a.k_pm.shape[0]
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(9)).to(DEV)
     inv = torch.empty_like(perm)
     inv[perm] = torch.arange(n, device=DEV)
@@ -291,7 +291,7 @@ def test_nan_poison_never_read(cfg):
     sp = b.spec
     table = b.block_table.cpu().numpy()
     lens = b.seq_lens.cpu().numpy()
-    used = np.zeros(b.k_pages.shape[0], dtype=bool)
+    used = np.zeros(b.k_pm.shape[0], dtype=bool)
     for s in range(sp.S):
         n = -(-int(lens[s]) // sp.P)
         used[table[s, :n]] = True
@@ -457,7 +457,7 @@ def test_check_inputs_counts_violations():
     spec = REDUCED["C3"]
     announce("check-inputs")
     b = wl.build(spec, 0, DEV)
-    NP = b.k_pages.shape[0]
+    NP = b.k_pm.shape[0]
     assert _lib.check_inputs(b.block_table, b.seq_lens, NP, spec.P) == 0
     bad = b.block_table.clone()
     lens = b.seq_lens.cpu().numpy()

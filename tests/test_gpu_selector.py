@@ -255,13 +255,14 @@ def test_selector_full_c5_sampled():
     16-token logical pages) in the launch configuration the benchmark times;
     statistics, scores and mask of sampled (request, KV head) units against
     the oracle run on those units alone."""
-    spec = wl.CONFIGS["C5"]
-    announce("selector full", spec.name)
+    spec = wl.CONFIGS["C5"].replace(layout=wl.PREFERRED_LAYOUT.get("C5", "page"))
+    announce("selector full", spec.name, spec.layout)
     b = wl.build(spec, 0, DEV)
     P, G, logical = spec.P, spec.G, 16
     flags = _select_flags("upper", spec.Hkv)
     sel_t = torch.from_numpy(flags).to(DEV)
-    stats = _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical)
+    stats = _lib.page_stats(b.k_pages, b.block_table, b.seq_lens, logical=logical,
+                            pool_layout=b.layout)
     scores = _lib.page_scores(b.q, stats, b.block_table, b.seq_lens, P=P, select_heads=sel_t)
     npg = -(-spec.max_len // P)  # pages holding each request's tokens
     budget = (npg - 3) // 4
@@ -274,7 +275,7 @@ def test_selector_full_c5_sampled():
         L = int(b.seq_lens[s].item())
         n = osel.n_pages(L, P)
         pages = b.block_table[s, :n].long()
-        k = h(b.k_pages[:, kvh:kvh + 1].index_select(0, pages).contiguous())
+        k = h(b.k_pm[:, kvh:kvh + 1].index_select(0, pages).contiguous())
         q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
         table = np.arange(n, dtype=np.int32)[None, :]
         lens = np.array([L], dtype=np.int32)
