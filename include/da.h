@@ -225,6 +225,36 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
                    float* out, hipStream_t stream);
 
 /*
+ * Fold b partials per (request, query head) into ONE partial triple and write
+ * it into slot `out_slot` of a gather buffer: the aggregation equations of
+ * the Infinite-LLM page (section 方法细节) without the final division,
+ *   m'  = max_j m_j
+ *   e'  = sum_j e_j * exp(m_j - m')
+ *   MA' = sum_j MA_j * exp(m_j - m')
+ * which is again the MicroAttention triple of the union of the partials'
+ * token sets, so folded triples merge like any others.  This is an
+ * instance's local step in distributed decoding (LoongServe page, section
+ * 4.2, single- and multi-master decoding: instances compute local attention
+ * and send results to the master): each instance folds its own splits, the
+ * triples are gathered into one buffer, and the master calls da_merge on it
+ * with max_splits = out_splits.
+ *
+ *   MA [S, Hq, b, D], m [S, Hq, b], e [S, Hq, b] float32 as for da_merge
+ *   (b = sh->max_splits).
+ *   MA_out [S, Hq, out_splits, D], m_out and e_out [S, Hq, out_splits]
+ *   float32, caller-owned; only slot out_slot of each (request, head) is
+ *   written, every other slot is left as it is.  A (request, head) whose
+ *   partials are all empty gets (MA', m', e') = (0, -inf, 0).
+ * The outputs must not overlap the inputs.  Reads sh->S, Hq, D and
+ * max_splits only.
+ * Errors: DA_ERR_INVALID_ARG (NULL or misaligned pointer, sizes < 1,
+ * out_splits < 1, out_slot outside [0, out_splits)), DA_ERR_HIP.
+ */
+da_status da_merge_partials(const da_shape* sh, const float* MA, const float* m, const float* e,
+                            int32_t out_splits, int32_t out_slot, float* MA_out, float* m_out,
+                            float* e_out, hipStream_t stream);
+
+/*
  * Device-side validation of the array contents that da_micro_attention
  * trusts: 0 <= seq_lens[s] <= max_pages * P for every request, and
  * 0 <= block_table[s, lp] < NP for every logical page lp < ceil(L_s / P)

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     check_inputs,
     load,
     merge,
+    merge_partials,
     micro_attention,
     stream_read,
 )

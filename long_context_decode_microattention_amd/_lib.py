@@ -73,6 +73,9 @@ def load() -> ctypes.CDLL:
     lib.da_micro_attention_workspace_size.restype = ctypes.c_int
     lib.da_merge.argtypes = [sp, _VP, _VP, _VP, _VP, _VP]
     lib.da_merge.restype = ctypes.c_int
+    lib.da_merge_partials.argtypes = [sp, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP,
+                                      _VP, _VP]
+    lib.da_merge_partials.restype = ctypes.c_int
     lib.da_check_inputs.argtypes = [sp, _VP, _VP, _VP, _VP]
     lib.da_check_inputs.restype = ctypes.c_int
     lib.da_last_error.argtypes = []
@@ -325,6 +328,39 @@ def merge(MA, m, e, *, out=None):
     sh = DaShape(S=S, Hq=Hq, Hkv=1, D=D, P=1, max_pages=1, max_splits=B, bounds_per_head=0,
                  dtype=DA_F32, scale=1.0, NP=1)
     _check(load().da_merge(ctypes.byref(sh), _ptr(MA), _ptr(m), _ptr(e), _ptr(out), _stream(dev)))
+    return out
+
+
+def merge_partials(MA, m, e, *, out=None, slot: int = 0, out_splits: int = 1):
+    """Fold the b partials of each (request, head) into one triple written to
+    slot `slot` of a gather buffer via da_merge_partials.
+
+    out: (MA_out [S, Hq, out_splits, D], m_out, e_out [S, Hq, out_splits])
+    float32 tensors to write into (other slots are left untouched); when
+    None, fresh buffers with out_splits slots are allocated.  Returns out."""
+    dev = MA.device
+    _need(MA, "MA", torch.float32, dev, 4)
+    _need(m, "m", torch.float32, dev, 3)
+    _need(e, "e", torch.float32, dev, 3)
+    S, Hq, B, D = MA.shape
+    if tuple(m.shape) != (S, Hq, B) or tuple(e.shape) != (S, Hq, B):
+        raise ValueError("m and e must be [S, Hq, b]")
+    if out is None:
+        out = (torch.zeros((S, Hq, out_splits, D), dtype=torch.float32, device=dev),
+               torch.full((S, Hq, out_splits), float("-inf"), dtype=torch.float32, device=dev),
+               torch.zeros((S, Hq, out_splits), dtype=torch.float32, device=dev))
+    MA_o, m_o, e_o = out
+    _need(MA_o, "MA_out", torch.float32, dev, 4)
+    _need(m_o, "m_out", torch.float32, dev, 3)
+    _need(e_o, "e_out", torch.float32, dev, 3)
+    n_out = MA_o.shape[2]
+    if (tuple(MA_o.shape) != (S, Hq, n_out, D) or tuple(m_o.shape) != (S, Hq, n_out)
+            or tuple(e_o.shape) != (S, Hq, n_out)):
+        raise ValueError("out must be ([S, Hq, n, D], [S, Hq, n], [S, Hq, n])")
+    sh = DaShape(S=S, Hq=Hq, Hkv=1, D=D, P=1, max_pages=1, max_splits=B, bounds_per_head=0,
+                 dtype=DA_F32, scale=1.0, NP=1)
+    _check(load().da_merge_partials(ctypes.byref(sh), _ptr(MA), _ptr(m), _ptr(e), n_out, slot,
+                                    _ptr(MA_o), _ptr(m_o), _ptr(e_o), _stream(dev)))
     return out
 
 

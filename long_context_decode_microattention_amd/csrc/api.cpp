@@ -297,6 +297,31 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
   return DA_OK;
 }
 
+da_status da_merge_partials(const da_shape* sh, const float* MA, const float* m, const float* e,
+                            int32_t out_splits, int32_t out_slot, float* MA_out, float* m_out,
+                            float* e_out, hipStream_t stream) {
+  if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->S < 1 || sh->Hq < 1 || sh->D < 1 || sh->max_splits < 1)
+    return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hq=%d D=%d max_splits=%d)", sh->S,
+                sh->Hq, sh->D, sh->max_splits);
+  if ((long long)sh->S * sh->Hq > INT_MAX)
+    return fail(DA_ERR_INVALID_ARG, "S * Hq exceeds the launch range");
+  if (out_splits < 1 || out_slot < 0 || out_slot >= out_splits)
+    return fail(DA_ERR_INVALID_ARG, "out_slot %d outside [0, out_splits = %d)", out_slot,
+                out_splits);
+  if (!MA || !m || !e || !MA_out || !m_out || !e_out)
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(MA, 4) || !aligned(m, 4) || !aligned(e, 4) || !aligned(MA_out, 4) ||
+      !aligned(m_out, 4) || !aligned(e_out, 4))
+    return fail(DA_ERR_INVALID_ARG, "float arrays must be 4-byte aligned");
+  const hipError_t err = da::launch_merge_partials(MA, m, e, MA_out, m_out, e_out, sh->S, sh->Hq,
+                                                   sh->D, sh->max_splits, out_splits, out_slot,
+                                                   stream);
+  if (err != hipSuccess)
+    return fail(DA_ERR_HIP, "partial merge launch failed: %s", hipGetErrorString(err));
+  return DA_OK;
+}
+
 da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
                           const int32_t* seq_lens, int32_t* err, hipStream_t stream) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");

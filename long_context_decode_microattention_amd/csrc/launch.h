@@ -57,6 +57,10 @@ hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, fl
 hipError_t launch_merge(const float* MA, const float* m, const float* e, float* out, int S, int Hq,
                         int D, int B, hipStream_t stream);
 
+hipError_t launch_merge_partials(const float* MA, const float* m, const float* e, float* MA_out,
+                                 float* m_out, float* e_out, int S, int Hq, int D, int B,
+                                 int out_splits, int slot, hipStream_t stream);
+
 hipError_t launch_check_inputs(const int32_t* table, const int32_t* lens, int S, int P,
                                int max_pages, int64_t NP, int32_t* err, hipStream_t stream);
 

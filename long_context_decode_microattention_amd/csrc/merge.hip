@@ -4,6 +4,11 @@
 // (Infinite-LLM page, section 方法细节, aggregation equations).  Empty
 // partials (m_j = -inf) get weight exp(-inf) = 0; if all are empty, out = 0.
 //
+// The partial form (kPartial) stops before the division and writes the
+// triple (sum_j MA_j exp(m_j - m_g), m_g, e_g) into one slot of a gather
+// buffer [S, Hq, out_splits, .]: the fold an instance applies to its own
+// splits before sending one triple per (request, head) back to the master.
+//
 // The split weights exp(m_j - m_g) are computed once per chunk of 256 splits
 // into LDS; the 256 lanes then cover (split phase, dimension) pairs so that
 // the loads of MA_j for many splits are in flight together.
@@ -28,11 +33,14 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+template <bool kPartial>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ MA,
                                                               const float* __restrict__ m,
                                                               const float* __restrict__ e,
-                                                              float* __restrict__ out, int D,
-                                                              int B) {
+                                                              float* __restrict__ out,
+                                                              float* __restrict__ m_out,
+                                                              float* __restrict__ e_out, int D,
+                                                              int B, int out_splits, int slot) {
   __shared__ float s_w[kMergeThreads];
   __shared__ float s_red[kMergeWaves];
   __shared__ float s_acc[kMergeThreads];
@@ -43,6 +51,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const float* mr = m + sh * B;
   const float* er = e + sh * B;
   const float* MAr = MA + sh * (size_t)B * D;
+  // the output row: out [S, Hq, D], or slot `slot` of [S, Hq, out_splits, D]
+  const size_t orow = kPartial ? sh * out_splits + slot : sh;
 
   // m_g
   float lm = neg_inf();
@@ -94,12 +104,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   float eg = 0.f;
 #pragma unroll
   for (int w = 0; w < kMergeWaves; ++w) eg += s_red[w];
+  if (kPartial && tid == 0) {
+    m_out[orow] = M;
+    e_out[orow] = eg;
+  }
 
   if (D <= kMergeThreads) {
     if (tid < D) {
       float total = 0.f;
       for (int q = 0; q < nph; ++q) total += s_acc[q * D + tid];
-      out[sh * D + tid] = eg > 0.f ? total / eg : 0.f;
+      out[orow * D + tid] = kPartial ? total : (eg > 0.f ? total / eg : 0.f);
     }
   } else {
     // D > 256: every lane owns a strided set of dimensions (not used by the
@@ -107,7 +121,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
     for (int dd = tid; dd < D; dd += kMergeThreads) {
       float t = 0.f;
       for (int j = 0; j < B; ++j) t = fmaf(MAr[(size_t)j * D + dd], expf(mr[j] - Ms), t);
-      out[sh * D + dd] = eg > 0.f ? t / eg : 0.f;
+      out[orow * D + dd] = kPartial ? t : (eg > 0.f ? t / eg : 0.f);
     }
   }
 }
@@ -163,8 +177,17 @@ hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, fl
 hipError_t launch_merge(const float* MA, const float* m, const float* e, float* out, int S, int Hq,
                         int D, int B, hipStream_t stream) {
   const long long n = (long long)S * Hq;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n), dim3(kMergeThreads), 0, stream, MA, m, e,
-                     out, D, B);
+  hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)n), dim3(kMergeThreads), 0, stream, MA, m,
+                     e, out, nullptr, nullptr, D, B, 1, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_partials(const float* MA, const float* m, const float* e, float* MA_out,
+                                 float* m_out, float* e_out, int S, int Hq, int D, int B,
+                                 int out_splits, int slot, hipStream_t stream) {
+  const long long n = (long long)S * Hq;
+  hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)n), dim3(kMergeThreads), 0, stream, MA, m,
+                     e, MA_out, m_out, e_out, D, B, out_splits, slot);
   return hipGetLastError();
 }
 

@@ -292,6 +292,29 @@ def check_associativity(o):
     assert np.max(np.abs(o.merge(*cat) - ref)) < 1e-12
 
 
+def check_fold_is_union_partial(o):
+    """Folding the partials of any splits (empty ones included) gives the
+    MicroAttention triple of the whole token range computed in one piece:
+    the same maximum, exp-sum and unnormalised sum, not only the same
+    attention after division."""
+    rng = np.random.default_rng(57)
+    q, kp, vp, table, lens = _random_problem(rng)
+    whole = np.array([[[0, int(L)]] for L in lens], dtype=np.int32)
+    wMA, wm, we = o.micro_attention(q, kp, vp, table, lens, whole)
+    for b in (1, 3, 8):
+        sb = np.stack([_random_bounds(rng, int(L), b) for L in lens])[:, None, :]
+        if b > 1:
+            sb[:, :, 1] = 0  # the first split is empty
+        MA, m, e = o.micro_attention(q, kp, vp, table, lens, sb)
+        fMA, fm, fe = o.merge_partials(MA, m, e)
+        assert np.max(np.abs(fm - wm[:, :, 0])) < 1e-12, b  # scores of subsets: fp64 rounding
+        assert np.max(np.abs(fe / we[:, :, 0] - 1)) < 1e-12, b
+        assert np.max(np.abs(fMA - wMA[:, :, 0]) / we[:, :, 0, None]) < 1e-12, b
+    # all partials empty: the empty triple
+    z = o.merge_partials(np.zeros((1, 1, 3, 2)), np.full((1, 1, 3), -np.inf), np.zeros((1, 1, 3)))
+    assert np.all(z[0] == 0) and np.isneginf(z[1]).all() and np.all(z[2] == 0)
+
+
 def check_mask_compaction(o):
     """Masked attention equals dense attention over a new contiguous cache that
     holds only the kept pages' tokens, copied out by plain loops."""
@@ -380,6 +403,7 @@ ALL_CHECKS = [
     check_split_order,
     check_per_head_bounds,
     check_associativity,
+    check_fold_is_union_partial,
     check_mask_compaction,
     check_bounds_clamp,
     check_golden_worked_example,

@@ -111,6 +111,30 @@ def test_merge_rejects(lib):
     assert lib.da_merge(ctypes.byref(sh), vp(FAKE + 2), vp(FAKE), vp(FAKE), vp(FAKE), None) == _lib.DA_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("case", [
+    dict(sh=None),
+    dict(shape=dict(max_splits=0)),
+    dict(shape=dict(D=0)),
+    dict(n_out=0, slot=0),
+    dict(n_out=4, slot=4),
+    dict(n_out=4, slot=-1),
+    dict(ptrs=dict(MA=None)),
+    dict(ptrs=dict(m_out=None)),
+    dict(ptrs=dict(e_out=FAKE + 2)),
+    dict(ptrs=dict(MA_out=FAKE + 1)),
+], ids=lambda x: str(x))
+def test_merge_partials_rejects(lib, case):
+    sh = None if "sh" in case else good_shape(**case.get("shape", {}))
+    p = dict(MA=FAKE, m=FAKE, e=FAKE, MA_out=FAKE, m_out=FAKE, e_out=FAKE)
+    p.update(case.get("ptrs", {}))
+    got = lib.da_merge_partials(None if sh is None else ctypes.byref(sh), _vp(p["MA"]),
+                                _vp(p["m"]), _vp(p["e"]), case.get("n_out", 2),
+                                case.get("slot", 1), _vp(p["MA_out"]), _vp(p["m_out"]),
+                                _vp(p["e_out"]), None)
+    assert got == _lib.DA_ERR_INVALID_ARG, lib.da_last_error()
+    assert len(lib.da_last_error()) > 0
+
+
 def test_check_inputs_and_stream_read_reject(lib):
     vp = ctypes.c_void_p
     sh = good_shape()

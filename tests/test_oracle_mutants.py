@@ -12,6 +12,7 @@ from oracle_pins import ALL_CHECKS
 
 _MICRO = oa.micro_tokens
 _KEPT = oa.kept_tokens
+_FOLD = oa.merge_partials
 
 
 def _no_scale(q, K, scale):
@@ -86,6 +87,16 @@ def _widen_wrong(x):
     return a.astype(np.float64)
 
 
+def _fold_unweighted_sum(MA, m, e):
+    MAf, mf, ef = _FOLD(MA, m, e)
+    return np.asarray(MA, dtype=np.float64).sum(axis=-2), mf, ef
+
+
+def _fold_normalised(MA, m, e):
+    MAf, mf, ef = _FOLD(MA, m, e)
+    return MAf / np.where(ef > 0, ef, 1.0)[..., None], mf, ef
+
+
 MUTANTS = {
     "scores: scale dropped": ("scores", _no_scale),
     "scores: sqrt of scale": ("scores", _sqrt_scale),
@@ -98,6 +109,8 @@ MUTANTS = {
     "mask ignored": ("kept_tokens", _kept_ignore_mask),
     "seq_len clamp dropped": ("kept_tokens", _kept_no_clamp),
     "merge: weights not rescaled": ("_weights", _weights_unshifted),
+    "fold: MA' not rescaled": ("merge_partials", _fold_unweighted_sum),
+    "fold: MA' divided by e'": ("merge_partials", _fold_normalised),
     "bf16 widen: wrong shift": ("to_f64", _widen_wrong),
 }
 
