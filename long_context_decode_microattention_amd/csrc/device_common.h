@@ -19,13 +19,14 @@ constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8-lane half row
 constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i inside each 16-lane row
 
-// Every permutation used here reads a lane of the same row, so the "old"
-// operand is never selected; passing the source itself saves a zeroed
-// register per call.
+// Every permutation used here reads a lane of the same row, so no lane takes
+// the bound-control fill; a plain DPP move with that fill lets the compiler
+// fold the permutation into the instruction that consumes it (one
+// v_add_f32_dpp / v_max_f32_dpp instead of two moves and the operation).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   const int xi = __builtin_bit_cast(int, x);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(xi, xi, CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, CTRL, 0xF, 0xF, true));
 }
 
 // True in every lane if `c` holds in any lane (a scalar, wave-uniform value:

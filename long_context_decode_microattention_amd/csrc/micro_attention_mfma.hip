@@ -78,9 +78,6 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
   return make_uint2(t.x, t.y);
 }
 
-template <bool B>
-using Bool = std::integral_constant<bool, B>;
-
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp<kDppQuadXor1>(x));
   x = fmaxf(x, dpp<kDppQuadXor2>(x));
@@ -110,7 +107,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // the wave index is the same in every lane; saying so keeps the slab loop,
+  // its page lookups and its address arithmetic on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15;  // score column: token within the slab
   const int grp = lane >> 4;  // score row group: heads 4*grp .. 4*grp+3
   const int vrow = lane / L::LPT;
@@ -152,17 +151,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 
     if (it.scan0 < it.scan1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
+      // slabs per page: P is a power of two, so slab sl is slab (sl & (spp - 1))
+      // of kept page (sl >> spp_log)
       const int spp = P / kSlab;
-      // page-major pool [NP, Hkv, P, D] or head-major pool [Hkv, NP, P, D]
-      const size_t page_stride = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P * L::TOKB;
-      const size_t head_off = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P * L::TOKB;
+      const int spp_log = __builtin_ctz(spp);
+      // rows are counted from this KV head's first row: a page-major pool
+      // [NP, Hkv, P, D] holds Hkv * P rows per page, a head-major pool
+      // [Hkv, NP, P, D] holds P; the fp8 row scales share the row numbering
+      const int page_rows = p.head_major ? P : p.Hkv * P;
+      const size_t head_row = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
       // key lane: token col; bf16: 16 bytes per step at 64*step + 16*grp;
       // fp8: 8*KS contiguous bytes at 8*KS*grp
-      const char* kbase = static_cast<const char*>(p.k) + head_off +
+      const char* kbase = static_cast<const char*>(p.k) + head_row * L::TOKB +
                           (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
-      const char* vbase = static_cast<const char*>(p.v) + head_off + lane * L::VB;
-      const size_t scale_page = (p.head_major ? (size_t)1 : (size_t)p.Hkv) * P;  // fp8 scales
-      const size_t scale_head = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
+      const char* vbase = static_cast<const char*>(p.v) + head_row * L::TOKB + lane * L::VB;
+      // fp8: the K scale of the key lane's token, the V scales of the value
+      // lane's rows (no scales for bf16 pages)
+      const float* ksb = DT == 2 ? p.ks + head_row + col : nullptr;
+      const float* vsb = DT == 2 ? p.vs + head_row + vrow : nullptr;
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
@@ -171,50 +177,68 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         // key load j of a lane: bf16 64*j (one score step), fp8 16*j (two steps)
         constexpr int KSTRIDE = DT == 1 ? 64 : 16;
         constexpr int VSTRIDE = L::TPI * L::TOKB;  // bytes per value load
+
+        // where slab sl lives; the page ids are read from LDS as wave-uniform
+        // values so that the offsets are computed on the scalar unit
+        struct Pos {
+          size_t row;  // the slab's first row (pool bytes: row * TOKB)
+          int tb;      // logical token of the slab's first row
+          bool whole;  // every row of the slab lies inside the split
+        };
+        auto pos = [&](int sl) {
+          const int kp = sl >> spp_log;
+          const int sub = sl & (spp - 1);
+          const int phys = __builtin_amdgcn_readfirstlane(s_phys[kp]);
+          const int lp = __builtin_amdgcn_readfirstlane(s_lp[kp]);
+          Pos q;
+          q.row = (size_t)phys * page_rows + sub * kSlab;
+          q.tb = lp * P + sub * kSlab;
+          q.whole = q.tb >= t0 && q.tb + kSlab <= t1;
+          return q;
+        };
+
         auto load = [&](int sl, MFrag<DT, D>& f) {
-          const int kp = sl / spp;
-          const int sub = sl - kp * spp;
-          const size_t off = (size_t)s_phys[kp] * page_stride + (size_t)sub * (kSlab * L::TOKB);
-          const size_t so = (size_t)s_phys[kp] * scale_page + scale_head + sub * kSlab;
-          const int tb = s_lp[kp] * P + sub * kSlab;
-          if (tb >= t0 && tb + kSlab <= t1) {  // whole slab inside the split
+          const Pos q = pos(sl);
+          const size_t off = q.row * L::TOKB;
+          if (q.whole) {
   #pragma unroll
             for (int j = 0; j < L::KL; ++j) f.k[j] = load_stream16(kbase + off + j * KSTRIDE);
-            if constexpr (DT == 2) f.ksc = p.ks[so + col];
+            if constexpr (DT == 2) f.ksc = ksb[q.row];
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               if constexpr (DT == 1) {
                 f.v[i] = load_stream16(vbase + off + i * VSTRIDE);
               } else {
                 f.v8[i] = load_stream8(vbase + off + i * VSTRIDE);
-                f.vsc[i] = p.vs[so + i * L::TPI + vrow];
+                f.vsc[i] = vsb[q.row + i * L::TPI];
               }
             }
-          } else {  // tokens outside the split read as zeros (and zero scales)
-            const int tk = tb + col;
+          } else {  // rows outside the split read as zeros (and zero scales)
+            const int tk = q.tb + col;
             const bool kok = tk >= t0 && tk < t1;
   #pragma unroll
             for (int j = 0; j < L::KL; ++j)
               f.k[j] = kok ? load_stream16(kbase + off + j * KSTRIDE) : make_uint4(0, 0, 0, 0);
-            if constexpr (DT == 2) f.ksc = kok ? p.ks[so + col] : 0.f;
+            if constexpr (DT == 2) f.ksc = kok ? ksb[q.row] : 0.f;
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
-              const int tv = tb + i * L::TPI + vrow;
+              const int tv = q.tb + i * L::TPI + vrow;
               const bool vok = tv >= t0 && tv < t1;
               if constexpr (DT == 1) {
                 f.v[i] = vok ? load_stream16(vbase + off + i * VSTRIDE) : make_uint4(0, 0, 0, 0);
               } else {
                 f.v8[i] = vok ? load_stream8(vbase + off + i * VSTRIDE) : make_uint2(0, 0);
-                f.vsc[i] = vok ? p.vs[so + i * L::TPI + vrow] : 0.f;
+                f.vsc[i] = vok ? vsb[q.row + i * L::TPI] : 0.f;
               }
             }
           }
         };
 
-        auto compute = [&](int sl, const MFrag<DT, D>& f, auto full_tag) {
-          constexpr bool FULL = decltype(full_tag)::value;
-          const int kp = sl / spp;
-          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
+        // One slab.  A slab cut by the split bounds differs only in its
+        // scores: rows outside the split score -inf (probability 0), and their
+        // keys and values were loaded as zeros.
+        auto compute = [&](int sl, const MFrag<DT, D>& f) {
+          const Pos q = pos(sl);
 
           // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
           f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -231,26 +255,31 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                                                         __builtin_bit_cast(bf16x8_t, kb), sc, 0, 0, 0);
           }
           if constexpr (DT == 2) sc *= f.ksc;
-          const bool kvalid = FULL || (tb + col >= t0 && tb + col < t1);
+          if (!q.whole) {  // wave-uniform branch
+            const bool kvalid = q.tb + col >= t0 && q.tb + col < t1;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = kvalid ? sc[i] : neg_inf();
+          }
 
           // slab maxima per head, then the running maxima (wave-uniform)
           float rm[4];
   #pragma unroll
-          for (int i = 0; i < 4; ++i) rm[i] = row_max16(kvalid ? sc[i] : neg_inf());
+          for (int i = 0; i < 4; ++i) rm[i] = row_max16(sc[i]);
           float alpha_h[G], nmc_h[G];
           bool moved = false;
   #pragma unroll
           for (int h = 0; h < G; ++h) {
             const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
             const float mn = fmaxf(m_h[h], mx);
-            const float ms = (FULL || mn != neg_inf()) ? mn : 0.f;
+            const float ms = mn != neg_inf() ? mn : 0.f;
             alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
             nmc_h[h] = -ms * c;
             moved |= mn != m_h[h];
             m_h[h] = mn;
           }
 
-          // probabilities in the score layout; exp-sums per token column
+          // probabilities in the score layout (0 for rows scored -inf);
+          // exp-sums per token column
           float pw[4];
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -262,7 +291,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                 al = alpha_h[4 + i];
               }
             }
-            pw[i] = kvalid ? fast_exp2(fmaf(sc[i], c, nmc)) : 0.f;
+            pw[i] = fast_exp2(fmaf(sc[i], c, nmc));
             e_l[i] = fmaf(e_l[i], al, pw[i]);
           }
 
@@ -314,44 +343,43 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           }
         };
 
-        auto step = [&](int sl, const MFrag<DT, D>& f) {
-          const int kp = sl / spp;
-          const int tb = s_lp[kp] * P + (sl - kp * spp) * kSlab;
-          if (tb >= t0 && tb + kSlab <= t1)
-            compute(sl, f, Bool<true>{});
-          else
-            compute(sl, f, Bool<false>{});
-        };
-
-        if constexpr (DT == 1) {
-          // bf16: one slab in flight while the other is computed
+        constexpr int W = kMicroWaves;
+        if constexpr (DT == 1 || G == 8) {
+          // bf16 (and fp8 with G = 8, whose accumulators leave no registers
+          // for a third fragment): one slab in flight while the other is
+          // computed
           MFrag<DT, D> fa, fb;
           int sl = wave;
           if (sl < nslab) load(sl, fa);
           while (sl < nslab) {
-            int sn = sl + kMicroWaves;
-            if (sn < nslab) load(sn, fb);
-            step(sl, fa);
-            sl = sn;
+            if (sl + W < nslab) load(sl + W, fb);
+            compute(sl, fa);
+            sl += W;
             if (sl >= nslab) break;
-            sn = sl + kMicroWaves;
-            if (sn < nslab) load(sn, fa);
-            step(sl, fb);
-            sl = sn;
+            if (sl + W < nslab) load(sl + W, fa);
+            compute(sl, fb);
+            sl += W;
           }
         } else {
-          // fp8: a slab carries half the bytes, so two are kept in flight
-          // (the 8-bit fragments fit the same register budget)
+          // fp8: a slab carries half the bytes, so two are kept in flight; the
+          // three fragments take turns (no register copies, which would have
+          // to wait for the loads in flight)
           MFrag<DT, D> f0, f1, f2;
           int sl = wave;
           if (sl < nslab) load(sl, f0);
-          if (sl + kMicroWaves < nslab) load(sl + kMicroWaves, f1);
+          if (sl + W < nslab) load(sl + W, f1);
           while (sl < nslab) {
-            if (sl + 2 * kMicroWaves < nslab) load(sl + 2 * kMicroWaves, f2);
-            step(sl, f0);
-            f0 = f1;
-            f1 = f2;
-            sl += kMicroWaves;
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f2);
+            compute(sl, f0);
+            sl += W;
+            if (sl >= nslab) break;
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f0);
+            compute(sl, f1);
+            sl += W;
+            if (sl >= nslab) break;
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f1);
+            compute(sl, f2);
+            sl += W;
           }
         }
         __syncthreads();  // the page list is rewritten by the next batch
