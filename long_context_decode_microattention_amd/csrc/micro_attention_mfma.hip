@@ -34,7 +34,10 @@
 // grp*D/4 + 8*step, q in the same order) are widened exactly to bf16 for the
 // score MFMA and the score column is multiplied by its token's K scale; the
 // value codes (8 per lane, 8-byte loads in the same row layout) are widened
-// exactly to fp32 and a token's V scale multiplies its probability operand.
+// exactly to fp32.  A token's V scale multiplies its probabilities in the
+// score layout (where the lane of token `col` loads it next to the K scale),
+// so the value operand arrives in LDS already scaled; the exp-sums take the
+// unscaled probabilities.
 #include "micro_common.h"
 
 namespace da {
@@ -63,7 +66,7 @@ struct MFrag {
   uint4 v[DT == 1 ? MLayout<DT, D>::NI : 1];  // bf16 values
   uint2 v8[DT == 2 ? MLayout<DT, D>::NI : 1];  // fp8 values
   float ksc;                                   // fp8: K scale of token `col`
-  float vsc[MLayout<DT, D>::NI];               // fp8: V scales of the value rows
+  float vsc;                                   // fp8: V scale of token `col`
 };
 
 // Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly.
@@ -165,10 +168,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       const char* kbase = static_cast<const char*>(p.k) + head_row * L::TOKB +
                           (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
       const char* vbase = static_cast<const char*>(p.v) + head_row * L::TOKB + lane * L::VB;
-      // fp8: the K scale of the key lane's token, the V scales of the value
-      // lane's rows (no scales for bf16 pages)
+      // fp8: the K and V scales of the key lane's token (no scales for bf16)
       const float* ksb = DT == 2 ? p.ks + head_row + col : nullptr;
-      const float* vsb = DT == 2 ? p.vs + head_row + vrow : nullptr;
+      const float* vsb = DT == 2 ? p.vs + head_row + col : nullptr;
 
       for (int base = it.scan0; base < it.scan1; base += kPageCap) {
         const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
@@ -203,14 +205,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           if (q.whole) {
   #pragma unroll
             for (int j = 0; j < L::KL; ++j) f.k[j] = load_stream16(kbase + off + j * KSTRIDE);
-            if constexpr (DT == 2) f.ksc = ksb[q.row];
+            if constexpr (DT == 2) {
+              f.ksc = ksb[q.row];
+              f.vsc = vsb[q.row];
+            }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               if constexpr (DT == 1) {
                 f.v[i] = load_stream16(vbase + off + i * VSTRIDE);
               } else {
                 f.v8[i] = load_stream8(vbase + off + i * VSTRIDE);
-                f.vsc[i] = vsb[q.row + i * L::TPI];
               }
             }
           } else {  // rows outside the split read as zeros (and zero scales)
@@ -219,7 +223,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   #pragma unroll
             for (int j = 0; j < L::KL; ++j)
               f.k[j] = kok ? load_stream16(kbase + off + j * KSTRIDE) : make_uint4(0, 0, 0, 0);
-            if constexpr (DT == 2) f.ksc = kok ? ksb[q.row] : 0.f;
+            if constexpr (DT == 2) {
+              f.ksc = kok ? ksb[q.row] : 0.f;
+              f.vsc = kok ? vsb[q.row] : 0.f;
+            }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
               const int tv = q.tb + i * L::TPI + vrow;
@@ -228,7 +235,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                 f.v[i] = vok ? load_stream16(vbase + off + i * VSTRIDE) : make_uint4(0, 0, 0, 0);
               } else {
                 f.v8[i] = vok ? load_stream8(vbase + off + i * VSTRIDE) : make_uint2(0, 0);
-                f.vsc[i] = vok ? vsb[q.row + i * L::TPI] : 0.f;
               }
             }
           }
@@ -295,12 +301,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             e_l[i] = fmaf(e_l[i], al, pw[i]);
           }
 
-          // probabilities to the value-product operand layout (per-wave LDS)
+          // probabilities to the value-product operand layout (per-wave LDS);
+          // over 8-bit pages each carries its token's V scale
           float* sp = s_p[wave];
           if (grp < HS) {
   #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (4 * grp + i < G) sp[col * G + 4 * grp + i] = pw[i];
+              if (4 * grp + i < G) sp[col * G + 4 * grp + i] = DT == 2 ? pw[i] * f.vsc : pw[i];
           }
 
           if (wave_any(moved)) {  // scalar branch: skipped, not masked
@@ -320,7 +327,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   #pragma unroll
             for (int hs = 0; hs < HS; ++hs) {
               pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
-              if constexpr (DT == 2) pa[hs] *= f.vsc[j];
             }
             float vf[8];
             if constexpr (DT == 1) {
