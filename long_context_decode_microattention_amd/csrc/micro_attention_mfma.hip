@@ -47,26 +47,30 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // DT: 1 = bf16 pages, 2 = fp8 E4M3 pages with per-row scales.  Either way a
-// value lane holds 8 dims of one token row (LPT lanes per row).
-template <int DT, int D>
+// value lane holds 8 dims of one token row (LPT lanes per row).  A slab is SL
+// = 16 or 32 tokens: NG score groups of 16 tokens (token 16*g + col of group
+// g in score column col).
+template <int DT, int D, int SL>
 struct MLayout {
   static constexpr int TOKB = DT == 1 ? D * 2 : D;  // token row bytes
   static constexpr int LPT = D / 8;                // value lanes per token row
   static constexpr int TPI = kWave / LPT;          // token rows per value load
-  static constexpr int NI = kSlab / TPI;           // value loads per slab
+  static constexpr int NI = SL / TPI;              // value loads per slab
+  static constexpr int NG = SL / 16;               // score groups per slab
   static constexpr int KS = D / 32;                // score k-steps
   static constexpr int KL = DT == 1 ? KS : KS / 2; // 16-byte key loads per lane
   static constexpr int VB = 8 * (TOKB / D);        // value bytes per lane per load
   static constexpr int EPL = 8;                    // elements per lane
 };
 
-template <int DT, int D>
+template <int DT, int D, int SL>
 struct MFrag {
-  uint4 k[MLayout<DT, D>::KL];
-  uint4 v[DT == 1 ? MLayout<DT, D>::NI : 1];  // bf16 values
-  uint2 v8[DT == 2 ? MLayout<DT, D>::NI : 1];  // fp8 values
-  float ksc;                                   // fp8: K scale of token `col`
-  float vsc;                                   // fp8: V scale of token `col`
+  using L = MLayout<DT, D, SL>;
+  uint4 k[L::NG][L::KL];
+  uint4 v[DT == 1 ? L::NI : 1];   // bf16 values
+  uint2 v8[DT == 2 ? L::NI : 1];  // fp8 values
+  float ksc[L::NG];               // fp8: K scale of token 16*g + col
+  float vsc[L::NG];               // fp8: V scale of token 16*g + col
 };
 
 // Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly.
@@ -96,16 +100,16 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // Two waves per SIMD: the register budget that holds the prefetched slab, the
 // query operand and the accumulators without spilling (measured faster than
 // three waves with spills).
-template <int DT, int D, int G>
+template <int DT, int D, int G, int SL>
 __global__ __launch_bounds__(kMicroThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
-  using L = MLayout<DT, D>;
+  using L = MLayout<DT, D, SL>;
   constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
   static_assert(G == 2 || G == 4 || G == 8, "group size");
   __shared__ int s_phys[kPageCap];
   __shared__ int s_lp[kPageCap];
   __shared__ int s_cnt[kMicroWaves];
-  __shared__ float s_p[kMicroWaves][kSlab * G];
+  __shared__ float s_p[kMicroWaves][SL * G];
   __shared__ FinishLds<G, D> s_fin;
 
   const int tid = threadIdx.x;
@@ -113,7 +117,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   // the wave index is the same in every lane; saying so keeps the slab loop,
   // its page lookups and its address arithmetic on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int col = lane & 15;  // score column: token within the slab
+  const int col = lane & 15;  // score column: token within a score group
   const int grp = lane >> 4;  // score row group: heads 4*grp .. 4*grp+3
   const int vrow = lane / L::LPT;
   const int quad = lane & 3;  // head within a 4x4 block of the value product
@@ -156,7 +160,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       // slabs per page: P is a power of two, so slab sl is slab (sl & (spp - 1))
       // of kept page (sl >> spp_log)
-      const int spp = P / kSlab;
+      const int spp = P / SL;
       const int spp_log = __builtin_ctz(spp);
       // rows are counted from this KV head's first row: a page-major pool
       // [NP, Hkv, P, D] holds Hkv * P rows per page, a head-major pool
@@ -193,21 +197,25 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           const int phys = __builtin_amdgcn_readfirstlane(s_phys[kp]);
           const int lp = __builtin_amdgcn_readfirstlane(s_lp[kp]);
           Pos q;
-          q.row = (size_t)phys * page_rows + sub * kSlab;
-          q.tb = lp * P + sub * kSlab;
-          q.whole = q.tb >= t0 && q.tb + kSlab <= t1;
+          q.row = (size_t)phys * page_rows + sub * SL;
+          q.tb = lp * P + sub * SL;
+          q.whole = q.tb >= t0 && q.tb + SL <= t1;
           return q;
         };
 
-        auto load = [&](int sl, MFrag<DT, D>& f) {
+        auto load = [&](int sl, MFrag<DT, D, SL>& f) {
           const Pos q = pos(sl);
           const size_t off = q.row * L::TOKB;
           if (q.whole) {
   #pragma unroll
-            for (int j = 0; j < L::KL; ++j) f.k[j] = load_stream16(kbase + off + j * KSTRIDE);
-            if constexpr (DT == 2) {
-              f.ksc = ksb[q.row];
-              f.vsc = vsb[q.row];
+            for (int g = 0; g < L::NG; ++g) {
+  #pragma unroll
+              for (int j = 0; j < L::KL; ++j)
+                f.k[g][j] = load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE);
+              if constexpr (DT == 2) {
+                f.ksc[g] = ksb[q.row + 16 * g];
+                f.vsc[g] = vsb[q.row + 16 * g];
+              }
             }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
@@ -218,14 +226,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
               }
             }
           } else {  // rows outside the split read as zeros (and zero scales)
-            const int tk = q.tb + col;
-            const bool kok = tk >= t0 && tk < t1;
   #pragma unroll
-            for (int j = 0; j < L::KL; ++j)
-              f.k[j] = kok ? load_stream16(kbase + off + j * KSTRIDE) : make_uint4(0, 0, 0, 0);
-            if constexpr (DT == 2) {
-              f.ksc = kok ? ksb[q.row] : 0.f;
-              f.vsc = kok ? vsb[q.row] : 0.f;
+            for (int g = 0; g < L::NG; ++g) {
+              const int tk = q.tb + 16 * g + col;
+              const bool kok = tk >= t0 && tk < t1;
+  #pragma unroll
+              for (int j = 0; j < L::KL; ++j)
+                f.k[g][j] = kok ? load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE)
+                                : make_uint4(0, 0, 0, 0);
+              if constexpr (DT == 2) {
+                f.ksc[g] = kok ? ksb[q.row + 16 * g] : 0.f;
+                f.vsc[g] = kok ? vsb[q.row + 16 * g] : 0.f;
+              }
             }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
@@ -243,34 +255,48 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         // One slab.  A slab cut by the split bounds differs only in its
         // scores: rows outside the split score -inf (probability 0), and their
         // keys and values were loaded as zeros.
-        auto compute = [&](int sl, const MFrag<DT, D>& f) {
+        auto compute = [&](int sl, const MFrag<DT, D, SL>& f) {
           const Pos q = pos(sl);
 
-          // scores of the slab: sc[i] = q_{4*grp+i} . k_{tb+col}
-          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+          // scores of each group: sc[g][i] = q_{4*grp+i} . k_{tb+16g+col}
+          f32x4_t sc[L::NG];
   #pragma unroll
-          for (int st = 0; st < L::KS; ++st) {
-            uint4 kb;
-            if constexpr (DT == 1) {
-              kb = f.k[st];
-            } else {
-              const uint4& w = f.k[st / 2];
-              kb = (st & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+          for (int g = 0; g < L::NG; ++g) {
+            sc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int st = 0; st < L::KS; ++st) {
+              uint4 kb;
+              if constexpr (DT == 1) {
+                kb = f.k[g][st];
+              } else {
+                const uint4& w = f.k[g][st / 2];
+                kb = (st & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+              }
+              sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                             __builtin_bit_cast(bf16x8_t, kb), sc[g],
+                                                             0, 0, 0);
             }
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
-                                                        __builtin_bit_cast(bf16x8_t, kb), sc, 0, 0, 0);
+            if constexpr (DT == 2) sc[g] *= f.ksc[g];
           }
-          if constexpr (DT == 2) sc *= f.ksc;
           if (!q.whole) {  // wave-uniform branch
-            const bool kvalid = q.tb + col >= t0 && q.tb + col < t1;
   #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = kvalid ? sc[i] : neg_inf();
+            for (int g = 0; g < L::NG; ++g) {
+              const int tk = q.tb + 16 * g + col;
+              const bool kvalid = tk >= t0 && tk < t1;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) sc[g][i] = kvalid ? sc[g][i] : neg_inf();
+            }
           }
 
           // slab maxima per head, then the running maxima (wave-uniform)
           float rm[4];
   #pragma unroll
-          for (int i = 0; i < 4; ++i) rm[i] = row_max16(sc[i]);
+          for (int i = 0; i < 4; ++i) {
+            float x = sc[0][i];
+  #pragma unroll
+            for (int g = 1; g < L::NG; ++g) x = fmaxf(x, sc[g][i]);
+            rm[i] = row_max16(x);
+          }
           float alpha_h[G], nmc_h[G];
           bool moved = false;
   #pragma unroll
@@ -286,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 
           // probabilities in the score layout (0 for rows scored -inf);
           // exp-sums per token column
-          float pw[4];
+          float pw[L::NG][4];
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int hi = (i < G) ? i : 0;
@@ -297,8 +323,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                 al = alpha_h[4 + i];
               }
             }
-            pw[i] = fast_exp2(fmaf(sc[i], c, nmc));
-            e_l[i] = fmaf(e_l[i], al, pw[i]);
+            float sum = 0.f;
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+              pw[g][i] = fast_exp2(fmaf(sc[g][i], c, nmc));
+              sum += pw[g][i];
+            }
+            e_l[i] = fmaf(e_l[i], al, sum);
           }
 
           // probabilities to the value-product operand layout (per-wave LDS);
@@ -306,8 +337,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           float* sp = s_p[wave];
           if (grp < HS) {
   #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * grp + i < G) sp[col * G + 4 * grp + i] = DT == 2 ? pw[i] * f.vsc : pw[i];
+            for (int g = 0; g < L::NG; ++g)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (4 * grp + i < G)
+                  sp[(16 * g + col) * G + 4 * grp + i] = DT == 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
           }
 
           if (wave_any(moved)) {  // scalar branch: skipped, not masked
@@ -350,11 +384,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         };
 
         constexpr int W = kMicroWaves;
-        if constexpr (DT == 1 || G == 8) {
-          // bf16 (and fp8 with G = 8, whose accumulators leave no registers
-          // for a third fragment): one slab in flight while the other is
-          // computed
-          MFrag<DT, D> fa, fb;
+        if constexpr (DT == 1 || G == 8 || SL == 32) {
+          // 8 KiB slabs (16 bf16 rows or 32 fp8 rows), and 16-row fp8 slabs
+          // with G = 8 (whose accumulators leave no registers for a third
+          // fragment): one slab in flight while the other is computed
+          MFrag<DT, D, SL> fa, fb;
           int sl = wave;
           if (sl < nslab) load(sl, fa);
           while (sl < nslab) {
@@ -367,10 +401,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             sl += W;
           }
         } else {
-          // fp8: a slab carries half the bytes, so two are kept in flight; the
-          // three fragments take turns (no register copies, which would have
-          // to wait for the loads in flight)
-          MFrag<DT, D> f0, f1, f2;
+          // 16-row fp8 slabs (pages of 16 tokens) carry half the bytes, so two
+          // are kept in flight; the three fragments take turns (no register
+          // copies, which would have to wait for the loads in flight)
+          MFrag<DT, D, SL> f0, f1, f2;
           int sl = wave;
           if (sl < nslab) load(sl, f0);
           if (sl + W < nslab) load(sl + W, f1);
@@ -422,17 +456,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 // Resident workgroups per CU (measured best for the grouped-query workload).
 constexpr int kMfmaWorkgroupsPerCU = 2;
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int SL>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_kernel(micro_mfma_kernel<DT, D, G>, kMfmaWorkgroupsPerCU, p, stream);
+  return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL>, kMfmaWorkgroupsPerCU, p, stream);
 }
 
+// bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups
+// under one softmax update, 8 KiB of K + V like a bf16 slab) when the page
+// size allows and G <= 4; otherwise 16-token slabs.
 template <int DT, int D>
 hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
+  if constexpr (DT == 2) {
+    if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
+    if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
+  }
   switch (G) {
-    case 2: return launch_one<DT, D, 2>(p, stream);
-    case 4: return launch_one<DT, D, 4>(p, stream);
-    case 8: return launch_one<DT, D, 8>(p, stream);
+    case 2: return launch_one<DT, D, 2, 16>(p, stream);
+    case 4: return launch_one<DT, D, 4, 16>(p, stream);
+    case 8: return launch_one<DT, D, 8, 16>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
