@@ -84,7 +84,8 @@ typedef struct da_shape {
   int32_t Hkv;
   int32_t D;               /* 64 or 128                                        */
   int32_t P;               /* 16, 32, 64, 128 or 256                           */
-  int32_t max_pages;       /* row length of block_table and block_mask         */
+  int32_t max_pages;       /* row length of block_table and block_mask;       */
+                           /* (max_pages + 1) * P must fit in int32            */
   int32_t max_splits;      /* b: splits per (request[, KV head]), >= 1          */
   int32_t bounds_per_head; /* 0: split_bounds is [S, 1, b+1]; 1: [S, Hkv, b+1]  */
   int32_t dtype;           /* da_dtype of q, k_pages and v_pages               */

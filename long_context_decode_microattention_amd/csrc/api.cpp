@@ -49,9 +49,11 @@ da_status check_shape(const da_shape* sh, bool fp8 = false) {
                 sh->dtype == DA_FP8_E4M3 ? " for this entry point (8-bit pages: da_micro_attention_fp8)" : "");
   if (!(sh->scale > 0.f) || !isfinite(sh->scale))
     return fail(DA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
-  if ((long long)sh->S * sh->Hkv * sh->max_splits > INT_MAX)
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
+  // stepwise: each partial product is checked before it is multiplied again
+  if ((long long)sh->S * sh->Hkv > INT_MAX ||
+      (long long)sh->S * sh->Hkv * sh->max_splits > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv * max_splits exceeds the launch range");
   if (sh->NP > (long long)INT_MAX + 1)
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
@@ -117,8 +119,8 @@ da_status check_selector(const da_shape* sh, int logical) {
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
   if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
     return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
   if (sh->NP > (long long)INT_MAX + 1)
     return fail(DA_ERR_INVALID_ARG, "NP exceeds the int32 block-table range");
   if (!da::selector_supported(sh->dtype, sh->D, sh->Hq / sh->Hkv, sh->P, logical))
@@ -152,6 +154,18 @@ extern "C" {
 
 namespace {
 
+// D, P and group size among the MicroAttention kernels built.
+da_status check_micro_built(const da_shape* sh) {
+  if (sh->D != 64 && sh->D != 128)
+    return fail(DA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", sh->D);
+  if (sh->P != 16 && sh->P != 32 && sh->P != 64 && sh->P != 128 && sh->P != 256)
+    return fail(DA_ERR_UNSUPPORTED, "page size %d not built (16, 32, 64, 128, 256)", sh->P);
+  const int G = sh->Hq / sh->Hkv;
+  if (!da::micro_supported(sh->dtype, sh->D, G))
+    return fail(DA_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", G);
+  return DA_OK;
+}
+
 // Body of both MicroAttention entry points; ks / vs are the per-row scales
 // of 8-bit pages (null otherwise).
 da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_pages,
@@ -167,13 +181,8 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(split_bounds, 4) ||
       !aligned(m, 4) || !aligned(e, 4))
     return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
-  if (sh->D != 64 && sh->D != 128)
-    return fail(DA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", sh->D);
-  if (sh->P != 16 && sh->P != 32 && sh->P != 64 && sh->P != 128 && sh->P != 256)
-    return fail(DA_ERR_UNSUPPORTED, "page size %d not built (16, 32, 64, 128, 256)", sh->P);
-  const int G = sh->Hq / sh->Hkv;
-  if (!da::micro_supported(sh->dtype, sh->D, G))
-    return fail(DA_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", G);
+  const da_status built = check_micro_built(sh);
+  if (built != DA_OK) return built;
 
   int chunks = resolve_chunks(sh);
   WsLayout ws = ws_layout(sh, chunks);
@@ -225,7 +234,7 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.scale = sh->scale;
   p.NP = sh->NP;
   p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
-  hipError_t err = da::launch_micro(sh->dtype, sh->D, G, p, stream);
+  hipError_t err = da::launch_micro(sh->dtype, sh->D, sh->Hq / sh->Hkv, p, stream);
   if (err != hipSuccess)
     return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
   if (chunks > 1) {
@@ -275,6 +284,8 @@ da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
   if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
   da_status st = check_shape(sh, true);
+  if (st != DA_OK) return st;
+  st = check_micro_built(sh);
   if (st != DA_OK) return st;
   *bytes = ws_layout(sh, resolve_chunks(sh)).total;
   return DA_OK;
@@ -390,8 +401,8 @@ da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t
   if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d)", sh->S,
                 sh->Hkv, sh->P, sh->max_pages);
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (sh->max_pages > da::select_max_pages())
@@ -428,8 +439,8 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype", sh->dtype);
   if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
     return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (!da::append_supported(sh->dtype, sh->D))
@@ -476,8 +487,8 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
     return fail(DA_ERR_INVALID_ARG, "dtype of the new rows must be DA_F32 or DA_BF16 (got %d)", sh->dtype);
   if (sh->pool_layout != DA_POOL_PAGE_MAJOR && sh->pool_layout != DA_POOL_HEAD_MAJOR)
     return fail(DA_ERR_INVALID_ARG, "pool_layout %d is not a da_pool_layout", sh->pool_layout);
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (!da::quantize_supported(sh->dtype, sh->D))
@@ -521,8 +532,8 @@ da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const i
   if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1 || sh->max_splits < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d max_splits=%d)",
                 sh->S, sh->Hkv, sh->P, sh->max_pages, sh->max_splits);
-  if ((long long)sh->max_pages * sh->P > INT_MAX)
-    return fail(DA_ERR_INVALID_ARG, "max_pages * P exceeds the int32 token range");
+  if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
+    return fail(DA_ERR_INVALID_ARG, "max_pages * P + P exceeds the int32 token range");
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (horizon < 0) return fail(DA_ERR_INVALID_ARG, "horizon must be >= 0");

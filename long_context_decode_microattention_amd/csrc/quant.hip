@@ -48,9 +48,7 @@ bool quantize_supported(int dtype, int D) { return (dtype == 0 || dtype == 1) &&
 hipError_t launch_quantize_rows(int dtype, int D, const void* x, uint8_t* codes, float* scales,
                                 long long rows, hipStream_t stream) {
   if (rows < 1) return hipSuccess;
-  const int per = (kQuantThreads / kWave) * (kWave / (D / 8));
-  const long long grid = (rows + per - 1) / per;
-  const dim3 g((unsigned)grid), b(kQuantThreads);
+  const dim3 g((unsigned)quantize_launch_blocks(D, rows)), b(kQuantThreads);
   if (dtype == 0 && D == 64) hipLaunchKernelGGL((quantize_rows_kernel<0, 64>), g, b, 0, stream, x, codes, scales, rows);
   else if (dtype == 0 && D == 128) hipLaunchKernelGGL((quantize_rows_kernel<0, 128>), g, b, 0, stream, x, codes, scales, rows);
   else if (dtype == 1 && D == 64) hipLaunchKernelGGL((quantize_rows_kernel<1, 64>), g, b, 0, stream, x, codes, scales, rows);
@@ -61,7 +59,7 @@ hipError_t launch_quantize_rows(int dtype, int D, const void* x, uint8_t* codes,
 
 long long quantize_launch_blocks(int D, long long rows) {
   const int per = (kQuantThreads / kWave) * (kWave / (D / 8));
-  return (rows + per - 1) / per;
+  return rows / per + (rows % per != 0 ? 1 : 0);  // no overflow near the int64 limit
 }
 
 }  // namespace da
