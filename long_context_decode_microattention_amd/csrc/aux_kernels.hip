@@ -38,32 +38,38 @@ constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 8;     // 8 KiB per wave in flight
 constexpr int kReadMaxGrid = 4096;
 
-// One workgroup per CU streams a contiguous chunk: each wave reads rows of
-// kReadUnroll KiB (lane-contiguous 16-byte non-temporal loads), the four
-// waves interleaving rows.  This shape measured the highest read rate.
+// One workgroup per CU; every wave of the grid sweeps the buffer together:
+// wave w reads the 1 KiB blocks w, w + W, w + 2W, ... (W waves in the grid,
+// lane-contiguous 16-byte non-temporal loads), kReadUnroll of them in
+// flight, so the reads in flight at any moment form one front across the
+// buffer.  This walk measured faster than giving each workgroup its own
+// contiguous chunk (7.32-7.36 vs 7.22 TB/s over 16 GiB), and waiting for the
+// wave's eight loads together faster than consuming them one by one.
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4* __restrict__ src,
-                                                                   size_t n16, size_t chunk16,
-                                                                   uint32_t* sink) {
+                                                                   size_t n16, uint32_t* sink) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const size_t begin = (size_t)blockIdx.x * chunk16;
-  const size_t end = begin + chunk16 < n16 ? begin + chunk16 : n16;
-  constexpr size_t kRow = (size_t)kReadUnroll * kWave;
+  const long long W = (long long)gridDim.x * (kReadThreads / kWave);
+  const long long w = (long long)blockIdx.x * (kReadThreads / kWave) +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar loop
+  const long long nblk = (long long)(n16 / kWave);  // whole 1 KiB blocks
   uint32_t x = 0;
-  for (size_t r = begin + (size_t)wave * kRow; r < end; r += 4 * kRow) {
+  for (long long b = w; b < nblk; b += kReadUnroll * W) {
     uint4 a[kReadUnroll];
-    if (r + kRow <= end) {
 #pragma unroll
-      for (int u = 0; u < kReadUnroll; ++u) a[u] = load_stream16(src + r + u * kWave + lane);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kReadUnroll; ++u) {
-        const size_t i = r + u * kWave + lane;
-        a[u] = i < end ? load_stream16(src + i) : make_uint4(0, 0, 0, 0);
-      }
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const long long bb = b + u * W;
+      a[u] = bb < nblk ? load_stream16(src + bb * kWave + lane) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) x ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+  }
+  // the partial last block (fewer than 64 16-byte units), by the grid's last wave
+  if (w == W - 1) {
+    const size_t i = (size_t)nblk * kWave + lane;
+    if (i < n16) {
+      const uint4 t = load_stream16(src + i);
+      x ^= t.x ^ t.y ^ t.z ^ t.w;
+    }
   }
   // data-dependent store: the loads cannot be dropped, the store almost never happens
   if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
@@ -88,13 +94,10 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hip
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
   const size_t n16 = bytes / 16;
-  size_t grid = cus < 1 ? 1 : (size_t)cus;
-  if (grid > (size_t)kReadMaxGrid) grid = kReadMaxGrid;
-  size_t chunk16 = (n16 + grid - 1) / grid;
-  chunk16 = (chunk16 + kWave - 1) / kWave * kWave;
-  grid = (n16 + chunk16 - 1) / chunk16;
+  int grid = cus < 1 ? 1 : cus;
+  if (grid > kReadMaxGrid) grid = kReadMaxGrid;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, stream,
-                     static_cast<const uint4*>(src), n16, chunk16, sink);
+                     static_cast<const uint4*>(src), n16, sink);
   return hipGetLastError();
 }
 
