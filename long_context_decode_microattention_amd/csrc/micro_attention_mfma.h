@@ -1,0 +1,490 @@
+// MicroAttention on the matrix cores, for bf16 K/V with G = 2, 4 or 8 query
+// heads per KV head (grouped-query attention).  Same per-item result as the
+// vector kernel -- m_j, e_j and MA_j of the MicroAttention equations
+// (Infinite-LLM page, section 方法细节) for every query head of the group --
+// with the page list, slabs and block-mask skipping of that kernel.
+//
+// With G query heads per KV head the scores and the value sums are small
+// dense contractions, and on the vector ALUs they cost about 3 instructions
+// per KV byte, too close to the issue budget to keep HBM saturated.  Per
+// 16-token slab a wave instead runs:
+//
+//   scores   S[h][t] = q_h . k_t on v_mfma_f32_16x16x32_bf16: A = the query
+//            heads (16 rows, G used), B = the slab's keys (16 columns), K =
+//            D in 32-wide steps.  The B operand wants lane l to hold 8
+//            consecutive dims of token l%16, so each key load reads 64
+//            contiguous bytes of 16 token rows (the dims are visited in the
+//            order chunk = 4*step + l/16; q uses the same order).  Lane l,
+//            register i receives S[4*(l/16) + i][l % 16].
+//   softmax  per-head slab maxima by DPP reductions over the 16 lanes of a
+//            row, read out as wave-uniform values; the running maximum is
+//            per wave, so the value accumulators are rescaled only when a
+//            head's maximum rises (wave-uniform branch).
+//   values   on v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4x4, K = 1): block
+//            b = l/4 takes A = p of heads 0..3 from lanes 4b..4b+3 and B = one
+//            value element from each of its 4 lanes, so the values are used
+//            in the coalesced layout of the vector kernel (lane l holds 8
+//            dims of token row l/LPT) and every lane ends up with its own 8
+//            dims x 4 heads, all four block rows useful for G >= 4.  The
+//            probabilities move from the score layout to that operand
+//            layout through a 16 x G float scratch in LDS per wave.
+//
+// fp8 (E4M3) pages with per-row scales take the same path: a lane's key codes
+// (8 dims per score step, the steps of a lane now contiguous: dims
+// grp*D/4 + 8*step, q in the same order) are widened exactly to bf16 for the
+// score MFMA and the score column is multiplied by its token's K scale; the
+// value codes (8 per lane, 8-byte loads in the same row layout) are widened
+// exactly to fp32.  A token's V scale multiplies its probabilities in the
+// score layout (where the lane of token `col` loads it next to the K scale),
+// so the value operand arrives in LDS already scaled; the exp-sums take the
+// unscaled probabilities.
+#pragma once
+
+#include "micro_common.h"
+
+namespace da {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// DT: 1 = bf16 pages, 2 = fp8 E4M3 pages with per-row scales.  Either way a
+// value lane holds 8 dims of one token row (LPT lanes per row).  A slab is SL
+// = 16 or 32 tokens: NG score groups of 16 tokens (token 16*g + col of group
+// g in score column col).
+template <int DT, int D, int SL>
+struct MLayout {
+  static constexpr int TOKB = DT == 1 ? D * 2 : D;  // token row bytes
+  static constexpr int LPT = D / 8;                // value lanes per token row
+  static constexpr int TPI = kWave / LPT;          // token rows per value load
+  static constexpr int NI = SL / TPI;              // value loads per slab
+  static constexpr int NG = SL / 16;               // score groups per slab
+  static constexpr int KS = D / 32;                // score k-steps
+  static constexpr int KL = DT == 1 ? KS : KS / 2; // 16-byte key loads per lane
+  static constexpr int VB = 8 * (TOKB / D);        // value bytes per lane per load
+  static constexpr int EPL = 8;                    // elements per lane
+};
+
+template <int DT, int D, int SL>
+struct MFrag {
+  using L = MLayout<DT, D, SL>;
+  uint4 k[L::NG][L::KL];
+  uint4 v[DT == 1 ? L::NI : 1];   // bf16 values
+  uint2 v8[DT == 2 ? L::NI : 1];  // fp8 values
+  float ksc[L::NG];               // fp8: K scale of token 16*g + col
+  float vsc[L::NG];               // fp8: V scale of token 16*g + col
+};
+
+// Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                    fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+}
+
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t.x, t.y);
+}
+
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
+// Two waves per SIMD: the register budget that holds the prefetched slab, the
+// query operand and the accumulators without spilling (measured faster than
+// three waves with spills).
+template <int DT, int D, int G, int SL>
+__global__ __launch_bounds__(kMicroThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
+  using L = MLayout<DT, D, SL>;
+  constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
+  static_assert(G == 2 || G == 4 || G == 8, "group size");
+  __shared__ int s_phys[kPageCap];
+  __shared__ int s_lp[kPageCap];
+  __shared__ int s_cnt[kMicroWaves];
+  __shared__ float s_p[kMicroWaves][SL * G];
+  __shared__ FinishLds<G, D> s_fin;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  // the wave index is the same in every lane; saying so keeps the slab loop,
+  // its page lookups and its address arithmetic on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane & 15;  // score column: token within a score group
+  const int grp = lane >> 4;  // score row group: heads 4*grp .. 4*grp+3
+  const int vrow = lane / L::LPT;
+  const int quad = lane & 3;  // head within a 4x4 block of the value product
+
+  __shared__ int s_claim;
+  for_each_item(p, &s_claim, [&](int x) {
+    const Item it = plan_item(p, x);
+    const int s = it.s, kvh = it.kvh, h0 = kvh * G;
+    const int t0 = it.t0, t1 = it.t1;
+    const int P = p.P;
+    const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
+
+    // score operand A: lane l -> head l%16 (zero beyond G), 8 bf16 dims per
+    // step: chunk 4*step + l/16 (bf16 pages) or chunk KS*(l/16) + step (fp8)
+    uint4 qa[L::KS];
+  #pragma unroll
+    for (int st = 0; st < L::KS; ++st) {
+      qa[st] = make_uint4(0, 0, 0, 0);
+      if (col < G) {
+        const int chunk8 = DT == 1 ? 4 * st + grp : L::KS * grp + st;
+        const char* qp = static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + col) * D * 2 +
+                         (size_t)chunk8 * 16;
+        qa[st] = *reinterpret_cast<const uint4*>(qp);
+      }
+    }
+
+    float m_h[G];        // running raw-dot maximum per head (wave-uniform)
+    float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
+    f32x4_t acc[HS][8];  // value sums: block layout, register i = head 4*hs + i
+  #pragma unroll
+    for (int h = 0; h < G; ++h) m_h[h] = neg_inf();
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) e_l[i] = 0.f;
+  #pragma unroll
+    for (int hs = 0; hs < HS; ++hs)
+  #pragma unroll
+      for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (it.scan0 < it.scan1) {
+      const int32_t* trow = p.table + (size_t)s * p.max_pages;
+      // slabs per page: P is a power of two, so slab sl is slab (sl & (spp - 1))
+      // of kept page (sl >> spp_log)
+      const int spp = P / SL;
+      const int spp_log = __builtin_ctz(spp);
+      // rows are counted from this KV head's first row: a page-major pool
+      // [NP, Hkv, P, D] holds Hkv * P rows per page, a head-major pool
+      // [Hkv, NP, P, D] holds P; the fp8 row scales share the row numbering
+      const int page_rows = p.head_major ? P : p.Hkv * P;
+      const size_t head_row = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
+      // key lane: token col; bf16: 16 bytes per step at 64*step + 16*grp;
+      // fp8: 8*KS contiguous bytes at 8*KS*grp
+      const char* kbase = static_cast<const char*>(p.k) + head_row * L::TOKB +
+                          (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
+      const char* vbase = static_cast<const char*>(p.v) + head_row * L::TOKB + lane * L::VB;
+      // fp8: the K and V scales of the key lane's token (no scales for bf16)
+      const float* ksb = DT == 2 ? p.ks + head_row + col : nullptr;
+      const float* vsb = DT == 2 ? p.vs + head_row + col : nullptr;
+
+      for (int base = it.scan0; base < it.scan1; base += kPageCap) {
+        const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
+        const int nslab = nk * spp;
+
+        // key load j of a lane: bf16 64*j (one score step), fp8 16*j (two steps)
+        constexpr int KSTRIDE = DT == 1 ? 64 : 16;
+        constexpr int VSTRIDE = L::TPI * L::TOKB;  // bytes per value load
+
+        // where slab sl lives; the page ids are read from LDS as wave-uniform
+        // values so that the offsets are computed on the scalar unit
+        struct Pos {
+          size_t row;  // the slab's first row (pool bytes: row * TOKB)
+          int tb;      // logical token of the slab's first row
+          bool whole;  // every row of the slab lies inside the split
+        };
+        auto pos = [&](int sl) {
+          const int kp = sl >> spp_log;
+          const int sub = sl & (spp - 1);
+          const int phys = __builtin_amdgcn_readfirstlane(s_phys[kp]);
+          const int lp = __builtin_amdgcn_readfirstlane(s_lp[kp]);
+          Pos q;
+          q.row = (size_t)phys * page_rows + sub * SL;
+          q.tb = lp * P + sub * SL;
+          q.whole = q.tb >= t0 && q.tb + SL <= t1;
+          return q;
+        };
+
+        auto load = [&](int sl, MFrag<DT, D, SL>& f) {
+          const Pos q = pos(sl);
+          const size_t off = q.row * L::TOKB;
+          if (q.whole) {
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+  #pragma unroll
+              for (int j = 0; j < L::KL; ++j)
+                f.k[g][j] = load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE);
+              if constexpr (DT == 2) {
+                f.ksc[g] = ksb[q.row + 16 * g];
+                f.vsc[g] = vsb[q.row + 16 * g];
+              }
+            }
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
+              if constexpr (DT == 1) {
+                f.v[i] = load_stream16(vbase + off + i * VSTRIDE);
+              } else {
+                f.v8[i] = load_stream8(vbase + off + i * VSTRIDE);
+              }
+            }
+          } else {  // rows outside the split read as zeros (and zero scales)
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+              const int tk = q.tb + 16 * g + col;
+              const bool kok = tk >= t0 && tk < t1;
+  #pragma unroll
+              for (int j = 0; j < L::KL; ++j)
+                f.k[g][j] = kok ? load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE)
+                                : make_uint4(0, 0, 0, 0);
+              if constexpr (DT == 2) {
+                f.ksc[g] = kok ? ksb[q.row + 16 * g] : 0.f;
+                f.vsc[g] = kok ? vsb[q.row + 16 * g] : 0.f;
+              }
+            }
+  #pragma unroll
+            for (int i = 0; i < L::NI; ++i) {
+              const int tv = q.tb + i * L::TPI + vrow;
+              const bool vok = tv >= t0 && tv < t1;
+              if constexpr (DT == 1) {
+                f.v[i] = vok ? load_stream16(vbase + off + i * VSTRIDE) : make_uint4(0, 0, 0, 0);
+              } else {
+                f.v8[i] = vok ? load_stream8(vbase + off + i * VSTRIDE) : make_uint2(0, 0);
+              }
+            }
+          }
+        };
+
+        // One slab.  A slab cut by the split bounds differs only in its
+        // scores: rows outside the split score -inf (probability 0), and their
+        // keys and values were loaded as zeros.
+        auto compute = [&](int sl, const MFrag<DT, D, SL>& f) {
+          const Pos q = pos(sl);
+
+          // scores of each group: sc[g][i] = q_{4*grp+i} . k_{tb+16g+col}
+          f32x4_t sc[L::NG];
+  #pragma unroll
+          for (int g = 0; g < L::NG; ++g) {
+            sc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int st = 0; st < L::KS; ++st) {
+              uint4 kb;
+              if constexpr (DT == 1) {
+                kb = f.k[g][st];
+              } else {
+                const uint4& w = f.k[g][st / 2];
+                kb = (st & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+              }
+              sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                             __builtin_bit_cast(bf16x8_t, kb), sc[g],
+                                                             0, 0, 0);
+            }
+            if constexpr (DT == 2) sc[g] *= f.ksc[g];
+          }
+          if (!q.whole) {  // wave-uniform branch
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+              const int tk = q.tb + 16 * g + col;
+              const bool kvalid = tk >= t0 && tk < t1;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) sc[g][i] = kvalid ? sc[g][i] : neg_inf();
+            }
+          }
+
+          // slab maxima per head, then the running maxima (wave-uniform)
+          float rm[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sc[0][i];
+  #pragma unroll
+            for (int g = 1; g < L::NG; ++g) x = fmaxf(x, sc[g][i]);
+            rm[i] = row_max16(x);
+          }
+          float alpha_h[G], nmc_h[G];
+          bool moved = false;
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
+            const float mn = fmaxf(m_h[h], mx);
+            const float ms = mn != neg_inf() ? mn : 0.f;
+            alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
+            nmc_h[h] = -ms * c;
+            moved |= mn != m_h[h];
+            m_h[h] = mn;
+          }
+
+          // probabilities in the score layout (0 for rows scored -inf);
+          // exp-sums per token column
+          float pw[L::NG][4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int hi = (i < G) ? i : 0;
+            float nmc = nmc_h[hi], al = alpha_h[hi];
+            if constexpr (G > 4) {
+              if (grp == 1) {
+                nmc = nmc_h[4 + i];
+                al = alpha_h[4 + i];
+              }
+            }
+            float sum = 0.f;
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+              pw[g][i] = fast_exp2(fmaf(sc[g][i], c, nmc));
+              sum += pw[g][i];
+            }
+            e_l[i] = fmaf(e_l[i], al, sum);
+          }
+
+          // probabilities to the value-product operand layout (per-wave LDS);
+          // over 8-bit pages each carries its token's V scale
+          float* sp = s_p[wave];
+          if (grp < HS) {
+  #pragma unroll
+            for (int g = 0; g < L::NG; ++g)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (4 * grp + i < G)
+                  sp[(16 * g + col) * G + 4 * grp + i] = DT == 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
+          }
+
+          if (wave_any(moved)) {  // scalar branch: skipped, not masked
+  #pragma unroll
+            for (int hs = 0; hs < HS; ++hs)
+  #pragma unroll
+              for (int k = 0; k < 8; ++k)
+  #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
+          }
+
+          // value sums: acc[hs][k] += p[4hs + i][token] * v[token][dim k of this lane]
+  #pragma unroll
+          for (int j = 0; j < L::NI; ++j) {
+            float pa[HS];
+  #pragma unroll
+            for (int hs = 0; hs < HS; ++hs) {
+              pa[hs] = (4 * hs + quad < G) ? sp[(j * L::TPI + vrow) * G + 4 * hs + quad] : 0.f;
+            }
+            float vf[8];
+            if constexpr (DT == 1) {
+              const uint32_t w4[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
+  #pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                vf[2 * k] = bf16_lo(w4[k]);
+                vf[2 * k + 1] = bf16_hi(w4[k]);
+              }
+            } else {
+              fp8x4_to_f32(f.v8[j].x, vf);
+              fp8x4_to_f32(f.v8[j].y, vf + 4);
+            }
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+  #pragma unroll
+              for (int hs = 0; hs < HS; ++hs)
+                acc[hs][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], vf[k], acc[hs][k], 0, 0, 0);
+            }
+          }
+        };
+
+        constexpr int W = kMicroWaves;
+        if constexpr (DT == 1 || G == 8 || SL == 32) {
+          // 8 KiB slabs (16 bf16 rows or 32 fp8 rows), and 16-row fp8 slabs
+          // with G = 8 (whose accumulators leave no registers for a third
+          // fragment): one slab in flight while the other is computed
+          MFrag<DT, D, SL> fa, fb;
+          int sl = wave;
+          if (sl < nslab) load(sl, fa);
+          while (sl < nslab) {
+            if (sl + W < nslab) load(sl + W, fb);
+            compute(sl, fa);
+            sl += W;
+            if (sl >= nslab) break;
+            if (sl + W < nslab) load(sl + W, fa);
+            compute(sl, fb);
+            sl += W;
+          }
+        } else {
+          // 16-row fp8 slabs (pages of 16 tokens) carry half the bytes, so two
+          // are kept in flight; the three fragments take turns (no register
+          // copies, which would have to wait for the loads in flight)
+          MFrag<DT, D, SL> f0, f1, f2;
+          int sl = wave;
+          if (sl < nslab) load(sl, f0);
+          if (sl + W < nslab) load(sl + W, f1);
+          while (sl < nslab) {
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f2);
+            compute(sl, f0);
+            sl += W;
+            if (sl >= nslab) break;
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f0);
+            compute(sl, f1);
+            sl += W;
+            if (sl >= nslab) break;
+            if (sl + 2 * W < nslab) load(sl + 2 * W, f1);
+            compute(sl, f2);
+            sl += W;
+          }
+        }
+        __syncthreads();  // the page list is rewritten by the next batch
+      }
+    }
+
+    // ---- per-wave totals: exp-sums over token columns, values over token rows ----
+    float we[G];
+  #pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x = e_l[h & 3];
+      x = x + dpp<kDppQuadXor1>(x);
+      x = x + dpp<kDppQuadXor2>(x);
+      x = x + dpp<kDppHalfMirror>(x);
+      x = x + dpp<kDppRowMirror>(x);
+      we[h] = lane_value(x, 16 * (h >> 2));
+    }
+    float accg[G][8];
+  #pragma unroll
+    for (int h = 0; h < G; ++h)
+  #pragma unroll
+      for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
+  #pragma unroll
+    for (int off = L::LPT; off < kWave; off <<= 1)
+  #pragma unroll
+      for (int h = 0; h < G; ++h)
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) accg[h][k] += __shfl_xor(accg[h][k], off, kWave);
+
+    finish_item<G, D, L::LPT, 8>(p, it, s_fin, m_h, we, accg, c);
+  });
+}
+
+// Resident workgroups per CU (measured best for the grouped-query workload).
+constexpr int kMfmaWorkgroupsPerCU = 2;
+
+template <int DT, int D, int G, int SL>
+hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
+  return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL>, kMfmaWorkgroupsPerCU, p, stream);
+}
+
+// bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups
+// under one softmax update, 8 KiB of K + V like a bf16 slab) when the page
+// size allows and G <= 4; otherwise 16-token slabs.
+template <int DT, int D>
+hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
+  if constexpr (DT == 2) {
+    if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
+    if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
+  }
+  switch (G) {
+    case 2: return launch_one<DT, D, 2, 16>(p, stream);
+    case 4: return launch_one<DT, D, 4, 16>(p, stream);
+    case 8: return launch_one<DT, D, 8, 16>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// 8-bit pages: micro_mfma_kernel<2, ...> for G in {2, 4, 8}, compiled in a
+// translation unit of its own (micro_attention_mfma_fp8.hip, built with NaNs
+// ruled out and IEEE mode off so that its DPP max steps fold).
+hipError_t launch_micro_mfma_fp8(int D, int G, const MicroParams& p, hipStream_t stream);
+
+}  // namespace da
