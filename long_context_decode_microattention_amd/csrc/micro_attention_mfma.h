@@ -1,5 +1,5 @@
-// MicroAttention on the matrix cores, for bf16 K/V with G = 2, 4 or 8 query
-// heads per KV head (grouped-query attention).  Same per-item result as the
+// MicroAttention on the matrix cores, for bf16 or FP8 K/V with G = 2, 4 or 8
+// query heads per KV head (grouped-query attention).  Same per-item result as the
 // vector kernel -- m_j, e_j and MA_j of the MicroAttention equations
 // (Infinite-LLM page, section 方法细节) for every query head of the group --
 // with the page list, slabs and block-mask skipping of that kernel.
@@ -27,7 +27,7 @@
 //            dims of token row l/LPT) and every lane ends up with its own 8
 //            dims x 4 heads, all four block rows useful for G >= 4.  The
 //            probabilities move from the score layout to that operand
-//            layout through a 16 x G float scratch in LDS per wave.
+//            layout through an SL x G float scratch in LDS per wave.
 //
 // fp8 (E4M3) pages with per-row scales take the same path: a lane's key codes
 // (8 dims per score step, the steps of a lane now contiguous: dims
@@ -37,7 +37,13 @@
 // exactly to fp32.  A token's V scale multiplies its probabilities in the
 // score layout (where the lane of token `col` loads it next to the K scale),
 // so the value operand arrives in LDS already scaled; the exp-sums take the
-// unscaled probabilities.
+// unscaled probabilities.  With pages of 32 tokens or more (and G <= 4) an
+// 8-bit slab is 32 tokens, two score groups of 16 under one running-max
+// update and one LDS round trip: 8 KiB of K + V, like a bf16 slab.
+//
+// The kernel template lives in this header; micro_attention_mfma.hip launches
+// the bf16 instances and micro_attention_mfma_fp8.hip the 8-bit ones, which
+// are built with different floating-point flags.
 #pragma once
 
 #include "micro_common.h"
