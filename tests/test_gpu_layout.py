@@ -26,6 +26,10 @@ CASES = {
     "C4": wl.CONFIGS["C4"].replace(Hq=8, Hkv=8, lens=("fixed", 16384 + 21)),
     "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 16384 + 5)),
     "C5_G8_D64": wl.CONFIGS["C5"].replace(S=1, Hq=64, D=64, lens=("fixed", 8192 + 50)),
+    # 16-token pages under a shuffled table (one slab per page), and 32-token
+    # pages under the grouped-query kernel (one 32-row 8-bit slab per page)
+    "C2": wl.CONFIGS["C2"].replace(S=2),
+    "C5_P32": wl.CONFIGS["C5"].replace(S=2, P=32, lens=("fixed", 8192 + 13)),
 }
 
 
@@ -63,7 +67,7 @@ def test_attention_layouts_identical(cfg):
     compare_out(rh[0].cpu().numpy(), want, TOL_OUT[bh.spec.dtype], f"{cfg} head-major vs oracle")
 
 
-@pytest.mark.parametrize("cfg", ["C4", "C5", "C5_G8_D64"])
+@pytest.mark.parametrize("cfg", ["C2", "C4", "C5", "C5_G8_D64", "C5_P32"])
 def test_fp8_layouts_identical(cfg):
     announce("layout fp8", cfg)
     bp, bh = _pair(cfg)
