@@ -30,6 +30,9 @@ CASES = {
     # pages under the grouped-query kernel (one 32-row 8-bit slab per page)
     "C2": wl.CONFIGS["C2"].replace(S=2),
     "C5_P32": wl.CONFIGS["C5"].replace(S=2, P=32, lens=("fixed", 8192 + 13)),
+    # the largest page size built, mid-slab splits
+    "C4_P256": wl.CONFIGS["C4"].replace(Hq=4, Hkv=4, P=256, lens=("fixed", 256 * 20 + 77),
+                                        splits=("equal", 5)),
 }
 
 
