@@ -410,6 +410,9 @@ for dtype in (wl.F32, wl.BF16):
         for P in (16, 64):
             for G in (1, 4, 8):
                 EDGE.append((dtype, D, P, G))
+# the other page sizes built (32, 128, 256 tokens: 2 to 16 slabs per page)
+EDGE += [(wl.BF16, 128, 32, 4), (wl.BF16, 64, 128, 2), (wl.BF16, 128, 256, 4),
+         (wl.BF16, 128, 256, 1), (wl.F32, 64, 256, 8)]
 
 
 @pytest.mark.parametrize("dtype,D,P,G", EDGE)
