@@ -13,7 +13,9 @@
 //                       stored values, so bf16 statistics are exact).  A lane
 //                       owns 16 bytes of one (KV head, logical page) column
 //                       and folds every row of it, 16 rows in flight, so no
-//                       cross-lane reduction is needed.  The statistics are
+//                       cross-lane reduction is needed; the statistics go out
+//                       with non-temporal stores (plain stores, mixed into
+//                       the read stream, cost 10% more time).  They are
 //                       head-major: one KV head's pages form one contiguous
 //                       run, which is what the score kernel streams (measured
 //                       6.5 TB/s against 5.5 TB/s for page-major blocks of
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(kSelThreads) void page_stats_kernel(SelectorParams 
         for (int i = 0; i < R::EPL; ++i) hi[i] = lo[i] = 0.f;
       }
       char* dst = spage + (size_t)kvh * head_stride + (size_t)sub * 2 * R::RB;
-      *reinterpret_cast<uint4*>(dst) = pack<DT>(hi);
-      *reinterpret_cast<uint4*>(dst + R::RB) = pack<DT>(lo);
+      store_stream16(dst, pack<DT>(hi));
+      store_stream16(dst + R::RB, pack<DT>(lo));
     }
   }
 }
