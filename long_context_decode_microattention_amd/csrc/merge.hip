@@ -128,26 +128,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 
 // Folds the page-range chunks of each split back into the split's triple
 // (the same aggregation rule, keeping the triple form): one wave per
-// (request, head, split).
+// (request, head, split).  Lane c holds chunk c's (m, e) (at most 64
+// chunks), so the maximum and the sum are wave reductions; the chunk weights
+// go through LDS, and each lane has the loads of its dimension for
+// kCombineBatch chunks in flight before it accumulates them.
+constexpr int kCombineBatch = 16;
+
 __global__ __launch_bounds__(kWave) void combine_kernel(const float* __restrict__ cMA,
                                                         const float* __restrict__ cm,
                                                         const float* __restrict__ ce,
                                                         float* __restrict__ MA,
                                                         float* __restrict__ m,
                                                         float* __restrict__ e, int chunks, int D) {
+  __shared__ float s_w[kWave];
   const size_t o = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* mr = cm + o * chunks;
-  const float* er = ce + o * chunks;
   const float* MAr = cMA + o * (size_t)chunks * D;
-  float M = neg_inf();
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, mr[c]);
+  const bool own = lane < chunks;
+  const float mc = own ? cm[o * chunks + lane] : neg_inf();
+  const float ec = own ? ce[o * chunks + lane] : 0.f;
+  const float M = wave_max(mc);
   const float Ms = (M == neg_inf()) ? 0.f : M;
-  float eg = 0.f;
-  for (int c = 0; c < chunks; ++c) eg = fmaf(er[c], expf(mr[c] - Ms), eg);
+  const float w = own ? expf(mc - Ms) : 0.f;  // 0 for an empty chunk (mc = -inf)
+  const float eg = wave_sum(ec * w);
+  s_w[lane] = w;
+  __syncthreads();
   for (int d = lane; d < D; d += kWave) {
     float acc = 0.f;
-    for (int c = 0; c < chunks; ++c) acc = fmaf(MAr[(size_t)c * D + d], expf(mr[c] - Ms), acc);
+    int c = 0;
+    for (; c + kCombineBatch <= chunks; c += kCombineBatch) {
+      float x[kCombineBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) x[u] = MAr[(size_t)(c + u) * D + d];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) acc = fmaf(x[u], s_w[c + u], acc);
+    }
+    for (; c < chunks; ++c) acc = fmaf(MAr[(size_t)c * D + d], s_w[c], acc);
     MA[o * D + d] = acc;
   }
   if (lane == 0) {
@@ -169,6 +185,7 @@ hipError_t launch_queue_reset(int* queue, hipStream_t stream) {
 
 hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
                           float* e, long long n, int chunks, int D, hipStream_t stream) {
+  if (chunks < 1 || chunks > kWave) return hipErrorInvalidValue;  // one lane per chunk
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n), dim3(kWave), 0, stream, cMA, cm, ce, MA, m,
                      e, chunks, D);
   return hipGetLastError();
