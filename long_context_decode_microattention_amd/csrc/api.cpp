@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kMaxChunks = 64;
 constexpr int kAutoMaxChunks = 16;
+constexpr long long kBalanceItemBytes = 4LL << 20;  // splits this large are cut for balance
 
 thread_local std::string g_last_error;
 
@@ -73,14 +74,44 @@ da_status check_shape(const da_shape* sh, bool fp8 = false) {
 // masked heads, ragged lengths); below that target, splits are cut into page
 // ranges, at most as many as a split of an evenly divided max-length request
 // has pages.
+// Compute units of the current device (256 on MI355X when the query fails).
+long long device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 256;
+  return cus;
+}
+
+// Chunks per split when the caller leaves the choice to the library.  A
+// chunked launch adds the combine kernel (5-9 us of a replayed step), so
+// splits are cut for two reasons only:
+//  - to fill the device: fewer work units than it runs at once leave compute
+//    units idle.  One workgroup of the vector kernel per CU already draws
+//    most of the bandwidth; the GQA kernel wants two (measured on single
+//    requests: 16 x 4K tokens over 256 splits runs best uncut, 8K tokens of
+//    GQA 32/8 over 32 splits best in 16 chunks);
+//  - to balance long items: splits of several MiB whose kept lengths differ
+//    (block-sparse heads beside dense ones) finish together when cut into
+//    more, shorter units (the chunk counts measured best on the 512K GQA
+//    batch).
 int resolve_chunks(const da_shape* sh) {
   if (sh->chunks > 0) return sh->chunks;
-  const long long target = da::micro_target_items(sh->dtype, sh->D, sh->Hq / sh->Hkv);
+  const int G = sh->Hq / sh->Hkv;
   const long long items = (long long)sh->S * sh->Hkv * sh->max_splits;
-  if (items >= target) return 1;
-  long long c = (target + items - 1) / items;
-  if (c > kAutoMaxChunks) c = kAutoMaxChunks;
   const long long pages_per_split = sh->max_pages / sh->max_splits;  // typical split size
+  const long long row = sh->dtype == DA_F32 ? 4LL * sh->D : sh->dtype == DA_BF16 ? 2LL * sh->D
+                                                                                 : sh->D + 4LL;
+  const long long item_bytes = pages_per_split * sh->P * 2 * row;  // K and V of a typical split
+  const long long fill = device_cus() * (da::micro_mfma_supported(sh->dtype, sh->D, G) ? 2 : 1);
+  long long c = (fill + items - 1) / items;
+  if (item_bytes >= kBalanceItemBytes) {
+    const long long target = da::micro_target_items(sh->dtype, sh->D, G);
+    const long long cb = (target + items - 1) / items;
+    if (cb > c) c = cb;
+  }
+  if (c > kAutoMaxChunks) c = kAutoMaxChunks;
   if (c > pages_per_split) c = pages_per_split;
   return c < 1 ? 1 : (int)c;
 }

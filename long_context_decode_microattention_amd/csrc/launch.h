@@ -44,6 +44,7 @@ bool micro_supported(int dtype, int D, int G);
 // target): the matrix-core kernel holds fewer workgroups per CU and gains
 // from finer pieces.
 long long micro_target_items(int dtype, int D, int G);
+bool micro_mfma_supported(int dtype, int D, int G);  // the GQA matrix-core kernel runs it
 
 // Folds `chunks` partials per (request, head, split) into one:
 // cMA [n, chunks, D], cm/ce [n, chunks] -> MA [n, D], m/e [n], n = S*Hq*max_splits.
