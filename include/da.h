@@ -226,6 +226,53 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
                    float* out, hipStream_t stream);
 
 /*
+ * One decode step in a single launch: the MicroAttention partials of every
+ * split and their aggregation into the attention output (Infinite-LLM page,
+ * section 方法细节: local MicroAttention per sub-block, then the aggregation
+ * equations), i.e. da_micro_attention followed by da_merge, with the merge
+ * done by the work item that completes the last partial of each (request,
+ * KV head) instead of by a second kernel.
+ *
+ *   Inputs as for da_micro_attention (da_attention_fp8: as for
+ *   da_micro_attention_fp8).
+ *   out        [S, Hq, D] float32, caller-owned, fully written: the merge of
+ *              the b splits (all-empty -> 0), within fp32 rounding of
+ *              da_micro_attention + da_merge on the same inputs.
+ *   workspace  device, caller-owned, 16-byte aligned, at least
+ *              da_attention_workspace_size() bytes.  Its first counter_bytes
+ *              (as returned there) hold one counter per (request, KV head)
+ *              and MUST BE ZERO before the first call (zero-fill the buffer
+ *              once when it is allocated); every call that completes leaves
+ *              them zero, so later calls need no clearing.  Clear them again
+ *              after using the buffer for anything else, or before a call
+ *              whose S * Hkv exceeds every earlier one (the new counters
+ *              then cover bytes that held partials).  The rest holds the
+ *              partials and a work-queue counter.  Concurrent calls must not
+ *              share a workspace.  A workspace too small is
+ *              DA_ERR_INVALID_ARG (with sh->chunks == 0 the call first falls
+ *              back to unchunked splits if those fit).
+ * Every call only enqueues kernels on `stream` (no allocation, no host
+ * synchronisation, no memset node), so a step can be captured in a HIP
+ * graph and replayed.
+ * Errors: as da_micro_attention.
+ */
+da_status da_attention(const da_shape* sh, const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+da_status da_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                           const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of da_attention / da_attention_fp8 for this shape, and
+ * (counter_bytes, nullable) how many of its first bytes are the counters
+ * that must start at zero.  Host-only. */
+da_status da_attention_workspace_size(const da_shape* sh, size_t* bytes, size_t* counter_bytes);
+
+/*
  * Fold b partials per (request, query head) into ONE partial triple and write
  * it into slot `out_slot` of a gather buffer: the aggregation equations of
  * the Infinite-LLM page (section 方法细节) without the final division,

@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     DaError,
     DaShape,
     attention,
+    attention_fp8,
+    attention_workspace_size,
     check_inputs,
     load,
     merge,

@@ -94,6 +94,15 @@ def load() -> ctypes.CDLL:
     lib.da_micro_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.da_micro_attention_fp8.restype = ctypes.c_int
+    lib.da_attention.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                 _VP]
+    lib.da_attention.restype = ctypes.c_int
+    lib.da_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                     ctypes.c_size_t, _VP]
+    lib.da_attention_fp8.restype = ctypes.c_int
+    lib.da_attention_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    lib.da_attention_workspace_size.restype = ctypes.c_int
     lib.da_quantize_rows.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP,
                                      _VP]
     lib.da_quantize_rows.restype = ctypes.c_int
@@ -364,12 +373,121 @@ def merge_partials(MA, m, e, *, out=None, slot: int = 0, out_splits: int = 1):
     return out
 
 
+def attention_workspace_size(sh: DaShape):
+    """(bytes, counter_bytes) of the fused step's workspace for this shape."""
+    n, c = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().da_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n), ctypes.byref(c)))
+    return int(n.value), int(c.value)
+
+
+class _FusedWorkspace:
+    """A per-device workspace for the fused step.  Its first `clean` bytes are
+    known to be zero: every completed call leaves its own counters zero and
+    may overwrite what lies beyond them with partials, so a call whose
+    counters reach past `clean` gets that range zeroed first."""
+
+    def __init__(self):
+        self.buf = None
+        self.clean = 0
+
+    def get(self, device, nbytes: int, counter_bytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.clean = nbytes
+        elif self.clean < counter_bytes:
+            self.buf[self.clean:counter_bytes].zero_()
+        self.clean = counter_bytes
+        return self.buf
+
+
+_FUSED_WORKSPACE = {}
+
+
+def _fused_workspace(device: torch.device, sh: DaShape, workspace) -> torch.Tensor:
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of q")
+        return workspace
+    nbytes, counter_bytes = attention_workspace_size(sh)
+    key = (device.type, device.index)
+    return _FUSED_WORKSPACE.setdefault(key, _FusedWorkspace()).get(device, nbytes, counter_bytes)
+
+
 def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
-              *, scale: Optional[float] = None, chunks: int = 0, pool_layout: str = "page"):
-    """One decode step: micro_attention then merge."""
-    MA, m, e = micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds,
-                               block_mask, scale=scale, chunks=chunks, pool_layout=pool_layout)
-    return merge(MA, m, e)
+              *, scale: Optional[float] = None, out=None, chunks: int = 0, schedule: int = 0,
+              workspace: Optional[torch.Tensor] = None, pool_layout: str = "page"):
+    """One decode step in one launch via da_attention: MicroAttention partials
+    and their merge into out [S, Hq, D] float32.  workspace: None uses a
+    cached per-device one; a caller's own must have been zero-filled once
+    (see da_attention) and must not be shared by concurrent calls."""
+    dev = q.device
+    _need(q, "q", None, dev, 3)
+    _need(k_pages, "k_pages", q.dtype, dev, 4)
+    _need(v_pages, "v_pages", q.dtype, dev, 4)
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages differ in shape")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule, pool_layout)
+    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
+        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
+    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
+        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
+    if out is None:
+        out = torch.empty((sh.S, sh.Hq, sh.D), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, 3)
+        if tuple(out.shape) != (sh.S, sh.Hq, sh.D):
+            raise ValueError("out must be [S, Hq, D]")
+    ws = _fused_workspace(dev, sh, workspace)
+    _check(load().da_attention(
+        ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+        _ptr(split_bounds), _ptr(block_mask), _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, split_bounds,
+                  block_mask=None, *, scale: Optional[float] = None, out=None, chunks: int = 0,
+                  schedule: int = 0, workspace: Optional[torch.Tensor] = None,
+                  pool_layout: str = "page"):
+    """One decode step over 8-bit pages in one launch via da_attention_fp8
+    (inputs as micro_attention_fp8, output and workspace as attention)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(k_codes, "k_codes", torch.uint8, dev, 4)
+    _need(v_codes, "v_codes", torch.uint8, dev, 4)
+    if v_codes.shape != k_codes.shape:
+        raise ValueError("k_codes and v_codes differ in shape")
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.float32, dev, 3)
+        if tuple(t.shape) != tuple(k_codes.shape[:3]):
+            raise ValueError(f"{name} must match the first three dims of the code pools")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule, pool_layout)
+    sh.dtype = DA_FP8_E4M3
+    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
+        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
+    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
+        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
+    if out is None:
+        out = torch.empty((sh.S, sh.Hq, sh.D), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, 3)
+        if tuple(out.shape) != (sh.S, sh.Hq, sh.D):
+            raise ValueError("out must be [S, Hq, D]")
+    ws = _fused_workspace(dev, sh, workspace)
+    _check(load().da_attention_fp8(
+        ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(block_table), _ptr(seq_lens), _ptr(split_bounds), _ptr(block_mask), _ptr(out),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return out
 
 
 def _dtype_code(t: torch.Tensor) -> int:

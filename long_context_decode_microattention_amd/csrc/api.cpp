@@ -137,6 +137,22 @@ WsLayout ws_layout(const da_shape* sh, int chunks) {
   return w;
 }
 
+// Workspace of the fused entry points: the group counters [S * Hkv] int32
+// first (zero before the first call, left zero by every call), the work-queue
+// counter, then the partials MA [n, D], m [n], e [n] with
+// n = S * Hq * max_splits * chunks, each part 16-byte aligned.
+WsLayout ws_fused_layout(const da_shape* sh, int chunks, size_t* counters) {
+  *counters = align16((size_t)sh->S * sh->Hkv * sizeof(int32_t));
+  WsLayout w{};
+  w.queue = *counters;
+  w.ma = w.queue + 16;
+  const size_t n = (size_t)sh->S * sh->Hq * sh->max_splits * chunks;
+  w.m = w.ma + align16(n * sh->D * sizeof(float));
+  w.e = w.m + align16(n * sizeof(float));
+  w.total = w.e + align16(n * sizeof(float));
+  return w;
+}
+
 // Shape checks of the page-selection entry points.
 da_status check_selector(const da_shape* sh, int logical) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
@@ -197,34 +213,44 @@ da_status check_micro_built(const da_shape* sh) {
   return DA_OK;
 }
 
-// Body of both MicroAttention entry points; ks / vs are the per-row scales
-// of 8-bit pages (null otherwise).
+// Body of the MicroAttention entry points; ks / vs are the per-row scales
+// of 8-bit pages (null otherwise).  out == null: partials into MA, m, e
+// (chunk partials folded by the combine kernel); out != null: the fused
+// step, partials in the workspace and the merge done by the last item of
+// each (request, KV head), attention output into out.
 da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_pages,
                                const void* v_pages, const float* ks, const float* vs,
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* split_bounds, const uint8_t* block_mask, float* MA,
-                               float* m, float* e, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds || !MA || !m || !e)
+                               float* m, float* e, float* out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const bool fused = out != nullptr;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds ||
+      (!fused && (!MA || !m || !e)))
     return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(MA, 16))
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      (!fused && !aligned(MA, 16)))
     return fail(DA_ERR_INVALID_ARG, "q, k_pages, v_pages and MA must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(split_bounds, 4) ||
-      !aligned(m, 4) || !aligned(e, 4))
+      (!fused && (!aligned(m, 4) || !aligned(e, 4))) || (fused && !aligned(out, 4)))
     return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
   const da_status built = check_micro_built(sh);
   if (built != DA_OK) return built;
 
   int chunks = resolve_chunks(sh);
-  WsLayout ws = ws_layout(sh, chunks);
   const size_t have = workspace == nullptr ? (size_t)0 : workspace_bytes;
+  size_t counters = 0;
+  WsLayout ws = fused ? ws_fused_layout(sh, chunks, &counters) : ws_layout(sh, chunks);
   if (chunks > 1 && have < ws.total) {
     if (sh->chunks > 1)
       return fail(DA_ERR_INVALID_ARG, "chunks=%d needs a workspace of %zu bytes (got %zu)",
                   chunks, ws.total, have);
     chunks = 1;
-    ws = ws_layout(sh, 1);
+    ws = fused ? ws_fused_layout(sh, 1, &counters) : ws_layout(sh, 1);
   }
+  if (fused && have < ws.total)
+    return fail(DA_ERR_INVALID_ARG, "the fused step needs a workspace of %zu bytes (got %zu)",
+                ws.total, have);
   // with room for the counter the launcher may run persistently (when the
   // grid far exceeds the resident slots); without, one workgroup per item
   const bool persistent = have >= ws.total;
@@ -247,9 +273,12 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.ks = ks;
   p.vs = vs;
   char* wsb = static_cast<char*>(workspace);
-  p.MA = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.ma) : MA;
-  p.m = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.m) : m;
-  p.e = chunks > 1 ? reinterpret_cast<float*>(wsb + ws.e) : e;
+  const bool in_ws = fused || chunks > 1;  // partials in the workspace
+  p.MA = in_ws ? reinterpret_cast<float*>(wsb + ws.ma) : MA;
+  p.m = in_ws ? reinterpret_cast<float*>(wsb + ws.m) : m;
+  p.e = in_ws ? reinterpret_cast<float*>(wsb + ws.e) : e;
+  p.group_count = fused ? reinterpret_cast<int*>(wsb) : nullptr;
+  p.out = out;
   p.chunks = chunks;
   p.n_items = sh->S * sh->Hkv * sh->max_splits * chunks;
   p.grab = 1;
@@ -268,7 +297,7 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   hipError_t err = da::launch_micro(sh->dtype, sh->D, sh->Hq / sh->Hkv, p, stream);
   if (err != hipSuccess)
     return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
-  if (chunks > 1) {
+  if (chunks > 1 && !fused) {
     err = da::launch_combine(p.MA, p.m, p.e, MA, m, e, (long long)sh->S * sh->Hq * sh->max_splits,
                              chunks, sh->D, stream);
     if (err != hipSuccess)
@@ -289,8 +318,8 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
   const da_status st = check_shape(sh);
   if (st != DA_OK) return st;
   return micro_attention_impl(sh, q, k_pages, v_pages, nullptr, nullptr, block_table, seq_lens,
-                              split_bounds, block_mask, MA, m, e, workspace, workspace_bytes,
-                              stream);
+                              split_bounds, block_mask, MA, m, e, nullptr, workspace,
+                              workspace_bytes, stream);
 }
 
 da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
@@ -308,8 +337,8 @@ da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_
   if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
     return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
   return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
-                              split_bounds, block_mask, MA, m, e, workspace, workspace_bytes,
-                              stream);
+                              split_bounds, block_mask, MA, m, e, nullptr, workspace,
+                              workspace_bytes, stream);
 }
 
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
@@ -319,6 +348,47 @@ da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
   st = check_micro_built(sh);
   if (st != DA_OK) return st;
   *bytes = ws_layout(sh, resolve_chunks(sh)).total;
+  return DA_OK;
+}
+
+da_status da_attention(const da_shape* sh, const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const da_status st = check_shape(sh);
+  if (st != DA_OK) return st;
+  if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  return micro_attention_impl(sh, q, k_pages, v_pages, nullptr, nullptr, block_table, seq_lens,
+                              split_bounds, block_mask, nullptr, nullptr, nullptr, out, workspace,
+                              workspace_bytes, stream);
+}
+
+da_status da_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                           const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const da_status st = check_shape(sh, true);
+  if (st != DA_OK) return st;
+  if (sh->dtype != DA_FP8_E4M3)
+    return fail(DA_ERR_INVALID_ARG, "da_attention_fp8 needs dtype DA_FP8_E4M3 (got %d)", sh->dtype);
+  if (!k_scales || !v_scales || !out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
+  return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
+                              split_bounds, block_mask, nullptr, nullptr, nullptr, out, workspace,
+                              workspace_bytes, stream);
+}
+
+da_status da_attention_workspace_size(const da_shape* sh, size_t* bytes, size_t* counter_bytes) {
+  if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
+  da_status st = check_shape(sh, true);
+  if (st != DA_OK) return st;
+  st = check_micro_built(sh);
+  if (st != DA_OK) return st;
+  size_t counters = 0;
+  *bytes = ws_fused_layout(sh, resolve_chunks(sh), &counters).total;
+  if (counter_bytes != nullptr) *counter_bytes = counters;
   return DA_OK;
 }
 

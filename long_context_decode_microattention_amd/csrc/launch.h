@@ -34,6 +34,12 @@ struct MicroParams {
   int n_items;
   int grab;
   int schedule;  // 0: launcher's choice, 1: one workgroup per item, 2: persistent
+  // Fused merge: group_count [S * Hkv] counters, zero when the kernel starts
+  // and left zero by it; the item completing the last partial of its
+  // (request, KV head) merges the group's partials into out [S, Hq, D].
+  // group_count == null: partials only.
+  int* group_count;
+  float* out;
 };
 
 // Returns hipErrorInvalidValue for a (dtype, D, G) combination that is not

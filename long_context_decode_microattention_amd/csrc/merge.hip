@@ -21,18 +21,6 @@ namespace {
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / kWave;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
-}
-
 template <bool kPartial>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ MA,
                                                               const float* __restrict__ m,

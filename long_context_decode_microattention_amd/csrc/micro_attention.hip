@@ -61,7 +61,7 @@ struct Frag {
   float vs[Layout<DT, D, SL>::NI];
 };
 
-template <int DT, int D, int G, int SL>
+template <int DT, int D, int G, int SL, bool kFused>
 __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   using L = Layout<DT, D, SL>;
   __shared__ int s_phys[kPageCap];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   const int chunk = lane % L::LPT;
 
   __shared__ int s_claim;
-  for_each_item(p, &s_claim, [&](int x) {
+  for_each_item<kFused>(p, &s_claim, [&](int x) {
     const Item it = plan_item(p, x);
     const int s = it.s, kvh = it.kvh, h0 = kvh * G;
     const int t0 = it.t0, t1 = it.t1;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
         m_[g] = M;
       }
     }
-    finish_item<G, D, L::LPT, L::EPL>(p, it, s_fin, m_, e_, acc, c);
+    finish_item<G, D, L::LPT, L::EPL, kFused>(p, it, s_fin, m_, e_, acc, c);
   });
 }
 
@@ -363,7 +363,9 @@ constexpr int kValuWorkgroupsPerCU = 0;
 
 template <int DT, int D, int G, int SL = kSlab>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_kernel(micro_kernel<DT, D, G, SL>, kValuWorkgroupsPerCU, p, stream);
+  if (p.group_count != nullptr)
+    return launch_micro_kernel(micro_kernel<DT, D, G, SL, true>, kValuWorkgroupsPerCU, p, stream);
+  return launch_micro_kernel(micro_kernel<DT, D, G, SL, false>, kValuWorkgroupsPerCU, p, stream);
 }
 
 template <int DT, int D>

@@ -108,7 +108,7 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // Two waves per SIMD: the register budget that holds the prefetched slab, the
 // query operand and the accumulators without spilling (measured faster than
 // three waves with spills).
-template <int DT, int D, int G, int SL>
+template <int DT, int D, int G, int SL, bool kFused>
 __global__ __launch_bounds__(kMicroThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   using L = MLayout<DT, D, SL>;
@@ -131,7 +131,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   const int quad = lane & 3;  // head within a 4x4 block of the value product
 
   __shared__ int s_claim;
-  for_each_item(p, &s_claim, [&](int x) {
+  for_each_item<kFused>(p, &s_claim, [&](int x) {
     const Item it = plan_item(p, x);
     const int s = it.s, kvh = it.kvh, h0 = kvh * G;
     const int t0 = it.t0, t1 = it.t1;
@@ -457,7 +457,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   #pragma unroll
         for (int k = 0; k < 8; ++k) accg[h][k] += __shfl_xor(accg[h][k], off, kWave);
 
-    finish_item<G, D, L::LPT, 8>(p, it, s_fin, m_h, we, accg, c);
+    finish_item<G, D, L::LPT, 8, kFused>(p, it, s_fin, m_h, we, accg, c);
   });
 }
 
@@ -466,7 +466,9 @@ constexpr int kMfmaWorkgroupsPerCU = 2;
 
 template <int DT, int D, int G, int SL>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL>, kMfmaWorkgroupsPerCU, p, stream);
+  if (p.group_count != nullptr)
+    return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL, true>, kMfmaWorkgroupsPerCU, p, stream);
+  return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL, false>, kMfmaWorkgroupsPerCU, p, stream);
 }
 
 // bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups

@@ -52,14 +52,30 @@ __device__ __forceinline__ Item plan_item(const MicroParams& p, int x) {
   return it;
 }
 
-// Runs body(x) for every work item x this workgroup owns: item blockIdx.x
+// The fused-merge arguments, copied to LDS once per workgroup before the
+// first item and read back at the end of each item, so that they hold no
+// scalar registers across the slab loop.  The fused merge is a separate
+// kernel instance (template flag kFused): compiled into every instance, its
+// code raised the register allocation of the slab loop by ~20 VGPRs even
+// where it never runs (one wave per SIMD less for the vector kernel).
+struct FusedArgs {
+  int* group_count;
+  float* out;
+};
+static __shared__ FusedArgs s_fused;
+
+// Runs body(x) for every work item x this workgroup owns (kFused: the
+// kernel instance with the fused merge): item blockIdx.x
 // for a one-per-item launch, or, for a persistent launch, items claimed from
 // p.queue `grab` at a time in increasing order until none are left.  The
 // next claim is issued before the current items are processed, so its
 // latency is hidden.  body may use LDS and barriers; every lane calls it with
 // the same x.
-template <class Body>
+template <bool kFused, class Body>
 __device__ __forceinline__ void for_each_item(const MicroParams& p, int* s_claim, Body&& body) {
+  if constexpr (kFused) {
+    if (threadIdx.x == 0) s_fused = FusedArgs{p.group_count, p.out};  // read after later barriers
+  }
   if (p.queue == nullptr) {
     body((int)blockIdx.x);
     return;
@@ -120,14 +136,165 @@ struct FinishLds {
   float acc[kMicroWaves][G][D];
   float m[kMicroWaves][G];
   float e[kMicroWaves][G];
+  int last;  // fused merge: this item completed its group
 };
+
+// Device-scope (agent) relaxed store and load: coherent across the XCDs'
+// L2 caches by themselves, so partials written by one workgroup can be read
+// by another without cache-wide fences.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's vector memory operations (its stores) completed:
+// s_waitcnt vmcnt(0), the other counters left unconstrained.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Fused merge.  Called by every thread after the item's partials are
+// written.  The partials are released to device scope and the group's
+// counter counted up; the item that brings it to max_splits * chunks folds
+// all partials of the group's G query heads with the aggregation rule of
+// the merge kernel (m_g = max m_j, w_j = exp(m_j - m_g), e_g = sum e_j w_j,
+// out = sum MA_j w_j / e_g, out = 0 when every partial is empty) and sets
+// the counter back to zero for the next call.  No workgroup waits for
+// another: only the last arrival does more work.
+template <int G, int D>
+__device__ __forceinline__ void merge_group(const MicroParams& p, const Item& it, FinishLds<G, D>& L) {
+  static_assert(kMicroThreads % D == 0 && G * D * kMicroWaves >= kMicroThreads, "merge scratch");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = p.max_splits * p.chunks;
+  int* count = s_fused.group_count + (size_t)it.s * p.Hkv + it.kvh;
+  // The partials were written as device-scope stores (coherent across the
+  // XCDs' L2 caches without a cache-wide write-back); wait until they have
+  // completed before the counter says so.  A device-scope fence here would
+  // write back and invalidate the whole L2 for every item, which measured
+  // 0.2-0.35 us per item.
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) L.last = atomicAdd(count, 1) == n - 1;
+  __syncthreads();
+  if (!L.last) return;
+  const size_t h0 = (size_t)it.s * p.Hq + it.kvh * G;  // first query head of the group
+  constexpr int SCR = kMicroWaves * G * D;              // floats of scratch in L.acc
+  constexpr int GD = G * D;
+  float* sw = &L.acc[0][0][0];
+  if (2 * G * n <= SCR) {
+    // m and e of every partial of the group into LDS in one pass (the
+    // group's heads are consecutive, so its partials are one run)
+    for (int x = tid; x < G * n; x += kMicroThreads) {
+      sw[x] = load_dev(p.m + h0 * n + x);
+      sw[G * n + x] = load_dev(p.e + h0 * n + x);
+    }
+    __syncthreads();
+    // per head (one wave each): m_g, the weights exp(m_i - m_g) in place of
+    // the m_i, and e_g
+    for (int g = wave; g < G; g += kMicroWaves) {
+      float lm = neg_inf();
+      for (int i = lane; i < n; i += kWave) lm = fmaxf(lm, sw[g * n + i]);
+      const float M = wave_max(lm);
+      const float Ms = (M == neg_inf()) ? 0.f : M;
+      float le = 0.f;
+      for (int i = lane; i < n; i += kWave) {
+        const float w = expf(sw[g * n + i] - Ms);
+        le = fmaf(sw[G * n + g * n + i], w, le);
+        sw[g * n + i] = w;
+      }
+      le = wave_sum(le);
+      if (lane == 0) L.e[0][g] = le;
+    }
+    __syncthreads();
+    // value sums of the G * D outputs, each split into phs phases over the
+    // partials (all threads busy), 8 loads in flight per thread; the phase
+    // sums go where the e_i were
+    const int phs = max(1, min(kMicroThreads / GD, (SCR - G * n) / GD));
+    float* red = sw + G * n;
+    for (int t = tid; t < phs * GD; t += kMicroThreads) {
+      const int o = t % GD, ph = t / GD;
+      const int g = o / D, d = o - g * D;
+      const float* MAr = p.MA + (h0 + g) * n * D + d;
+      const float* w = sw + g * n;
+      float acc = 0.f;
+      int i = ph;
+      for (; i + 7 * phs < n; i += 8 * phs) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = load_dev(MAr + (size_t)(i + u * phs) * D);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = fmaf(x[u], w[i + u * phs], acc);
+      }
+      for (; i < n; i += phs) acc = fmaf(load_dev(MAr + (size_t)i * D), w[i], acc);
+      if (phs == 1) {
+        const float eg = L.e[0][g];
+        s_fused.out[(h0 + g) * D + d] = eg > 0.f ? acc / eg : 0.f;
+      } else {
+        red[t] = acc;
+      }
+    }
+    if (phs > 1) {
+      __syncthreads();
+      for (int o = tid; o < GD; o += kMicroThreads) {
+        float total = 0.f;
+        for (int q = 0; q < phs; ++q) total += red[q * GD + o];
+        const int g = o / D;
+        const float eg = L.e[0][g];
+        s_fused.out[(h0 + g) * D + (o - g * D)] = eg > 0.f ? total / eg : 0.f;
+      }
+    }
+  } else {
+    // many partials (more than 2 D per head): head by head, in phases of D
+    constexpr int PH = kMicroThreads / D;
+    const int d = tid % D;
+    const int ph = tid / D;
+    float* red = sw;  // kMicroThreads floats
+    for (int g = 0; g < G; ++g) {
+      const size_t h = h0 + g;
+      const float* mr = p.m + h * n;
+      const float* er = p.e + h * n;
+      const float* MAr = p.MA + h * n * D;
+      float lm = neg_inf();
+      for (int i = tid; i < n; i += kMicroThreads) lm = fmaxf(lm, load_dev(mr + i));
+      lm = wave_max(lm);
+      if (lane == 0) L.m[wave][g] = lm;
+      __syncthreads();
+      float M = L.m[0][g];
+#pragma unroll
+      for (int w = 1; w < kMicroWaves; ++w) M = fmaxf(M, L.m[w][g]);
+      const float Ms = (M == neg_inf()) ? 0.f : M;
+      float le = 0.f;
+      for (int i = tid; i < n; i += kMicroThreads)
+        le = fmaf(load_dev(er + i), expf(load_dev(mr + i) - Ms), le);
+      le = wave_sum(le);
+      if (lane == 0) L.e[wave][g] = le;
+      float acc = 0.f;
+      for (int i = ph; i < n; i += PH)
+        acc = fmaf(load_dev(MAr + (size_t)i * D + d), expf(load_dev(mr + i) - Ms), acc);
+      red[tid] = acc;
+      __syncthreads();
+      if (tid < D) {
+        float total = 0.f;
+#pragma unroll
+        for (int q = 0; q < PH; ++q) total += red[q * D + tid];
+        float eg = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMicroWaves; ++w) eg += L.e[w][g];
+        s_fused.out[h * D + tid] = eg > 0.f ? total / eg : 0.f;
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) *count = 0;
+}
 
 // Combines the four waves' triples and writes the item's partials.  Each
 // wave supplies, per head g: raw-dot maximum wm[g] and exp-sum we[g] (valid
 // in every lane) and, in the lanes of its first row (lane < LPT), the value
 // sums acc[g][k] for dimensions lane*EPL + k.  Output index
 // ((s*Hq + h)*max_splits + j)*chunks + c.
-template <int G, int D, int LPT, int EPL>
+template <int G, int D, int LPT, int EPL, bool kFused>
 __device__ __forceinline__ void finish_item(const MicroParams& p, const Item& it, FinishLds<G, D>& L,
                                             const float (&wm)[G], const float (&we)[G],
                                             const float (&acc)[G][EPL], float c) {
@@ -162,12 +329,21 @@ __device__ __forceinline__ void finish_item(const MicroParams& p, const Item& it
       den = fmaf(L.e[w][g], f, den);
     }
     const size_t o = ((size_t)(it.s * p.Hq + h0 + g) * p.max_splits + it.j) * p.chunks + it.c;
-    p.MA[o * D + d] = num;
-    if (d == 0) {
-      p.m[o] = M * p.scale;
-      p.e[o] = den;
+    if constexpr (kFused) {  // read by another workgroup of the same launch
+      store_dev(p.MA + o * D + d, num);
+      if (d == 0) {
+        store_dev(p.m + o, M * p.scale);
+        store_dev(p.e + o, den);
+      }
+    } else {
+      p.MA[o * D + d] = num;
+      if (d == 0) {
+        p.m[o] = M * p.scale;
+        p.e[o] = den;
+      }
     }
   }
+  if constexpr (kFused) merge_group<G, D>(p, it, L);
 }
 
 // Dynamic LDS that caps a kernel at `wg` resident workgroups per CU (0 = no

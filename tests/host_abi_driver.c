@@ -2,8 +2,8 @@
  * UndefinedBehaviorSanitizer on the host code (tests/test_host_sanitizers.py).
  *
  * Every call below is rejected by the library's argument checks before any
- * GPU work is enqueued, or (da_micro_attention_workspace_size) is pure host
- * arithmetic, so the driver runs on a machine without a GPU.  It exercises
+ * GPU work is enqueued, or (da_micro_attention_workspace_size,
+ * da_attention_workspace_size) is pure host arithmetic, so the driver runs on a machine without a GPU.  It exercises
  * the checks' arithmetic on extreme sizes and the error-message formatting;
  * the sanitizers turn any out-of-bounds access, overflow or other undefined
  * behaviour on those paths into a failed run.  The pointers are never
@@ -120,6 +120,57 @@ int main(void) {
          da_micro_attention_fp8(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE,
                                 FAKE, FAKE, NULL, 0, NULL),
          DA_ERR_INVALID_ARG);
+
+  /* the fused step (attention in one launch) */
+  s = good();
+  expect("fused: null out",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, 1 << 20, NULL),
+         DA_ERR_INVALID_ARG);
+  expect("fused: no workspace",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 0, NULL),
+         DA_ERR_INVALID_ARG);
+  expect("fused: workspace too small",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 64, NULL),
+         DA_ERR_INVALID_ARG);
+  expect("fused: misaligned workspace",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, (char*)FAKE + 8,
+                      (size_t)1 << 30, NULL),
+         DA_ERR_INVALID_ARG);
+  expect("fused: misaligned out",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, (char*)FAKE + 2, FAKE,
+                      (size_t)1 << 30, NULL),
+         DA_ERR_INVALID_ARG);
+  s = good(); s.S = INT32_MAX; s.Hkv = INT32_MAX; s.Hq = INT32_MAX; s.max_splits = INT32_MAX;
+  expect("fused: S * Hkv * b overflow",
+         da_attention(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 1 << 20, NULL),
+         DA_ERR_INVALID_ARG);
+  s = good(); s.dtype = DA_FP8_E4M3;
+  expect("fused fp8: null scales",
+         da_attention_fp8(&s, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE,
+                          1 << 20, NULL),
+         DA_ERR_INVALID_ARG);
+  s = good();
+  expect("fused fp8: bf16 dtype",
+         da_attention_fp8(&s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE,
+                          1 << 20, NULL),
+         DA_ERR_INVALID_ARG);
+  {
+    size_t counters = 0;
+    s = good();
+    expect("fused workspace size", da_attention_workspace_size(&s, &bytes, &counters), DA_OK);
+    if (counters < (size_t)s.S * s.Hkv * 4 || bytes <= counters) {
+      fprintf(stderr, "FAIL fused workspace size: bytes %zu counters %zu\n", bytes, counters);
+      ++failures;
+    }
+    expect("fused workspace size, no counters out", da_attention_workspace_size(&s, &bytes, NULL),
+           DA_OK);
+    s = good(); s.S = 4096; s.Hq = 64; s.Hkv = 64; s.max_pages = 1 << 20; s.P = 16;
+    s.max_splits = 64; s.chunks = 64;
+    expect("fused workspace size, huge", da_attention_workspace_size(&s, &bytes, &counters),
+           DA_OK);
+    expect("fused workspace size, null out", da_attention_workspace_size(&s, NULL, &counters),
+           DA_ERR_INVALID_ARG);
+  }
 
   /* merge and the partial fold */
   s = good(); s.max_splits = 0;

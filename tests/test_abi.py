@@ -80,6 +80,72 @@ def test_micro_rejects(lib, case, status):
     assert len(lib.da_last_error()) > 0
 
 
+def call_fused(lib, sh, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, bounds=FAKE, mask=None, out=FAKE,
+                ws=FAKE, ws_bytes=1 << 30)
+    args.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.da_attention(None if sh is None else ctypes.byref(sh),
+                            *(vp(args[k]) for k in ("q", "k", "v", "table", "lens", "bounds",
+                                                    "mask", "out", "ws")),
+                            args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(sh=None), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(S=0)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(Hq=6, Hkv=4)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(out=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(out=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(q=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(ws=None, ws_bytes=0)), _lib.DA_ERR_INVALID_ARG),   # the fused step needs one
+    (dict(ptrs=dict(ws_bytes=64)), _lib.DA_ERR_INVALID_ARG),           # too small
+    (dict(ptrs=dict(ws=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),           # misaligned
+    (dict(shape=dict(chunks=4), ptrs=dict(ws_bytes=1024)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(dtype=_lib.DA_FP8_E4M3)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
+], ids=lambda x: str(x))
+def test_fused_rejects(lib, case, status):
+    sh = None if "sh" in case else good_shape(**case.get("shape", {}))
+    got = call_fused(lib, sh, **case.get("ptrs", {}))
+    assert got == status, (got, lib.da_last_error())
+    assert len(lib.da_last_error()) > 0
+
+
+def test_fused_fp8_rejects(lib):
+    vp = ctypes.c_void_p
+    sh = good_shape(dtype=_lib.DA_BF16)  # the 8-bit entry needs DA_FP8_E4M3
+    # q, k_codes, k_scales, v_codes, v_scales, table, lens, bounds, mask, out, workspace
+    got = lib.da_attention_fp8(ctypes.byref(sh), *([vp(FAKE)] * 8), None, vp(FAKE), vp(FAKE),
+                               1 << 30, None)
+    assert got == _lib.DA_ERR_INVALID_ARG
+    sh = good_shape(dtype=_lib.DA_FP8_E4M3)
+    got = lib.da_attention_fp8(ctypes.byref(sh), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE),
+                               vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 1 << 30, None)
+    assert got == _lib.DA_ERR_INVALID_ARG  # NULL k_scales
+
+
+def test_fused_workspace_size(lib):
+    """Counters first (one int32 per (request, KV head), 16-byte aligned),
+    then the work-queue counter and the partials of every split and chunk."""
+    sh = good_shape()
+    n, c = _lib.attention_workspace_size(sh)
+    assert c == 16 and n > c
+    chunks = 1
+    parts = sh.S * sh.Hq * sh.max_splits * chunks
+    # with automatic chunks the partials grow with the chunk count
+    assert n >= c + 16 + parts * (sh.D + 2) * 4
+    sh2 = good_shape(S=37, Hkv=2, Hq=8)
+    n2, c2 = _lib.attention_workspace_size(sh2)
+    assert c2 == ((37 * 2 * 4 + 15) // 16) * 16
+    forced = good_shape(chunks=3)
+    n3, _ = _lib.attention_workspace_size(forced)
+    assert n3 >= 16 + 16 + forced.S * forced.Hq * forced.max_splits * 3 * (forced.D + 2) * 4
+    with pytest.raises(_lib.DaError):
+        _lib.attention_workspace_size(good_shape(D=96))
+
+
 def test_workspace_size(lib):
     n = ctypes.c_size_t(7)
     # few items: the library cuts splits into chunks and needs a workspace

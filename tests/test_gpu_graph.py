@@ -1,8 +1,10 @@
 """A decode step captured once in a HIP graph (torch.cuda.CUDAGraph) and
 replayed, through the C ABI: append of the step's K/V rows (with page
 statistics), seq_lens + 1, MicroAttention with the chunk's reused mask and
-split bounds, merge.  Every replay is checked bit for bit against the same
-step run eagerly on the same state: the kernels are deterministic (one
+split bounds, merge -- as two calls, or as the fused single launch whose
+group counters must return to zero for the next replay.  Every replay is
+checked bit for bit against the same step run eagerly on the same state:
+the kernels are deterministic (one
 workgroup owns each item or chunk, whatever order the work queue hands them
 out in), so a replay must reproduce the eager bits exactly.  Between
 replays the program does eager work of its own and synchronizes, and the
@@ -50,11 +52,12 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_call", "fused"])
 @pytest.mark.parametrize("schedule,chunks", SCHEDULES)
 @pytest.mark.parametrize("name", list(SPECS))
-def test_graph_replay_matches_eager(name, schedule, chunks):
+def test_graph_replay_matches_eager(name, schedule, chunks, fused):
     spec, logical = SPECS[name]
-    announce("graph replay", name, f"schedule={schedule} chunks={chunks}")
+    announce("graph replay", name, f"schedule={schedule} chunks={chunks} fused={fused}")
     b = wl.build(spec, 3, DEV)
     P, Hkv = spec.P, spec.Hkv
     sel = torch.tensor([1 if i >= Hkv // 2 else 0 for i in range(Hkv)], dtype=torch.uint8,
@@ -81,13 +84,21 @@ def test_graph_replay_matches_eager(name, schedule, chunks):
     e = torch.empty((S, Hq, 8), dtype=torch.float32, device=DEV)
     out = torch.empty((S, Hq, D), dtype=torch.float32, device=DEV)
 
+    sh = _lib.shape_of(b.q, b.k_pages, b.block_table, bounds, b.scale, chunks, schedule)
+    fws = torch.zeros(_lib.attention_workspace_size(sh)[0], dtype=torch.uint8, device=DEV)
+
     def step():
         _lib.append_kv(kn, vn, b.block_table, lens, b.k_pages, b.v_pages, stats=stats,
                        logical=logical, select_heads=sel)
         lens.add_(1)
-        _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
-                             scale=b.scale, out=(MA, m, e), schedule=schedule, chunks=chunks)
-        _lib.merge(MA, m, e, out=out)
+        if fused:  # one launch: partials and merge (group counters in fws)
+            _lib.attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
+                           scale=b.scale, out=out, schedule=schedule, chunks=chunks,
+                           workspace=fws)
+        else:
+            _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
+                                 scale=b.scale, out=(MA, m, e), schedule=schedule, chunks=chunks)
+            _lib.merge(MA, m, e, out=out)
 
     def restore():
         for t, t0 in zip((b.k_pages, b.v_pages, stats), init):
@@ -137,3 +148,5 @@ def test_graph_replay_matches_eager(name, schedule, chunks):
         assert torch.equal(lens, lens0 + i + 1), f"replay {i}: seq_lens"
     for got, ref, what in zip((b.k_pages, b.v_pages, stats), want_state, ("K", "V", "stats")):
         assert torch.equal(got, ref), f"{what} after {STEPS} replays differs from the eager steps"
+    counters = _lib.attention_workspace_size(sh)[1]
+    assert int(fws[:counters].count_nonzero()) == 0, "group counters left non-zero"
