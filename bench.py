@@ -142,6 +142,22 @@ def time_workload(key, steps, warmup, dev):
     avg_micro = sum(micro_ms) / steps
     avg_merge = sum(merge_ms) / steps
     assert torch.isfinite(out).all(), "non-finite output"
+
+    # the same step in one launch (da_attention / da_attention_fp8), beside it
+    fused = _lib.attention_fp8 if fp8 else _lib.attention
+    out_f = torch.empty_like(out)
+    for _ in range(max(1, warmup)):
+        fused(*args, scale=b.scale, out=out_f, pool_layout=b.layout)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(steps):
+        fused(*args, scale=b.scale, out=out_f, pool_layout=b.layout)
+    f1.record()
+    torch.cuda.synchronize()
+    us_fused = f0.elapsed_time(f1) * 1e3 / steps
+    fused_diff = float((out_f - out).abs().max())
+    assert fused_diff <= 1e-4, f"one-launch step differs from the two calls by {fused_diff}"
     res = dict(
         workload=spec.name, key=key, kv_bytes=kv_bytes, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, us_micro=avg_micro * 1e3, us_merge=avg_merge * 1e3,
@@ -153,6 +169,7 @@ def time_workload(key, steps, warmup, dev):
                    max_len=spec.max_len, block_mask=spec.mask is not None),
         kept_tokens=kept,
         tokens_per_s=kept / (ms_step * 1e-3),
+        us_per_step_one_launch=us_fused, one_launch_max_abs_diff=fused_diff,
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
     return b, res
@@ -501,6 +518,7 @@ def main():
         },
         "us_merge": round(head["us_merge"], 2),
         "merge_share_of_step": round(head["merge_share"], 5),
+        "us_per_step_one_launch": round(head["us_per_step_one_launch"], 2),
         "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "frac_of_read_ceiling": None if ceiling is None else round(head["GBps"] / ceiling, 4),
         "cpu_baseline": cpu,
