@@ -385,3 +385,28 @@ def test_append_kv_fp8_rejects(lib, case, status):
                                                     "vc", "vs")], case.get("logical", 16), None,
                                _vp(p.get("stats")), None)
     assert got == status, _lib.load().da_last_error()
+
+
+def test_fused_workspace_clean_prefix_bookkeeping():
+    """The binding's cached workspace for the one-launch step (host logic,
+    CPU tensors): a new buffer is all zero; a call whose counters reach past
+    what the previous call left clean gets exactly that range zeroed first;
+    a buffer too small is replaced by a larger zeroed one."""
+    w = _lib._FusedWorkspace()
+    buf = w.get("cpu", 256, 32)
+    assert buf.numel() == 256 and int(buf.count_nonzero()) == 0
+    buf[32:].fill_(7)          # the call's partials land after its 32 counter bytes
+    again = w.get("cpu", 256, 32)
+    assert again is buf and int(buf[:32].count_nonzero()) == 0
+    assert int((buf[32:] == 7).sum()) == 224   # not touched: this call's counters end at 32
+    grown = w.get("cpu", 256, 96)               # more counters, over the old partials
+    assert grown is buf
+    assert int(buf[:96].count_nonzero()) == 0 and int((buf[96:] == 7).sum()) == 160
+    buf[96:].fill_(5)
+    small = w.get("cpu", 128, 16)               # fits: same buffer, clean prefix shrinks to 16
+    assert small is buf and w.clean == 16
+    buf[16:].fill_(3)
+    w.get("cpu", 256, 64)
+    assert int(buf[:64].count_nonzero()) == 0 and int((buf[64:] == 3).sum()) == 192
+    big = w.get("cpu", 1024, 64)                # too small: a fresh zeroed buffer
+    assert big is not buf and big.numel() == 1024 and int(big.count_nonzero()) == 0
