@@ -136,8 +136,10 @@ typedef struct da_shape {
  *   da_micro_attention_workspace_size() bytes.  It holds a work-queue
  *   counter (reset on `stream` by the call itself) used when the grid of
  *   (request, KV head, split) items is far larger than the GPU can hold at
- *   once, and, when there are few items, the partials of page-range chunks
- *   that every split is cut into for balance and folded back afterwards.
+ *   once, and the partials of page-range chunks that every split is cut
+ *   into and folded back afterwards: with sh->chunks == 0, when there are
+ *   fewer items than the GPU runs at once, or when splits are long (4 MiB
+ *   of K and V or more) and cutting them balances the launch.
  *   With sh->chunks == 0 and a NULL or smaller workspace the call runs with
  *   one workgroup per unchunked item (same results, possibly slower); with
  *   sh->chunks > 1 a missing workspace is DA_ERR_INVALID_ARG.  Concurrent
