@@ -172,6 +172,7 @@ def time_workload(key, steps, warmup, dev):
         us_per_step_one_launch=us_fused, one_launch_max_abs_diff=fused_diff,
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
+    b.out = out  # the timed step's output, compared with the oracle's in cpu_baseline
     return b, res
 
 
@@ -427,7 +428,7 @@ def cpu_baseline(b, budget_s):
     lens = b.seq_lens.cpu().numpy()
     kept = b.kept_tokens()
     units = [(s, kvh) for s in range(sp.S) for kvh in range(sp.Hkv)]
-    done_bytes, secs, n = 0, 0.0, 0
+    done_bytes, secs, n, err = 0, 0.0, 0, 0.0
     with threadpool_limits(limits=1):
         for s, kvh in units:
             L = int(lens[s])
@@ -442,15 +443,21 @@ def cpu_baseline(b, budget_s):
                 mask = h(b.block_mask[s:s + 1, kvh:kvh + 1, :npg].contiguous())
             table = np.arange(npg, dtype=np.int32)[None, :]
             t0 = time.perf_counter()
-            oracle.attention(q, k, v, table, np.array([L], dtype=np.int32), block_mask=mask, scale=b.scale)
+            want = oracle.attention(q, k, v, table, np.array([L], dtype=np.int32), block_mask=mask,
+                                    scale=b.scale)
             secs += time.perf_counter() - t0
+            got = b.out[s:s + 1, kvh * G:(kvh + 1) * G].double().cpu().numpy()
+            err = max(err, float(np.max(np.abs(got - want))))
             done_bytes += int(kept[s, kvh]) * 2 * sp.D * sp.esize
             n += 1
             if secs >= budget_s:
                 break
+    tol = 1e-5 if sp.dtype == wl.F32 else 2e-3
+    assert err <= tol, f"timed step differs from the oracle on the sample by {err:.3e} (> {tol})"
     return dict(value=done_bytes / secs / 1e9, unit="GB/s", cores=1, kind="oracle",
                 sample=f"{sp.name}: {n} (request, KV head) unit(s), {done_bytes / 2**30:.2f} GiB of "
-                       f"K+V, fp64 numpy oracle.attention, BLAS limited to 1 thread, {secs:.1f} s")
+                       f"K+V, fp64 numpy oracle.attention, BLAS limited to 1 thread, {secs:.1f} s",
+                max_abs_err_vs_step=err, tolerance=tol)
 
 
 def main():
