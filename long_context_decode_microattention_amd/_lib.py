@@ -204,6 +204,66 @@ def _cached_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tenso
     return ws
 
 
+def _paged_args(q, k, v, block_table, seq_lens, split_bounds, block_mask, scale, chunks, schedule,
+                pool_layout, k_scales=None, v_scales=None) -> DaShape:
+    """Checks the arguments every attention entry point shares and returns
+    the call's da_shape: bf16 / fp32 pools (k, v as q's dtype), or 8-bit
+    pools (k, v uint8 codes with k_scales / v_scales, q bf16)."""
+    dev = q.device
+    fp8 = k_scales is not None
+    _need(q, "q", torch.bfloat16 if fp8 else None, dev, 3)
+    _need(k, "k_codes" if fp8 else "k_pages", torch.uint8 if fp8 else q.dtype, dev, 4)
+    _need(v, "v_codes" if fp8 else "v_pages", torch.uint8 if fp8 else q.dtype, dev, 4)
+    if v.shape != k.shape:
+        raise ValueError("the K and V pools differ in shape")
+    if fp8:
+        for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+            _need(t, name, torch.float32, dev, 3)
+            if tuple(t.shape) != tuple(k.shape[:3]):
+                raise ValueError(f"{name} must match the first three dims of the code pools")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, dev, 3)
+    sh = shape_of(q, k, block_table, split_bounds, scale, chunks, schedule, pool_layout)
+    if fp8:
+        sh.dtype = DA_FP8_E4M3
+    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
+        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
+    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
+        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
+    return sh
+
+
+def _partials_out(sh: DaShape, out, dev):
+    """(MA, m, e) to write: fresh tensors, or the caller's."""
+    if out is None:
+        return (torch.empty((sh.S, sh.Hq, sh.max_splits, sh.D), dtype=torch.float32, device=dev),
+                torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev),
+                torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev))
+    return out
+
+
+def _micro_workspace(sh: DaShape, workspace, dev):
+    if workspace is False:
+        return None
+    if workspace is None:
+        return _cached_workspace(dev, workspace_size(sh))
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    return workspace
+
+
+def _step_out(sh: DaShape, out, dev):
+    if out is None:
+        return torch.empty((sh.S, sh.Hq, sh.D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, 3)
+    if tuple(out.shape) != (sh.S, sh.Hq, sh.D):
+        raise ValueError("out must be [S, Hq, D]")
+    return out
+
+
 def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
                     *, scale: Optional[float] = None, out=None, chunks: int = 0,
                     workspace: Optional[torch.Tensor] = None, schedule: int = 0,
@@ -216,33 +276,10 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
     workgroup per item, no chunks).  schedule: 0 library choice, 1 one
     workgroup per item, 2 persistent workgroups on a work queue."""
     dev = q.device
-    _need(q, "q", None, dev, 3)
-    _need(k_pages, "k_pages", q.dtype, dev, 4)
-    _need(v_pages, "v_pages", q.dtype, dev, 4)
-    if v_pages.shape != k_pages.shape:
-        raise ValueError("k_pages and v_pages differ in shape")
-    _need(block_table, "block_table", torch.int32, dev, 2)
-    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
-    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule, pool_layout)
-    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
-        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
-    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
-        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
-    if out is None:
-        MA = torch.empty((sh.S, sh.Hq, sh.max_splits, sh.D), dtype=torch.float32, device=dev)
-        m = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
-        e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
-    else:
-        MA, m, e = out
-    if workspace is False:
-        workspace = None
-    elif workspace is None:
-        workspace = _cached_workspace(dev, workspace_size(sh))
-    elif workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout)
+    MA, m, e = _partials_out(sh, out, dev)
+    workspace = _micro_workspace(sh, workspace, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().da_micro_attention(
         ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
@@ -283,38 +320,10 @@ def micro_attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, se
     k_scales / v_scales [NP, Hkv, P] float32.  Arguments otherwise as
     micro_attention."""
     dev = q.device
-    _need(q, "q", torch.bfloat16, dev, 3)
-    _need(k_codes, "k_codes", torch.uint8, dev, 4)
-    _need(v_codes, "v_codes", torch.uint8, dev, 4)
-    if v_codes.shape != k_codes.shape:
-        raise ValueError("k_codes and v_codes differ in shape")
-    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
-        _need(t, name, torch.float32, dev, 3)
-        if tuple(t.shape) != tuple(k_codes.shape[:3]):
-            raise ValueError(f"{name} must match the first three dims of the code pools")
-    _need(block_table, "block_table", torch.int32, dev, 2)
-    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
-    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule, pool_layout)
-    sh.dtype = DA_FP8_E4M3
-    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
-        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
-    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
-        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
-    if out is None:
-        MA = torch.empty((sh.S, sh.Hq, sh.max_splits, sh.D), dtype=torch.float32, device=dev)
-        m = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
-        e = torch.empty((sh.S, sh.Hq, sh.max_splits), dtype=torch.float32, device=dev)
-    else:
-        MA, m, e = out
-    if workspace is False:
-        workspace = None
-    elif workspace is None:
-        workspace = _cached_workspace(dev, workspace_size(sh))
-    elif workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    sh = _paged_args(q, k_codes, v_codes, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout, k_scales, v_scales)
+    MA, m, e = _partials_out(sh, out, dev)
+    workspace = _micro_workspace(sh, workspace, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().da_micro_attention_fp8(
         ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
@@ -421,27 +430,9 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
     cached per-device one; a caller's own must have been zero-filled once
     (see da_attention) and must not be shared by concurrent calls."""
     dev = q.device
-    _need(q, "q", None, dev, 3)
-    _need(k_pages, "k_pages", q.dtype, dev, 4)
-    _need(v_pages, "v_pages", q.dtype, dev, 4)
-    if v_pages.shape != k_pages.shape:
-        raise ValueError("k_pages and v_pages differ in shape")
-    _need(block_table, "block_table", torch.int32, dev, 2)
-    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
-    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_pages, block_table, split_bounds, scale, chunks, schedule, pool_layout)
-    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
-        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
-    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
-        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
-    if out is None:
-        out = torch.empty((sh.S, sh.Hq, sh.D), dtype=torch.float32, device=dev)
-    else:
-        _need(out, "out", torch.float32, dev, 3)
-        if tuple(out.shape) != (sh.S, sh.Hq, sh.D):
-            raise ValueError("out must be [S, Hq, D]")
+    sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout)
+    out = _step_out(sh, out, dev)
     ws = _fused_workspace(dev, sh, workspace)
     _check(load().da_attention(
         ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
@@ -456,32 +447,9 @@ def attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens
     """One decode step over 8-bit pages in one launch via da_attention_fp8
     (inputs as micro_attention_fp8, output and workspace as attention)."""
     dev = q.device
-    _need(q, "q", torch.bfloat16, dev, 3)
-    _need(k_codes, "k_codes", torch.uint8, dev, 4)
-    _need(v_codes, "v_codes", torch.uint8, dev, 4)
-    if v_codes.shape != k_codes.shape:
-        raise ValueError("k_codes and v_codes differ in shape")
-    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
-        _need(t, name, torch.float32, dev, 3)
-        if tuple(t.shape) != tuple(k_codes.shape[:3]):
-            raise ValueError(f"{name} must match the first three dims of the code pools")
-    _need(block_table, "block_table", torch.int32, dev, 2)
-    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
-    _need(split_bounds, "split_bounds", torch.int32, dev, 3)
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k_codes, block_table, split_bounds, scale, chunks, schedule, pool_layout)
-    sh.dtype = DA_FP8_E4M3
-    if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
-        raise ValueError("block_table, seq_lens and split_bounds must have S rows")
-    if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
-        raise ValueError(f"block_mask must be [S, Hkv, max_pages] = {(sh.S, sh.Hkv, sh.max_pages)}")
-    if out is None:
-        out = torch.empty((sh.S, sh.Hq, sh.D), dtype=torch.float32, device=dev)
-    else:
-        _need(out, "out", torch.float32, dev, 3)
-        if tuple(out.shape) != (sh.S, sh.Hq, sh.D):
-            raise ValueError("out must be [S, Hq, D]")
+    sh = _paged_args(q, k_codes, v_codes, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout, k_scales, v_scales)
+    out = _step_out(sh, out, dev)
     ws = _fused_workspace(dev, sh, workspace)
     _check(load().da_attention_fp8(
         ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
