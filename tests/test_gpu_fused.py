@@ -137,6 +137,22 @@ def test_fused_repeated_calls_and_growing_shapes():
         assert max_abs(got, two_call(bb)) <= TOL_SAME[bb.spec.dtype], bb.spec.name
 
 
+@pytest.mark.parametrize("schedule", [1, 2])
+def test_fused_many_groups_same_bits_every_call(schedule):
+    """Many groups of short, chunked items (every group's last arrival
+    merges partials other workgroups wrote moments before): 20 calls give
+    the same bits, equal to the two calls within fp32 rounding."""
+    spec = REDUCED["C3"]
+    announce("fused many groups", schedule)
+    b = wl.build(spec, 11, DEV)
+    ws, counters = fused_workspace(b, 3, schedule)
+    first = fused(b, ws, 3, schedule)
+    assert max_abs(first, two_call(b, 3, schedule)) <= TOL_SAME[spec.dtype]
+    for i in range(19):
+        assert torch.equal(fused(b, ws, 3, schedule), first), f"call {i + 2} differs"
+    assert int(ws[:counters].count_nonzero()) == 0
+
+
 def test_fused_masks_empty_requests_and_poison():
     """All-masked-but-one page, only the partial last page kept, an empty
     request (output 0) and NaN in every page slot no split may read."""
