@@ -272,9 +272,11 @@ def micro_attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, bl
 
     chunks: 0 lets the library cut splits into page ranges when that balances
     the launch; a positive value forces that many.  workspace: a uint8
-    device tensor; None uses a cached per-device one; False passes none (one
-    workgroup per item, no chunks).  schedule: 0 library choice, 1 one
-    workgroup per item, 2 persistent workgroups on a work queue."""
+    device tensor; None uses a cached per-device one (which a later call
+    with a larger shape replaces: a HIP graph must be captured with a
+    workspace of its own); False passes none (one workgroup per item, no
+    chunks).  schedule: 0 library choice, 1 one workgroup per item, 2
+    persistent workgroups on a work queue."""
     dev = q.device
     sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
                      chunks, schedule, pool_layout)
@@ -427,8 +429,10 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
               workspace: Optional[torch.Tensor] = None, pool_layout: str = "page"):
     """One decode step in one launch via da_attention: MicroAttention partials
     and their merge into out [S, Hq, D] float32.  workspace: None uses a
-    cached per-device one; a caller's own must have been zero-filled once
-    (see da_attention) and must not be shared by concurrent calls."""
+    cached per-device one (replaced by a later call with a larger shape, so
+    a HIP graph must be captured with a workspace of its own); a caller's
+    own must have been zero-filled once (see da_attention) and must not be
+    shared by concurrent calls."""
     dev = q.device
     sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
                      chunks, schedule, pool_layout)
