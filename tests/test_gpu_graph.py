@@ -85,7 +85,9 @@ def test_graph_replay_matches_eager(name, schedule, chunks, fused):
     out = torch.empty((S, Hq, D), dtype=torch.float32, device=DEV)
 
     sh = _lib.shape_of(b.q, b.k_pages, b.block_table, bounds, b.scale, chunks, schedule)
+    # workspaces of the graph's own (the binding's cached ones may be replaced)
     fws = torch.zeros(_lib.attention_workspace_size(sh)[0], dtype=torch.uint8, device=DEV)
+    mws = torch.empty(max(16, _lib.workspace_size(sh)), dtype=torch.uint8, device=DEV)
 
     def step():
         _lib.append_kv(kn, vn, b.block_table, lens, b.k_pages, b.v_pages, stats=stats,
@@ -97,7 +99,8 @@ def test_graph_replay_matches_eager(name, schedule, chunks, fused):
                            workspace=fws)
         else:
             _lib.micro_attention(b.q, b.k_pages, b.v_pages, b.block_table, lens, bounds, mask,
-                                 scale=b.scale, out=(MA, m, e), schedule=schedule, chunks=chunks)
+                                 scale=b.scale, out=(MA, m, e), schedule=schedule, chunks=chunks,
+                                 workspace=mws)
             _lib.merge(MA, m, e, out=out)
 
     def restore():
