@@ -477,8 +477,13 @@ hipError_t launch_select_pages(const SelectorParams& p, hipStream_t stream) {
   else if (need <= 2) hipLaunchKernelGGL(select_pages_kernel<2>, g, b, 0, stream, p);
   else if (need <= 4) hipLaunchKernelGGL(select_pages_kernel<4>, g, b, 0, stream, p);
   else if (need <= 8) hipLaunchKernelGGL(select_pages_kernel<8>, g, b, 0, stream, p);
+  // each bit round counts every key a lane holds: steps of 4 past 8 keep the
+  // count close to what the row needs (a 8193-page row takes 12, not 16)
+  else if (need <= 12) hipLaunchKernelGGL(select_pages_kernel<12>, g, b, 0, stream, p);
   else if (need <= 16) hipLaunchKernelGGL(select_pages_kernel<16>, g, b, 0, stream, p);
+  else if (need <= 24) hipLaunchKernelGGL(select_pages_kernel<24>, g, b, 0, stream, p);
   else if (need <= 32) hipLaunchKernelGGL(select_pages_kernel<32>, g, b, 0, stream, p);
+  else if (need <= 48) hipLaunchKernelGGL(select_pages_kernel<48>, g, b, 0, stream, p);
   else if (need <= kTopkMaxKeys) hipLaunchKernelGGL(select_pages_kernel<kTopkMaxKeys>, g, b, 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();

@@ -181,7 +181,7 @@ def test_selector_parity(name, seed):
     _run_case(name, spec, logical, seed)
 
 
-@pytest.mark.parametrize("max_pages", [5, 1000, 1024, 1025, 2049, 8192 + 77, 32768 + 1, 65536])
+@pytest.mark.parametrize("max_pages", [5, 1000, 1024, 1025, 2049, 8192 + 77, 20000, 32768 + 1, 65536])
 @pytest.mark.parametrize("kind", ["ties", "continuous", "signed_zero"])
 def test_select_pages_direct(max_pages, kind):
     """da_select_pages on seeded score arrays: heavy ties, continuous values,
