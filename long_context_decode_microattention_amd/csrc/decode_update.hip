@@ -30,6 +30,7 @@ namespace {
 constexpr int kAppendWaves = 4;
 constexpr int kBoundsThreads = 256;
 constexpr int kBoundsWaves = kBoundsThreads / kWave;
+constexpr int kBoundsBits = 64;  // pages per thread held as a bit word
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -155,6 +156,8 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
 // its chunk.
 __global__ __launch_bounds__(kBoundsThreads) void split_bounds_kernel(BoundsParams p) {
   __shared__ int s_wave[kBoundsWaves];
+  __shared__ int s_base[kBoundsThreads];        // first kept ordinal of each chunk
+  __shared__ uint64_t s_bits[kBoundsThreads];   // kept flags of each chunk (packed rows)
   const int s = blockIdx.x / p.Hkv;
   const int kvh = blockIdx.x - s * p.Hkv;
   const int tid = threadIdx.x;
@@ -168,8 +171,23 @@ __global__ __launch_bounds__(kBoundsThreads) void split_bounds_kernel(BoundsPara
   const int per = (n + kBoundsThreads - 1) / kBoundsThreads;
   const int c0 = min(n, tid * per);
   const int c1 = min(n, c0 + per);
+  // Chunks of up to 64 pages (rows of up to 16384 pages): the chunk's kept
+  // flags as one bit word, read with 64 independent loads issued together
+  // (clamped to the row, so every load is in bounds) instead of one
+  // dependent load per page; longer rows walk the mask page by page.
+  const bool packed = per <= kBoundsBits;
+  uint64_t bits = 0;
+  if (packed && n > 0) {
+    uint8_t v[kBoundsBits];
+#pragma unroll
+    for (int u = 0; u < kBoundsBits; ++u) v[u] = mrow == nullptr ? 1 : mrow[min(c0 + u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kBoundsBits; ++u) bits |= (c0 + u < c1 && v[u] != 0) ? 1ull << u : 0ull;
+  }
   int cnt = 0;
-  for (int lp = c0; lp < c1; ++lp) cnt += (mrow == nullptr || mrow[lp] != 0) ? 1 : 0;
+  if (packed) cnt = __popcll(bits);
+  else
+    for (int lp = c0; lp < c1; ++lp) cnt += (mrow == nullptr || mrow[lp] != 0) ? 1 : 0;
   int incl = cnt;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -192,7 +210,30 @@ __global__ __launch_bounds__(kBoundsThreads) void split_bounds_kernel(BoundsPara
     if (K == 0)
       for (int j = 1; j < b; ++j) out[j] = E;
   }
-  if (K == 0 || cnt == 0) return;
+  if (K == 0) return;
+  if (packed) {
+    // bound j (1 <= j < b) starts at the kept page of ordinal floor(j K / b):
+    // one thread per bound finds the chunk holding that ordinal (binary
+    // search over the chunks' first ordinals) and the page within it (the
+    // matching set bit), one division per bound
+    s_base[tid] = base;
+    s_bits[tid] = bits;
+    __syncthreads();
+    for (int j = 1 + tid; j < b; j += kBoundsThreads) {
+      const int t = (int)(((long long)j * K) / b);
+      int lo = 0, hi = kBoundsThreads - 1;  // the last chunk whose first ordinal <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (s_base[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      uint64_t w = s_bits[lo];
+      for (int r = t - s_base[lo]; r > 0; --r) w &= w - 1;  // drop the lower set bits
+      out[j] = (lo * per + __builtin_ctzll(w)) * p.P;
+    }
+    return;
+  }
+  if (cnt == 0) return;
   int o = base;
   for (int lp = c0; lp < c1; ++lp) {
     if (mrow != nullptr && mrow[lp] == 0) continue;

@@ -103,10 +103,13 @@ def test_append_matches_oracle(name, flags_kind):
 
 @pytest.mark.parametrize("b_splits", [1, 3, 16, 40])
 @pytest.mark.parametrize("kind", ["random", "sparse", "empty", "dense_none"])
-def test_split_bounds_matches_oracle(kind, b_splits):
-    announce("split bounds", kind, b_splits)
+@pytest.mark.parametrize("max_pages", [300, 8193, 20000])
+def test_split_bounds_matches_oracle(kind, b_splits, max_pages):
+    """Rows of 300 and 8193 pages (each thread's pages read as one bit
+    word) and 20000 pages (more than 64 per thread: read page by page)."""
+    announce("split bounds", kind, b_splits, max_pages)
     rng = np.random.default_rng(100 + b_splits)
-    S, Hkv, P, max_pages = 4, 3, 16, 300
+    S, Hkv, P = 4, 3, 16
     lens = np.array([max_pages * P, 1, 4000, 0], dtype=np.int32)
     if kind == "random":
         mask = (rng.random((S, Hkv, max_pages)) < 0.5).astype(np.uint8)
