@@ -151,9 +151,11 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
 // One workgroup per (request, KV head).  Pages [0, n) with n = ceil(E / P),
 // E = min(L + horizon, capacity), are split into contiguous per-thread
 // chunks (thread order = page order); a block-wide exclusive scan of the
-// per-chunk kept counts gives each chunk the ordinal of its first kept page,
-// and every thread writes the bounds whose ordinal floor(j K / b) falls in
-// its chunk.
+// per-chunk kept counts gives each chunk the ordinal of its first kept page.
+// Bound j starts at the kept page of ordinal floor(j K / b): with up to 64
+// pages per thread one thread per bound locates that page (chunk by binary
+// search, page by the chunk's bit word); longer rows let every thread write
+// the bounds whose ordinal falls in its chunk.
 __global__ __launch_bounds__(kBoundsThreads) void split_bounds_kernel(BoundsParams p) {
   __shared__ int s_wave[kBoundsWaves];
   __shared__ int s_base[kBoundsThreads];        // first kept ordinal of each chunk
