@@ -66,11 +66,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="C4", help="headline workload (C2, C3, C4, C5)")
-    ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8",
+    ap.add_argument("--workload", default="C4", help="headline workload (C1..C5)")
+    ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8,C1,C2,C3",
                     help="comma list reported beside it ('_fp8': over 8-bit pages), or ''")
+    ap.add_argument("--seed", default="0",
+                    help="seed(s) of the synthetic inputs, comma list; one record per (workload, seed)")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps per workload before the warm-up steps")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB written between the timed steps of workloads that fit in the caches' reach")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: one per core this process may run on)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--chunks", type=int, default=3,
                     help="timed 16-step chunks of the decode loop with a reused selection")
@@ -79,10 +86,38 @@ def parse():
     return ap.parse_args()
 
 
-def time_workload(key, steps, warmup, dev):
+# Workloads whose pools are small enough that the last-level caches could
+# keep part of them between steps: timed with a cache flush between steps
+# (outside the timed region) and reported as the median step.
+FLUSHED = {"C1", "C2", "C3"}
+
+
+def _settle(step, seconds):
+    """Untimed steps for `seconds`: the GPU's clocks and the pools' address
+    translations reach their steady state under sustained load (the first
+    ~0.3 s of a fresh process measured 3-5% slower)."""
+    import torch
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
+def _median(x):
+    s = sorted(x)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     """Times the decode step of workload `key`; a "_fp8" suffix runs it over
     8-bit pages made from the workload's bf16 pools by da_quantize_rows
-    (quantization is untimed: it belongs to the cache write)."""
+    (quantization is untimed: it belongs to the cache write).  With
+    flush_mib > 0 a buffer of that size is overwritten before every timed
+    step (outside the events) and the step time is the median; otherwise the
+    steps run back to back and the step time is their mean."""
     import torch
 
     from long_context_decode_microattention_amd import _lib
@@ -92,9 +127,9 @@ def time_workload(key, steps, warmup, dev):
     base = key[:-4] if fp8 else key
     spec = wl.CONFIGS[base].replace(layout=wl.PREFERRED_LAYOUT.get(base, "page"))
     t0 = time.time()
-    b = wl.build(spec, 0, dev)
+    b = wl.build(spec, seed, dev)
     torch.cuda.synchronize()
-    log(f"[bench] built {key} in {time.time() - t0:.1f}s: NP={b.k_pm.shape[0]}")
+    log(f"[bench] built {key} seed {seed} in {time.time() - t0:.1f}s: NP={b.k_pm.shape[0]}")
     S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
     kept = int(b.kept_tokens().sum())
     if fp8:
@@ -120,15 +155,24 @@ def time_workload(key, steps, warmup, dev):
     dst = torch.empty_like(src)
     dst.copy_(src)
     del src, dst
+    flush = None
+    if flush_mib > 0:
+        flush = torch.empty(flush_mib << 18, dtype=torch.int32, device=dev)
 
-    for _ in range(warmup):
+    def step():
         micro(*args, scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
         _lib.merge(MA, m, e, out=out)
+
+    _settle(step, settle)
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     torch.cuda.synchronize()
     for i in range(steps):
+        if flush is not None:
+            flush.fill_(i)
         ev[3 * i].record()
         micro(*args, scale=b.scale, out=(MA, m, e), pool_layout=b.layout)
         ev[3 * i + 1].record()
@@ -137,31 +181,48 @@ def time_workload(key, steps, warmup, dev):
     torch.cuda.synchronize()
     micro_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)]
     merge_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)]
-    total_ms = ev[0].elapsed_time(ev[-1])
-    ms_step = total_ms / steps
-    avg_micro = sum(micro_ms) / steps
-    avg_merge = sum(merge_ms) / steps
+    step_ms = [ev[3 * i].elapsed_time(ev[3 * i + 2]) for i in range(steps)]
+    if flush is None:
+        ms_step = ev[0].elapsed_time(ev[-1]) / steps
+        avg_micro = sum(micro_ms) / steps
+        avg_merge = sum(merge_ms) / steps
+    else:
+        ms_step = _median(step_ms)
+        avg_micro = _median(micro_ms)
+        avg_merge = _median(merge_ms)
     assert torch.isfinite(out).all(), "non-finite output"
 
     # the same step in one launch (da_attention / da_attention_fp8), beside it
     fused = _lib.attention_fp8 if fp8 else _lib.attention
     out_f = torch.empty_like(out)
+
+    def step_fused():
+        fused(*args, scale=b.scale, out=out_f, pool_layout=b.layout)
+
     for _ in range(max(1, warmup)):
-        fused(*args, scale=b.scale, out=out_f, pool_layout=b.layout)
+        step_fused()
     torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(steps):
-        fused(*args, scale=b.scale, out=out_f, pool_layout=b.layout)
-    f1.record()
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i)
+        fev[2 * i].record()
+        step_fused()
+        fev[2 * i + 1].record()
     torch.cuda.synchronize()
-    us_fused = f0.elapsed_time(f1) * 1e3 / steps
+    if flush is None:
+        us_fused = fev[0].elapsed_time(fev[-1]) * 1e3 / steps
+    else:
+        us_fused = _median([fev[2 * i].elapsed_time(fev[2 * i + 1]) for i in range(steps)]) * 1e3
     fused_diff = float((out_f - out).abs().max())
     assert fused_diff <= 1e-4, f"one-launch step differs from the two calls by {fused_diff}"
     res = dict(
-        workload=spec.name, key=key, kv_bytes=kv_bytes, ms_per_step=ms_step,
+        workload=spec.name, key=key, seed=seed, kv_bytes=kv_bytes, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, us_micro=avg_micro * 1e3, us_merge=avg_merge * 1e3,
+        us_per_step_median=_median(step_ms) * 1e3,
         us_micro_min=min(micro_ms) * 1e3, merge_share=avg_merge / (avg_micro + avg_merge),
+        timing=(f"median of {steps} steps, {flush_mib} MiB written between steps" if flush is not None
+                else f"mean of {steps} back-to-back steps"),
         GBps=kv_bytes / (ms_step * 1e-3) / 1e9, micro_GBps=kv_bytes / (avg_micro * 1e-3) / 1e9,
         shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B,
                    kv_dtype="fp8_e4m3+f32 row scale" if fp8 else spec.dtype,
@@ -172,7 +233,8 @@ def time_workload(key, steps, warmup, dev):
         us_per_step_one_launch=us_fused, one_launch_max_abs_diff=fused_diff,
     )
     res["frac_of_peak"] = res["GBps"] / HBM_PEAK_GBPS
-    b.out = out  # the timed step's output, compared with the oracle's in cpu_baseline
+    res["roofline_frac"] = res["micro_GBps"] / HBM_PEAK_GBPS
+    b.out = out  # the timed step's output, compared with the oracle's in oracle_check
     return b, res
 
 
@@ -415,49 +477,144 @@ def read_ceiling(b):
     return nbytes / (s.elapsed_time(t) * 1e-3) / 1e9
 
 
-def cpu_baseline(b, budget_s):
-    """The fp64 oracle on a bounded sample of the same workload, one thread."""
+# ---------------------------------------------------------------------------
+# the oracle on the host's cores
+# ---------------------------------------------------------------------------
+#
+# A pool of worker processes is forked at start-up, before anything touches
+# the GPU, so the workers hold no GPU state.  For a check, the workload's K and
+# V pools are copied into memory-mapped files in shared memory; each task is
+# one (request, KV head) unit, for which a worker runs oracle.attention over
+# its query heads through the real block table and mask, gathering from the
+# mapped pools.  Every worker runs one BLAS thread: one process per core.
+
+_POOL = None
+_POOL_N = 0
+
+
+def _worker_init():
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[v] = "1"
+
+
+def _unit_task(a):
+    """One (request, KV head) unit through the fp64 oracle; returns (s, kvh,
+    out [G, D] float64, seconds)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle
+
+    t0 = time.perf_counter()
+    dt = np.dtype(a["dtype"])
+    kp = np.memmap(a["k_path"], dtype=dt, mode="r", shape=tuple(a["pool_shape"]))
+    vp = np.memmap(a["v_path"], dtype=dt, mode="r", shape=tuple(a["pool_shape"]))
+    kvh = a["kvh"]
+    if a["head_major"]:  # [Hkv, NP, P, D] -> the head's [NP, 1, P, D]
+        kv, vv = kp[kvh][:, None], vp[kvh][:, None]
+    else:
+        kv, vv = kp[:, kvh:kvh + 1], vp[:, kvh:kvh + 1]
+    mask = None if a["mask"] is None else a["mask"][None, None]
+    out = oracle.attention(a["q"][None], kv, vv, a["table"][None],
+                           np.array([a["L"]], dtype=np.int32), block_mask=mask, scale=a["scale"])
+    del kp, vp
+    return a["s"], kvh, out[0], time.perf_counter() - t0
+
+
+def start_pool(n):
+    """Fork the oracle workers (call before the GPU is touched)."""
+    global _POOL, _POOL_N
+    import multiprocessing as mp
+
+    _POOL = mp.get_context("fork").Pool(n, initializer=_worker_init)
+    _POOL_N = n
+
+
+def stop_pool():
+    global _POOL
+    if _POOL is not None:
+        _POOL.close()
+        _POOL.join()
+        _POOL = None
+
+
+def _shm_dir():
+    return "/dev/shm" if os.path.isdir("/dev/shm") else __import__("tempfile").gettempdir()
+
+
+def oracle_check(b, label, units=None, one_core_units=0):
+    """The fp64 oracle over the given (request, KV head) units of batch b
+    (all units when None) on the worker pool, compared with the timed step's
+    output b.out.  Returns the wall time on the pool's cores, the oracle's
+    effective GB/s over the same algorithmic bytes, the largest deviation of
+    the GPU output, and (one_core_units > 0) the same oracle run on one core,
+    unit after unit, over the first units."""
+    import numpy as np
+    import torch
+
     from long_context_decode_microattention_amd import workloads as wl
 
     sp = b.spec
     G = sp.G
-    lens = b.seq_lens.cpu().numpy()
+    h = wl.host
     kept = b.kept_tokens()
-    units = [(s, kvh) for s in range(sp.S) for kvh in range(sp.Hkv)]
-    done_bytes, secs, n, err = 0, 0.0, 0, 0.0
-    with threadpool_limits(limits=1):
+    lens = b.seq_lens.cpu().numpy()
+    table = b.block_table.cpu().numpy()
+    mask = None if b.block_mask is None else b.block_mask.cpu().numpy()
+    q = h(b.q)
+    got_all = b.out.double().cpu().numpy()
+    if units is None:
+        units = [(s, kvh) for s in range(sp.S) for kvh in range(sp.Hkv)]
+    # the pools into shared memory (untimed: a copy of the workload's input)
+    tag = f"da_bench_{os.getpid()}_{label.replace('/', '_')}"
+    kpath = os.path.join(_shm_dir(), tag + "_k")
+    vpath = os.path.join(_shm_dir(), tag + "_v")
+    npdt = np.uint16 if b.k_pages.dtype == torch.bfloat16 else np.float32
+    shape = tuple(b.k_pages.shape)
+    try:
+        for src, path in ((b.k_pages, kpath), (b.v_pages, vpath)):
+            mm = np.memmap(path, dtype=npdt, mode="w+", shape=shape)
+            dst = torch.from_numpy(mm.view(np.int16) if npdt == np.uint16 else mm)
+            step = max(1, shape[0] // 16)
+            for i in range(0, shape[0], step):  # in slices: no host copy of the whole pool
+                sl = src[i:i + step]
+                dst[i:i + step].copy_(sl.view(torch.int16) if npdt == np.uint16 else sl)
+            mm.flush()
+            del mm, dst
+        tasks = []
         for s, kvh in units:
             L = int(lens[s])
             npg = -(-L // sp.P)
-            pages = b.block_table[s, :npg].long()
-            h = wl.host
-            k = h(b.k_pm[:, kvh:kvh + 1].index_select(0, pages).contiguous())
-            v = h(b.v_pm[:, kvh:kvh + 1].index_select(0, pages).contiguous())
-            q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
-            mask = None
-            if b.block_mask is not None:
-                mask = h(b.block_mask[s:s + 1, kvh:kvh + 1, :npg].contiguous())
-            table = np.arange(npg, dtype=np.int32)[None, :]
-            t0 = time.perf_counter()
-            want = oracle.attention(q, k, v, table, np.array([L], dtype=np.int32), block_mask=mask,
-                                    scale=b.scale)
-            secs += time.perf_counter() - t0
-            got = b.out[s:s + 1, kvh * G:(kvh + 1) * G].double().cpu().numpy()
-            err = max(err, float(np.max(np.abs(got - want))))
-            done_bytes += int(kept[s, kvh]) * 2 * sp.D * sp.esize
-            n += 1
-            if secs >= budget_s:
-                break
+            tasks.append(dict(
+                s=s, kvh=kvh, k_path=kpath, v_path=vpath, pool_shape=shape, dtype=np.dtype(npdt).str,
+                head_major=b.layout == "head", q=q[s, kvh * G:(kvh + 1) * G].copy(),
+                table=table[s, :max(npg, 1)].copy(), L=L,
+                mask=None if mask is None else mask[s, kvh, :max(npg, 1)].copy(), scale=b.scale))
+        order = sorted(range(len(tasks)), key=lambda i: -int(kept[tasks[i]["s"], tasks[i]["kvh"]]))
+        t0 = time.perf_counter()
+        results = _POOL.map(_unit_task, [tasks[i] for i in order], chunksize=1)
+        wall = time.perf_counter() - t0
+        one = None
+        if one_core_units > 0:
+            secs, nb = 0.0, 0
+            for tsk in tasks[:one_core_units]:
+                _, _, _, sec = _POOL.apply(_unit_task, (tsk,))
+                secs += sec
+                nb += int(kept[tsk["s"], tsk["kvh"]]) * 2 * sp.D * sp.esize
+            one = dict(value=nb / secs / 1e9, unit="GB/s", cores=1, seconds=round(secs, 3),
+                       units=f"{min(one_core_units, len(tasks))} (request, KV head) unit(s)")
+    finally:
+        for path in (kpath, vpath):
+            if os.path.exists(path):
+                os.remove(path)
+    err = 0.0
+    for s, kvh, want, _ in results:
+        got = got_all[s, kvh * G:(kvh + 1) * G]
+        err = max(err, float(np.max(np.abs(got - want))))
+    nbytes = sum(int(kept[s, kvh]) for s, kvh in units) * 2 * sp.D * sp.esize
     tol = 1e-5 if sp.dtype == wl.F32 else 2e-3
-    assert err <= tol, f"timed step differs from the oracle on the sample by {err:.3e} (> {tol})"
-    return dict(value=done_bytes / secs / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{sp.name}: {n} (request, KV head) unit(s), {done_bytes / 2**30:.2f} GiB of "
-                       f"K+V, fp64 numpy oracle.attention, BLAS limited to 1 thread, {secs:.1f} s",
-                max_abs_err_vs_step=err, tolerance=tol)
+    assert err <= tol, f"{label}: timed step differs from the oracle by {err:.3e} (> {tol})"
+    return dict(units=f"{len(units)}/{sp.S * sp.Hkv}", workers=_POOL_N, wall_s=round(wall, 3),
+                GBps=nbytes / wall / 1e9, max_abs_err_vs_step=err, tolerance=tol, one_core=one)
 
 
 def main():
@@ -466,6 +623,22 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               f"(the path is single-GPU; multi-GPU sharding is a design note, not built)", file=sys.stderr)
         sys.exit(2)
+    seeds = [int(x) for x in str(a.seed).split(",") if x != ""]
+    cores = a.cpu_workers or len(os.sched_getaffinity(0))
+    if not a.no_cpu_baseline:
+        start_pool(cores)  # before the GPU is touched
+    try:
+        line = run(a, seeds)
+    finally:
+        stop_pool()
+    print(json.dumps(line), flush=True)
+
+
+def _rounded(r):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+
+
+def run(a, seeds):
     import torch
 
     dev = torch.device("cuda:0")
@@ -473,30 +646,55 @@ def main():
     from long_context_decode_microattention_amd import _lib
 
     _lib.load()
+    check = not a.no_cpu_baseline
 
-    b, head = time_workload(a.workload, a.steps, a.warmup, dev)
-    bf16_pools = b.k_pages is not None  # an "_fp8" headline keeps only the 8-bit pools
-    ceiling = None if a.no_ceiling or not bf16_pools else read_ceiling(b)
-    cpu = None if a.no_cpu_baseline or not bf16_pools else cpu_baseline(b, a.cpu_budget)
-    head_selector = None
-    if b.spec.mask is not None and not a.no_selector and bf16_pools:
-        head_selector = time_selector(b, a.steps, a.warmup, dev)
-        head_selector["decode_loop"] = time_decode_chunks(b, a.chunks, dev)
-    del b
-    torch.cuda.empty_cache()
+    def flush_for(key):
+        return a.flush_mib if key.split("_")[0] in FLUSHED else 0
+
+    head, cpu, ceiling, head_selector = None, None, None, None
+    records = []
+    for seed in seeds:
+        b, r = time_workload(a.workload, a.steps, a.warmup, dev, seed, a.settle, flush_for(a.workload))
+        bf16_pools = b.k_pages is not None  # an "_fp8" headline keeps only the 8-bit pools
+        if check and bf16_pools:
+            oc = oracle_check(b, f"{a.workload}/{seed}", one_core_units=2)
+            r["oracle_check"] = oc
+        records.append(r)
+        if head is None:
+            head = r
+            ceiling = None if a.no_ceiling or not bf16_pools else read_ceiling(b)
+            if check and bf16_pools:
+                cpu = dict(value=oc["GBps"], unit="GB/s", cores=oc["workers"], kind="oracle",
+                           sample=(f"{sp_key(b.spec)} (all {oc['units']} (request, KV head) units, "
+                                   f"{r['kv_bytes'] / 2**30:.2f} GiB of K+V): fp64 numpy "
+                                   f"oracle.attention, one process per core, {oc['wall_s']:.1f} s wall"),
+                           wall_s=oc["wall_s"], units=oc["units"], one_core=oc["one_core"],
+                           max_abs_err_vs_step=oc["max_abs_err_vs_step"], tolerance=oc["tolerance"])
+            if b.spec.mask is not None and not a.no_selector and bf16_pools:
+                head_selector = time_selector(b, a.steps, a.warmup, dev)
+                head_selector["decode_loop"] = time_decode_chunks(b, a.chunks, dev)
+        del b
+        torch.cuda.empty_cache()
     secondary = {}
     for key in [k for k in a.secondary.split(",") if k and k != a.workload]:
-        b2, r2 = time_workload(key, a.steps, a.warmup, dev)
-        r2["roofline_frac"] = r2["micro_GBps"] / HBM_PEAK_GBPS
-        r2["traffic"] = measured_traffic(key)
-        secondary[key] = r2
-        if b2.spec.mask is not None and not a.no_selector and b2.k_pages is not None:
-            secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
-            secondary[key + "_selector"]["decode_loop"] = time_decode_chunks(b2, a.chunks, dev)
-        del b2
-        torch.cuda.empty_cache()
+        for seed in seeds:
+            b2, r2 = time_workload(key, a.steps, a.warmup, dev, seed, a.settle, flush_for(key))
+            r2["traffic"] = measured_traffic(key) if seed == 0 else None
+            if check and b2.k_pages is not None:
+                base = key.split("_")[0]
+                r2["oracle_check"] = oracle_check(b2, f"{key}/{seed}",
+                                                  one_core_units=(10**9 if base in ("C1", "C2") else 0))
+            records.append(r2)
+            if seed == seeds[0]:
+                secondary[key] = r2
+                if b2.spec.mask is not None and not a.no_selector and b2.k_pages is not None:
+                    secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
+                    secondary[key + "_selector"]["decode_loop"] = time_decode_chunks(b2, a.chunks, dev)
+            del b2
+            torch.cuda.empty_cache()
 
-    line = {
+    kv = head["shape"]["kv_dtype"]
+    return {
         "metric": METRIC,
         "value": round(head["GBps"], 2),
         "unit": "GB/s",
@@ -507,11 +705,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if kv == "bf16" else ("f32" if kv == "f32" else "fp8"),
         "data": "synthetic",
-        "config": {"workload": head["workload"], **head["shape"], "seed": 0,
-                   "kv_bytes_per_step": head["kv_bytes"]},
+        "config": {"workload": head["workload"], **head["shape"], "accum_dtype": "f32",
+                   "seed": seeds[0], "kv_bytes_per_step": head["kv_bytes"]},
         "us_per_step": round(head["us_per_step"], 2),
+        "us_per_step_median": round(head["us_per_step_median"], 2),
         "frac_of_hbm_peak": round(head["frac_of_peak"], 4),
         "roofline": {
             "bound": "hbm",
@@ -529,12 +728,16 @@ def main():
         "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "frac_of_read_ceiling": None if ceiling is None else round(head["GBps"] / ceiling, 4),
         "cpu_baseline": cpu,
-        "selector": None if head_selector is None else
-        {k: (round(v, 4) if isinstance(v, float) else v) for k, v in head_selector.items()},
-        "secondary": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
-                      for k, r in secondary.items()},
+        "selector": None if head_selector is None else _rounded(head_selector),
+        "secondary": {k: _rounded(r) for k, r in secondary.items()},
+        "records": [dict(workload=r["key"], seed=r["seed"], us_per_step=round(r["us_per_step"], 2),
+                         GBps=round(r["GBps"], 1), frac_of_peak=round(r["frac_of_peak"], 4),
+                         roofline_frac=round(r["roofline_frac"], 4), timing=r["timing"],
+                         us_per_step_one_launch=round(r["us_per_step_one_launch"], 2),
+                         oracle_max_abs_err=(None if "oracle_check" not in r
+                                             else r["oracle_check"]["max_abs_err_vs_step"]))
+                    for r in records],
     }
-    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

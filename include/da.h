@@ -99,6 +99,10 @@ typedef struct da_shape {
                            /* work queue in the workspace                      */
   int32_t pool_layout;     /* da_pool_layout of the K / V pools (and fp8 scale  */
                            /* arrays); read by every call that takes them      */
+  int32_t fuse;            /* read by da_attention* only: 0 library choice;    */
+                           /* 1 one launch (each group merged by the item that */
+                           /* completes it); 2 two launches (partials into the */
+                           /* workspace, then the merge kernel)                */
 } da_shape;
 
 /*
@@ -206,7 +210,9 @@ da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x
  * the statistics of the receiving logical page are kept current from the
  * full-precision key row exactly as da_append_kv does (select_heads and
  * logical as there), so page selection keeps working on 8-bit pools.  Reads
- * sh->S, Hkv, D, P, NP, max_pages, dtype.  Supported: D 64 or 128.
+ * sh->S, Hkv, D, P, NP, max_pages, dtype.  Supported: D 64 or 128.  As for
+ * da_append_kv, a block-table entry outside [0, NP) for the receiving page
+ * writes nothing for that request.
  */
 da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
@@ -233,7 +239,14 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
  * section 方法细节: local MicroAttention per sub-block, then the aggregation
  * equations), i.e. da_micro_attention followed by da_merge, with the merge
  * done by the work item that completes the last partial of each (request,
- * KV head) instead of by a second kernel.
+ * KV head) instead of by a second kernel.  sh->fuse picks the form: 1 that
+ * one launch; 2 two launches (the partials of every piece into the
+ * workspace, then the merge kernel over them); 0 the library's choice per
+ * shape: one launch when the grid is one round of workgroups, when it runs
+ * persistently on the work queue, or for grouped query heads with at most
+ * 128 partials per (request, head); two launches otherwise (the shapes where
+ * each was measured faster).  Either form gives the same result within fp32
+ * rounding.
  *
  *   Inputs as for da_micro_attention (da_attention_fp8: as for
  *   da_micro_attention_fp8).
@@ -397,7 +410,10 @@ da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t
  *
  * Reads sh->S, Hkv, D, P, NP, max_pages, dtype.  Supported: dtype F32 or
  * BF16, D 64 or 128 (statistics: as for da_page_stats).  Two requests must
- * not append into the same physical page in one call.
+ * not append into the same physical page in one call.  The block-table entry
+ * of the receiving page (logical page t / P, which da_check_inputs does not
+ * cover when t is a multiple of P) is checked on the device: an entry outside
+ * [0, NP) writes nothing for that request.
  */
 da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
                        const int32_t* block_table, const int32_t* seq_lens, void* k_pages,

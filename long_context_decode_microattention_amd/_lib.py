@@ -42,6 +42,7 @@ class DaShape(ctypes.Structure):
         ("chunks", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
         ("pool_layout", ctypes.c_int32),
+        ("fuse", ctypes.c_int32),
     ]
 
 
@@ -426,9 +427,10 @@ def _fused_workspace(device: torch.device, sh: DaShape, workspace) -> torch.Tens
 
 def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
               *, scale: Optional[float] = None, out=None, chunks: int = 0, schedule: int = 0,
-              workspace: Optional[torch.Tensor] = None, pool_layout: str = "page"):
-    """One decode step in one launch via da_attention: MicroAttention partials
-    and their merge into out [S, Hq, D] float32.  workspace: None uses a
+              workspace: Optional[torch.Tensor] = None, pool_layout: str = "page", fuse: int = 0):
+    """One decode step via da_attention: MicroAttention partials and their
+    merge into out [S, Hq, D] float32, in one launch or two (fuse: 0 the
+    library's choice, 1 one launch, 2 two).  workspace: None uses a
     cached per-device one (replaced by a later call with a larger shape, so
     a HIP graph must be captured with a workspace of its own); a caller's
     own must have been zero-filled once (see da_attention) and must not be
@@ -436,6 +438,7 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
     dev = q.device
     sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
                      chunks, schedule, pool_layout)
+    sh.fuse = int(fuse)
     out = _step_out(sh, out, dev)
     ws = _fused_workspace(dev, sh, workspace)
     _check(load().da_attention(
@@ -447,12 +450,13 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
 def attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, split_bounds,
                   block_mask=None, *, scale: Optional[float] = None, out=None, chunks: int = 0,
                   schedule: int = 0, workspace: Optional[torch.Tensor] = None,
-                  pool_layout: str = "page"):
-    """One decode step over 8-bit pages in one launch via da_attention_fp8
-    (inputs as micro_attention_fp8, output and workspace as attention)."""
+                  pool_layout: str = "page", fuse: int = 0):
+    """One decode step over 8-bit pages via da_attention_fp8 (inputs as
+    micro_attention_fp8, output, workspace and fuse as attention)."""
     dev = q.device
     sh = _paged_args(q, k_codes, v_codes, block_table, seq_lens, split_bounds, block_mask, scale,
                      chunks, schedule, pool_layout, k_scales, v_scales)
+    sh.fuse = int(fuse)
     out = _step_out(sh, out, dev)
     ws = _fused_workspace(dev, sh, workspace)
     _check(load().da_attention_fp8(

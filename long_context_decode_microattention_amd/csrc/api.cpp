@@ -66,6 +66,8 @@ da_status check_shape(const da_shape* sh, bool fp8 = false) {
   if (sh->chunks < 0 || sh->chunks > kMaxChunks)
     return fail(DA_ERR_INVALID_ARG, "chunks must be 0 (library choice) or 1..%d (got %d)",
                 kMaxChunks, sh->chunks);
+  if (sh->fuse < 0 || sh->fuse > 2)
+    return fail(DA_ERR_INVALID_ARG, "fuse must be 0, 1 or 2 (got %d)", sh->fuse);
   return DA_OK;
 }
 
@@ -114,6 +116,17 @@ int resolve_chunks(const da_shape* sh) {
   if (c > kAutoMaxChunks) c = kAutoMaxChunks;
   if (c > pages_per_split) c = pages_per_split;
   return c < 1 ? 1 : (int)c;
+}
+
+// Target kept pages per piece: a typical split (the table width over the
+// split count) cut into `chunks`; a split with K kept pages is cut into
+// about K / T pieces (at most `chunks`), so the splits of block-sparse heads
+// are cut less than those of dense heads.
+int piece_pages(const da_shape* sh, int chunks) {
+  long long per_split = sh->max_pages / sh->max_splits;
+  if (per_split < 1) per_split = 1;
+  const long long T = (per_split + chunks - 1) / chunks;
+  return T < 1 ? 1 : (int)T;
 }
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -195,10 +208,6 @@ da::SelectorParams selector_params(const da_shape* sh, int logical) {
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
 // D, P and group size among the MicroAttention kernels built.
@@ -279,7 +288,9 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.e = in_ws ? reinterpret_cast<float*>(wsb + ws.e) : e;
   p.group_count = fused ? reinterpret_cast<int*>(wsb) : nullptr;
   p.out = out;
+  p.fuse = sh->fuse;
   p.chunks = chunks;
+  p.piece_pages = piece_pages(sh, chunks);
   p.n_items = sh->S * sh->Hkv * sh->max_splits * chunks;
   p.grab = 1;
   p.schedule = sh->schedule;

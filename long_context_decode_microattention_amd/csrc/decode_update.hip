@@ -72,6 +72,10 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_kernel(AppendP
   const int lp = t / p.P;
   const int slot = t - lp * p.P;
   const long long phys = p.table[(size_t)s * p.max_pages + lp];
+  // the entry of the page that receives the token lies outside the range
+  // da_check_inputs validates when L_s is a multiple of P: an entry outside
+  // the pool writes nothing (wave-uniform)
+  if (phys < 0 || phys >= p.NP) return;
   const bool stats = p.stats != nullptr && (p.select == nullptr || p.select[kvh] != 0);
   const int parts = stats ? 4 : 2;
   const size_t new_off = ((size_t)s * p.Hkv + kvh) * RB;
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
   const int lp = t / p.P;
   const int slot = t - lp * p.P;
   const long long phys = p.table[(size_t)s * p.max_pages + lp];
+  if (phys < 0 || phys >= p.NP) return;  // entry outside the pool: nothing is written
   const int lane = threadIdx.x % kWave;
   const int part = lane / LPR;  // 0 = key row, 1 = value row, else idle
   const int col = lane % LPR;

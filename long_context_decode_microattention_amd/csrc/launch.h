@@ -22,7 +22,8 @@ struct MicroParams {
   float* m;   // else one partial per chunk (workspace), folded by launch_combine
   float* e;
   int S, Hq, Hkv, P, max_pages, max_splits, bounds_per_head;
-  int chunks;  // page-range pieces per split, >= 1
+  int chunks;       // pieces per split, >= 1 (plan_piece)
+  int piece_pages;  // T: target kept pages per piece, >= 1
   float scale;
   long long NP;     // pages in the pools
   int head_major;   // 0: pools [NP, Hkv, P, D] (scales [NP, Hkv, P]); 1: [Hkv, NP, P, D] ([Hkv, NP, P])
@@ -40,6 +41,7 @@ struct MicroParams {
   // group_count == null: partials only.
   int* group_count;
   float* out;
+  int fuse;  // with group_count: 0 launcher's choice, 1 one launch, 2 plain kernel + merge kernel
 };
 
 // Returns hipErrorInvalidValue for a (dtype, D, G) combination that is not

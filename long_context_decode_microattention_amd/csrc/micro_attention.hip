@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
       for (int k = 0; k < L::EPL; ++k) acc[g][k] = 0.f;
     }
 
-    if (it.scan0 < it.scan1) {
+    const Piece pc = plan_piece(p, it, s_cnt);
+    if (pc.o0 < pc.o1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       // slabs per page: P is a power of two, so slab sl is slab (sl & (spp - 1))
       // of kept page (sl >> spp_log)
@@ -129,8 +130,12 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
       const float* ksb = DT == 2 ? p.ks + head_row + row : nullptr;
       const float* vsb = DT == 2 ? p.vs + head_row + row : nullptr;
 
-      for (int base = it.scan0; base < it.scan1; base += kPageCap) {
-        const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
+      // resume point of the page scan: without a mask, ordinal = page - pa
+      int rlp = it.mrow ? it.pa : it.pa + pc.o0;
+      int rord = it.mrow ? 0 : pc.o0;
+      for (int w0 = pc.o0; w0 < pc.o1; w0 += kPageCap) {
+        const int nk = compact_window(rlp, rord, it.pb, w0, min(pc.o1, w0 + kPageCap), it.mrow,
+                                      trow, s_phys, s_lp, s_cnt);
 
         // ---- stream the piece's slabs: wave w takes slabs w, w+4, ... ----
         const int nslab = nk * spp;
@@ -363,9 +368,8 @@ constexpr int kValuWorkgroupsPerCU = 0;
 
 template <int DT, int D, int G, int SL = kSlab>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  if (p.group_count != nullptr)
-    return launch_micro_kernel(micro_kernel<DT, D, G, SL, true>, kValuWorkgroupsPerCU, p, stream);
-  return launch_micro_kernel(micro_kernel<DT, D, G, SL, false>, kValuWorkgroupsPerCU, p, stream);
+  return launch_micro_step<D>(micro_kernel<DT, D, G, SL, false>, micro_kernel<DT, D, G, SL, true>,
+                              kValuWorkgroupsPerCU, p, stream);
 }
 
 template <int DT, int D>

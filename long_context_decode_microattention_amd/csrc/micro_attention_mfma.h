@@ -164,7 +164,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   #pragma unroll
       for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (it.scan0 < it.scan1) {
+    const Piece pc = plan_piece(p, it, s_cnt);
+    if (pc.o0 < pc.o1) {
       const int32_t* trow = p.table + (size_t)s * p.max_pages;
       // slabs per page: P is a power of two, so slab sl is slab (sl & (spp - 1))
       // of kept page (sl >> spp_log)
@@ -184,8 +185,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       const float* ksb = DT == 2 ? p.ks + head_row + col : nullptr;
       const float* vsb = DT == 2 ? p.vs + head_row + col : nullptr;
 
-      for (int base = it.scan0; base < it.scan1; base += kPageCap) {
-        const int nk = compact_pages(base, it.scan1, it.mrow, trow, s_phys, s_lp, s_cnt);
+      // resume point of the page scan: without a mask, ordinal = page - pa
+      int rlp = it.mrow ? it.pa : it.pa + pc.o0;
+      int rord = it.mrow ? 0 : pc.o0;
+      for (int w0 = pc.o0; w0 < pc.o1; w0 += kPageCap) {
+        const int nk = compact_window(rlp, rord, it.pb, w0, min(pc.o1, w0 + kPageCap), it.mrow,
+                                      trow, s_phys, s_lp, s_cnt);
         const int nslab = nk * spp;
 
         // key load j of a lane: bf16 64*j (one score step), fp8 16*j (two steps)
@@ -466,9 +471,8 @@ constexpr int kMfmaWorkgroupsPerCU = 2;
 
 template <int DT, int D, int G, int SL>
 hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  if (p.group_count != nullptr)
-    return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL, true>, kMfmaWorkgroupsPerCU, p, stream);
-  return launch_micro_kernel(micro_mfma_kernel<DT, D, G, SL, false>, kMfmaWorkgroupsPerCU, p, stream);
+  return launch_micro_step<D>(micro_mfma_kernel<DT, D, G, SL, false>,
+                              micro_mfma_kernel<DT, D, G, SL, true>, kMfmaWorkgroupsPerCU, p, stream);
 }
 
 // bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups

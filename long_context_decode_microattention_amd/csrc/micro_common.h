@@ -1,6 +1,7 @@
 // Pieces shared by the MicroAttention kernels: work-item decoding (with the
-// optional cut of a split into page-range chunks), kept-page compaction into
-// LDS, and the end-of-item combine of the four waves' partial triples.
+// optional cut of a split into pieces of its kept pages), kept-page
+// compaction into LDS, and the end-of-item combine of the four waves' partial
+// triples.
 #pragma once
 
 #include "device_common.h"
@@ -15,20 +16,33 @@ constexpr int kSlab = 16;       // tokens per slab
 
 // One work item: (request s, KV head kvh, split j, piece c).  A split is the
 // token range [t0, t1) (split bounds intersected with [0, L_s)) on logical
-// pages [pa, pb); piece c of `chunks` takes the logical pages
-// [scan0, scan1) = the c-th equal share of [pa, pb), and within them the
-// pages the block mask keeps.
+// pages [pa, pb); piece c takes a contiguous run of the split's kept pages
+// (plan_piece).
 struct Item {
   int s, kvh, j, c;
   int t0, t1;        // split token range (empty if t0 >= t1)
-  int scan0, scan1;  // logical pages of this piece
+  int pa, pb;        // logical pages of the split
   const uint8_t* mrow;  // block-mask row of (s, kvh), or null
 };
 
+// Items are numbered piece slowest: x = c * (S * Hkv * b) + (s * Hkv + kvh) * b
+// + j.  Every split has a non-empty first piece, and the later pieces are
+// empty for splits with few kept pages, so the non-empty items come first
+// and form one run.  Empty items scattered through the grid at a regular
+// stride (the piece numbered fastest, 4 pieces, block-sparse splits with one
+// piece) serialised the long items: the hardware hands workgroups to the 8
+// XCDs round-robin by index, and inside each XCD the long items did not fill
+// the slots the short ones left (a per-workgroup trace of XCC id and
+// real-time clock: 64 long items per XCD, 221 us each, ran in about four
+// rounds, 971 us, against 343 us for the same items numbered in one run).
+// Dense heads stream 2% slower this way than with
+// a split's pieces adjacent in the grid; the GQA batch as a whole is 1%
+// faster, and 7% faster over 8-bit pages.
 __device__ __forceinline__ Item plan_item(const MicroParams& p, int x) {
   Item it;
-  it.c = x % p.chunks;
-  x /= p.chunks;
+  const int per_piece = p.n_items / p.chunks;
+  it.c = x / per_piece;
+  x -= it.c * per_piece;
   it.j = x % p.max_splits;
   x /= p.max_splits;
   it.kvh = x % p.Hkv;
@@ -42,14 +56,58 @@ __device__ __forceinline__ Item plan_item(const MicroParams& p, int x) {
                                      (size_t)(p.max_splits + 1);
   it.t0 = max(sb[it.j], 0);
   it.t1 = min(sb[it.j + 1], Ls);
-  it.scan0 = it.scan1 = 0;
+  it.pa = it.pb = 0;
   if (it.t0 < it.t1) {
-    const int pa = it.t0 / P, pb = (it.t1 + P - 1) / P;
-    const long long n = pb - pa;
-    it.scan0 = pa + (int)((n * it.c) / p.chunks);
-    it.scan1 = pa + (int)((n * (it.c + 1)) / p.chunks);
+    it.pa = it.t0 / P;
+    it.pb = (it.t1 + P - 1) / P;
   }
   return it;
+}
+
+// Sum of an int over the 64 lanes of a wave; every lane receives it.
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// The kept pages of a piece: ordinals [o0, o1) among the split's kept pages.
+struct Piece {
+  int o0, o1;
+};
+
+// Cuts a split into pieces by its kept pages: the K kept pages of [pa, pb)
+// (mask != 0; every page without a mask) form n = clamp(round(K / T), 1, C)
+// runs of equal length, T = p.piece_pages, C = p.chunks, and piece c takes
+// run c (nothing when c >= n).  A piece's fixed cost -- the chain of
+// metadata loads before its first slab, the compaction, the end-of-item
+// combine, its partial -- is the same whatever its length, so pieces of
+// about T pages keep that cost small next to the streaming time; cutting the
+// logical range instead gives a block-sparse head's splits pieces of a
+// quarter of the dense heads' size (1 MiB against 4 MiB on the GQA batch),
+// which streamed 13% slower.  Every thread calls it (barriers inside).
+__device__ __forceinline__ Piece plan_piece(const MicroParams& p, const Item& it, int* s_cnt) {
+  Piece pc{0, 0};
+  if (it.pa >= it.pb) return pc;
+  int K = it.pb - it.pa;
+  if (it.mrow != nullptr) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int n = 0;
+    for (int lp = it.pa + (int)threadIdx.x; lp < it.pb; lp += kMicroThreads) n += it.mrow[lp] != 0;
+    n = wave_sum_int(n);
+    if (lane == 0) s_cnt[wave] = n;
+    __syncthreads();
+    K = __builtin_amdgcn_readfirstlane(s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
+    __syncthreads();  // s_cnt is reused by the compaction
+  }
+  const int T = p.piece_pages;
+  const int n = max(1, min((int)(((long long)K + T / 2) / T), p.chunks));
+  if (it.c < n) {
+    pc.o0 = (int)(((long long)K * it.c) / n);
+    pc.o1 = (int)(((long long)K * (it.c + 1)) / n);
+  }
+  return pc;
 }
 
 // The fused-merge arguments, copied to LDS once per workgroup before the
@@ -98,36 +156,51 @@ __device__ __forceinline__ void for_each_item(const MicroParams& p, int* s_claim
   }
 }
 
-// Compacts the kept pages of [base, min(base + kPageCap, lp1)) into LDS
-// (physical page ids and logical page ids, in logical order) with wave
-// ballots; returns the count.  Every thread of the workgroup must call it.
-
-__device__ __forceinline__ int compact_pages(int base, int lp1, const uint8_t* mrow,
-                                             const int32_t* trow, int* s_phys, int* s_lp,
-                                             int* s_cnt) {
+// Compacts into LDS (physical and logical page ids, in logical order) the
+// kept pages of ordinals [w0, w1) (w1 - w0 <= kPageCap) among the kept pages
+// of the logical pages [lp, pb), with wave ballots over groups of 256 pages.
+// (lp, ord) is the resume point: the group starting at logical page lp,
+// whose first kept page has ordinal ord <= w0; it is left at the group that
+// holds ordinal w1, where the next window starts.  The block-table entries
+// of a group are loaded together with its mask bytes (the two loads are not
+// chained; an entry of a masked page is read and not used).  Every thread
+// must call it; returns the number of pages stored (w1 - w0 unless the
+// split has fewer kept pages).
+__device__ __forceinline__ int compact_window(int& lp, int& ord, int pb, int w0, int w1,
+                                              const uint8_t* mrow, const int32_t* trow,
+                                              int* s_phys, int* s_lp, int* s_cnt) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  int nk = 0;
-  const int span = min(kPageCap, lp1 - base);
-  for (int r = 0; r < span; r += kMicroThreads) {
-    const int lp = base + r + tid;
-    const bool keep = lp < lp1 && (mrow == nullptr || mrow[lp] != 0);
+  int got = w0;  // ordinals below `got` (and >= w0) are stored
+  while (lp < pb) {
+    const int x = lp + tid;
+    const bool in = x < pb;
+    const int phys = in ? trow[x] : 0;
+    const bool keep = in && (mrow == nullptr || mrow[x] != 0);
     const uint64_t bal = __ballot(keep);
     const int pre = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) s_cnt[wave] = __popcll(bal);
     __syncthreads();
-    int off = nk;
+    int off = ord;
     for (int w = 0; w < wave; ++w) off += s_cnt[w];
-    if (keep) {
-      s_phys[off + pre] = trow[lp];
-      s_lp[off + pre] = lp;
+    const int gend = __builtin_amdgcn_readfirstlane(ord + s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
+    const int o = off + pre;
+    if (keep && o >= w0 && o < w1) {
+      s_phys[o - w0] = phys;
+      s_lp[o - w0] = x;
     }
-    nk += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-    __syncthreads();
+    __syncthreads();  // s_cnt is rewritten by the next group
+    if (gend > w1) {  // the group also holds pages of the next window: resume here
+      got = w1;
+      break;
+    }
+    got = max(got, gend);
+    ord = gend;
+    lp += kMicroThreads;
+    if (ord == w1) break;
   }
-  // the count is the same in every lane; saying so keeps the slab loop scalar
-  return __builtin_amdgcn_readfirstlane(nk);
+  return got - w0;
 }
 
 // LDS for the end-of-item combine.
@@ -142,6 +215,26 @@ struct FinishLds {
 // Device-scope (agent) relaxed store and load: coherent across the XCDs'
 // L2 caches by themselves, so partials written by one workgroup can be read
 // by another without cache-wide fences.
+//
+// What the fused merge relies on.  On gfx942 and gfx950 the compiler lowers
+// a monotonic agent-scope atomic store to a global_store with sc1 and a
+// monotonic agent-scope atomic load to a global_load with sc1 (the AMDGPU
+// backend's memory model for these targets): the store is made coherent
+// across the XCDs when it completes, and the load does not hit a stale
+// line in this XCD's L2.  A writer waits for its stores to complete
+// (s_waitcnt vmcnt(0)) before the barrier that precedes its counter update,
+// and the reader loads only after its own counter update returned the last
+// count, so every partial it loads completed before it was issued.  Under
+// the HIP/C++ memory model relaxed accesses to different locations are not
+// ordered by this; the formal pair (a release counter update per item, an
+// acquire fence in the last arrival) compiles to an L2 write-back per item
+// and an L2 invalidate per group and measured 1.8x (C2: 355 vs 194 us) to
+// 2.8x (C3: 2852 vs 1009 us) slower, so the kernels keep the lowering-based
+// form, and the fused instances build only for the two targets whose
+// lowering is this.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__) && !defined(__gfx942__)
+#error "the fused merge relies on the gfx942/gfx950 lowering of agent-scope atomics"
+#endif
 __device__ __forceinline__ void store_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -168,15 +261,9 @@ __device__ __forceinline__ void merge_group(const MicroParams& p, const Item& it
   const int wave = tid / kWave;
   const int n = p.max_splits * p.chunks;
   int* count = s_fused.group_count + (size_t)it.s * p.Hkv + it.kvh;
-  // The partials were written as device-scope atomic stores (sc1: made
-  // coherent across the XCDs' L2 caches by the access itself, as the
-  // compiler's memory model implements monotonic device-scope atomics) and
-  // are read back the same way; waiting until they have completed orders
-  // them before the counter.  A device-scope fence, or an acquire-release
-  // counter update, writes back and invalidates a whole L2 per item:
-  // measured 0.2-0.35 us per item with the fence in every thread, and with
-  // the acquire-release update in one thread C2 366 us against 194 us and
-  // C3 2.93 ms against 1.0 ms.
+  // The partials were written as device-scope atomic stores and are read
+  // back the same way; waiting until they have completed orders them before
+  // the counter (the rule stated at store_dev).
   wait_stores();
   __syncthreads();
   if (tid == 0) L.last = atomicAdd(count, 1) == n - 1;
@@ -391,6 +478,44 @@ constexpr long long kPersistentFactor = 8;
 // itself becomes the bottleneck; then the launch is persistent: one
 // workgroup per resident slot, each claiming items from the counter in
 // batches small enough that the tail stays short.
+template <class Kernel>
+hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipStream_t stream);
+
+// The step in one launch or two (p.group_count != null).  One launch: the
+// kernel instance with the fused merge.  Two: the plain instance writes
+// every piece's partial into p.MA / p.m / p.e (the workspace), then the merge
+// kernel folds the max_splits * chunks partials of each (request, query
+// head) -- the same aggregation rule, associative, so the pieces need no
+// separate combine.  The fused merge saves a launch and the partials' round
+// trip but makes every item count its group up, and the group's last item
+// merge alone; measured (HIP-graph replays) it wins where the grid is one
+// round of workgroups, on the persistent work queue (many short items), and
+// for grouped query heads with few partials per group, and loses on long
+// grids of short single-head items (C2: 190 vs 171 us) and on groups of
+// hundreds of partials.  fuse = 1 or 2 forces a form.
+template <int D, class KPlain, class KFused>
+hipError_t launch_micro_step(KPlain plain, KFused fused, int wg_per_cu, MicroParams p,
+                             hipStream_t stream) {
+  if (p.group_count == nullptr) return launch_micro_kernel(plain, wg_per_cu, p, stream);
+  bool one = p.fuse == 1;
+  if (p.fuse == 0) {
+    const void* fn = reinterpret_cast<const void*>(plain);
+    const int slots = resident_slots(fn, occupancy_lds(fn, wg_per_cu));
+    const bool persistent = p.queue != nullptr && slots > 0 &&
+                            (p.schedule == 2 ||
+                             (p.schedule == 0 && p.n_items > kPersistentFactor * slots));
+    const long long per_group = (long long)p.max_splits * p.chunks;
+    one = persistent || p.n_items <= slots || (p.Hq > p.Hkv && per_group <= 128);
+  }
+  if (one) return launch_micro_kernel(fused, wg_per_cu, p, stream);
+  MicroParams q = p;
+  q.group_count = nullptr;
+  q.out = nullptr;
+  const hipError_t err = launch_micro_kernel(plain, wg_per_cu, q, stream);
+  if (err != hipSuccess) return err;
+  return launch_merge(q.MA, q.m, q.e, p.out, p.S, p.Hq, D, p.max_splits * p.chunks, stream);
+}
+
 template <class Kernel>
 hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(kernel);

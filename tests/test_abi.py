@@ -103,6 +103,8 @@ def call_fused(lib, sh, **ptrs):
     (dict(ptrs=dict(ws=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),           # misaligned
     (dict(shape=dict(chunks=4), ptrs=dict(ws_bytes=1024)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(dtype=_lib.DA_FP8_E4M3)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(fuse=3)), _lib.DA_ERR_INVALID_ARG),
+    (dict(shape=dict(fuse=-1)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
     (dict(shape=dict(Hq=6, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),
 ], ids=lambda x: str(x))

@@ -61,10 +61,10 @@ def fused_workspace(b: wl.Batch, chunks: int = 0, schedule: int = 0):
     return torch.zeros(nbytes, dtype=torch.uint8, device=DEV), counters
 
 
-def fused(b: wl.Batch, ws=None, chunks: int = 0, schedule: int = 0):
+def fused(b: wl.Batch, ws=None, chunks: int = 0, schedule: int = 0, fuse: int = 0):
     out = _lib.attention(b.q, b.k_pages, b.v_pages, b.block_table, b.seq_lens, b.split_bounds,
                          b.block_mask, scale=b.scale, chunks=chunks, schedule=schedule,
-                         workspace=ws, pool_layout=b.layout)
+                         workspace=ws, pool_layout=b.layout, fuse=fuse)
     torch.cuda.synchronize()
     return out
 
@@ -82,14 +82,17 @@ def max_abs(a: torch.Tensor, b: torch.Tensor) -> float:
     return float((a.double() - b.double()).abs().max())
 
 
+@pytest.mark.parametrize("fuse", [0, 1, 2])
 @pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("cfg", sorted(REDUCED))
-def test_fused_matches_oracle_and_two_call_path(cfg, seed):
+def test_fused_matches_oracle_and_two_call_path(cfg, seed, fuse):
+    """fuse 1: the merge in the same launch; 2: partials then the merge
+    kernel; 0: the library's choice between them."""
     spec = REDUCED[cfg].replace(layout=wl.PREFERRED_LAYOUT.get(cfg, "page"))
-    announce("fused", cfg, "seed", seed)
+    announce("fused", cfg, "seed", seed, "fuse", fuse)
     b = wl.build(spec, seed, DEV)
     ws, counters = fused_workspace(b)
-    out = fused(b, ws)
+    out = fused(b, ws, fuse=fuse)
     compare_out(out.cpu().numpy(), oracle_out(host_inputs(b), b.scale), TOL_OUT[spec.dtype],
                 f"fused {cfg}/{seed}")
     ref = two_call(b)
@@ -97,21 +100,22 @@ def test_fused_matches_oracle_and_two_call_path(cfg, seed):
     assert int(ws[:counters].count_nonzero()) == 0, "group counters not cleared"
 
 
+@pytest.mark.parametrize("fuse", [1, 2])
 @pytest.mark.parametrize("schedule,chunks", [(1, 0), (2, 0), (1, 1), (1, 3), (2, 3), (1, 7),
                                              (2, 16), (1, 40)])
 @pytest.mark.parametrize("cfg", ["C1", "C3", "C5"])
-def test_fused_schedules_and_chunks(cfg, schedule, chunks):
+def test_fused_schedules_and_chunks(cfg, schedule, chunks, fuse):
     """One workgroup per item and persistent workgroups on the work queue,
-    with forced chunk counts: the merge runs over every chunk partial (40
-    chunks: more than 2 D partials per head, the merge's head-by-head
-    branch)."""
+    with forced chunk counts, in one launch (the merge runs over every piece
+    partial; 40 pieces: more than 2 D partials per head, the merge's
+    head-by-head branch) and in two (the merge kernel over them)."""
     spec = REDUCED[cfg]
-    announce("fused schedule", cfg, schedule, chunks)
+    announce("fused schedule", cfg, schedule, chunks, fuse)
     b = wl.build(spec, 5, DEV)
     ws, counters = fused_workspace(b, chunks, schedule)
-    out = fused(b, ws, chunks, schedule)
+    out = fused(b, ws, chunks, schedule, fuse)
     compare_out(out.cpu().numpy(), oracle_out(host_inputs(b), b.scale), TOL_OUT[spec.dtype],
-                f"fused {cfg} schedule={schedule} chunks={chunks}")
+                f"fused {cfg} schedule={schedule} chunks={chunks} fuse={fuse}")
     assert int(ws[:counters].count_nonzero()) == 0
 
 

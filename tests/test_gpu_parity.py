@@ -129,7 +129,7 @@ FULL_SAMPLES = {
     "C2": [(0, 0, 1), (15, 31, 32), (7, 13, 14)],
     "C3": None,  # chosen from the drawn lengths: longest, shortest, median
     "C4": [(0, 0, 1), (0, 31, 32)],
-    "C5": [(0, 0, 1), (7, 7, 8)],
+    "C5": [(0, 0, 1), (7, 7, 8), (3, 0, 8)],  # (3, 0, 8): every KV head of one request, dense and masked
 }
 
 
