@@ -437,6 +437,30 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
 da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
                           int32_t horizon, int32_t* split_bounds, hipStream_t stream);
 
+/*
+ * The decode step of da_attention for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same inputs, output, forms (sh->fuse) and
+ * results as da_attention (bf16 / fp32 pools), with no workspace argument:
+ * the counters, work queue and partials live in a device array the library
+ * holds for the life of the process, DA_NOALLOC_SCRATCH_BYTES (32 MiB) per
+ * GPU, enough for every workload of the configurations C1-C5.  The call
+ * allocates nothing and frees nothing; it clears the counters itself (a fill
+ * kernel on `stream`) before the step.  A shape whose step needs more than
+ * the array (da_attention_workspace_size, unchunked if the library's chunking
+ * does not fit) is DA_ERR_INVALID_ARG before any launch.
+ * The array is shared by every call on the same GPU and keeps the last
+ * call's contents: calls that may overlap on one GPU (different streams
+ * without ordering between them) race on it and must not be issued.
+ * Errors: as da_attention; DA_ERR_HIP also when the array's device address
+ * cannot be obtained.
+ */
+#define DA_NOALLOC_SCRATCH_BYTES (32u << 20)
+da_status da_attention_noalloc(const da_shape* sh, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* split_bounds,
+                               const uint8_t* block_mask, float* out, hipStream_t stream);
+
 /* Message for the last non-OK status returned on the calling thread
  * (thread-local; never NULL; empty if none). */
 const char* da_last_error(void);

@@ -101,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.da_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]
     lib.da_attention_fp8.restype = ctypes.c_int
+    lib.da_attention_noalloc.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.da_attention_noalloc.restype = ctypes.c_int
     lib.da_attention_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.da_attention_workspace_size.restype = ctypes.c_int
@@ -444,6 +446,24 @@ def attention(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_ma
     _check(load().da_attention(
         ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
         _ptr(split_bounds), _ptr(block_mask), _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def attention_noalloc(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask=None,
+                      *, scale: Optional[float] = None, out=None, chunks: int = 0,
+                      schedule: int = 0, pool_layout: str = "page", fuse: int = 0):
+    """The step of attention via da_attention_noalloc: no workspace, the
+    library's per-GPU scratch array instead (calls on one GPU must not
+    overlap).  out: [S, Hq, D] float32 (allocated here when None; pass one to
+    call without any allocation)."""
+    dev = q.device
+    sh = _paged_args(q, k_pages, v_pages, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout)
+    sh.fuse = int(fuse)
+    out = _step_out(sh, out, dev)
+    _check(load().da_attention_noalloc(
+        ctypes.byref(sh), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+        _ptr(split_bounds), _ptr(block_mask), _ptr(out), _stream(dev)))
     return out
 
 

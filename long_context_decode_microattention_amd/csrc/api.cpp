@@ -4,7 +4,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <hip/hip_runtime.h>
+
 #include <climits>
+#include <mutex>
 #include <string>
 
 #include "da.h"
@@ -232,7 +235,8 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* split_bounds, const uint8_t* block_mask, float* MA,
                                float* m, float* e, float* out, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               size_t workspace_bytes, hipStream_t stream,
+                               bool clear_counters = false) {
   const bool fused = out != nullptr;
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !split_bounds ||
       (!fused && (!MA || !m || !e)))
@@ -305,6 +309,11 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.scale = sh->scale;
   p.NP = sh->NP;
   p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
+  if (fused && clear_counters) {
+    const hipError_t zerr = da::launch_zero_ints(p.group_count, (long long)sh->S * sh->Hkv, stream);
+    if (zerr != hipSuccess)
+      return fail(DA_ERR_HIP, "counter clear launch failed: %s", hipGetErrorString(zerr));
+  }
   hipError_t err = da::launch_micro(sh->dtype, sh->D, sh->Hq / sh->Hkv, p, stream);
   if (err != hipSuccess)
     return fail(DA_ERR_HIP, "micro-attention launch failed: %s", hipGetErrorString(err));
@@ -389,6 +398,76 @@ da_status da_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_c
   return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
                               split_bounds, block_mask, nullptr, nullptr, nullptr, out, workspace,
                               workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of da_attention_noalloc: the counters, work queue and partials of
+// the step, in device memory the library holds from load until the process
+// ends (one copy per GPU), so that the entry point allocates nothing.  In
+// host code `scratch` is only a stand-in for the symbol: its device address
+// on each GPU comes from hipGetSymbolAddress, taken once per device.
+__device__ __align__(256) unsigned char scratch[DA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // address of `scratch` on each device, or null
+
+da_status scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(DA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DA_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return fail(DA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(err));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_attention_noalloc(const da_shape* sh, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* split_bounds,
+                               const uint8_t* block_mask, float* out, hipStream_t stream) {
+  da_status st = check_shape(sh);
+  if (st != DA_OK) return st;
+  if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  st = check_micro_built(sh);
+  if (st != DA_OK) return st;
+  // the workspace the step needs, unchunked when the library's chunking
+  // would not fit (as da_attention does with a workspace too small)
+  size_t counters = 0;
+  const int chunks = resolve_chunks(sh);
+  size_t need = ws_fused_layout(sh, chunks, &counters).total;
+  if (need > DA_NOALLOC_SCRATCH_BYTES && sh->chunks == 0)
+    need = ws_fused_layout(sh, 1, &counters).total;
+  if (need > DA_NOALLOC_SCRATCH_BYTES)
+    return fail(DA_ERR_INVALID_ARG,
+                "the step needs %zu bytes of scratch; da_attention_noalloc holds %zu (use "
+                "da_attention with a workspace)",
+                need, (size_t)DA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != DA_OK) return st;
+  // the group counters are cleared by a fill kernel before every call: an
+  // earlier call of another shape may have left partials where they lie
+  return micro_attention_impl(sh, q, k_pages, v_pages, nullptr, nullptr, block_table, seq_lens,
+                              split_bounds, block_mask, nullptr, nullptr, nullptr, out, ws,
+                              DA_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 da_status da_attention_workspace_size(const da_shape* sh, size_t* bytes, size_t* counter_bytes) {

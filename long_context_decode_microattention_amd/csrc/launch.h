@@ -59,6 +59,8 @@ bool micro_mfma_supported(int dtype, int D, int G);  // the GQA matrix-core kern
 // Zeroes the persistent-launch counter (a one-lane kernel, not a memset, so
 // it can be captured in a graph).
 hipError_t launch_queue_reset(int* queue, hipStream_t stream);
+// Zeroes n ints with a fill kernel (capturable in a graph, unlike a memset node).
+hipError_t launch_zero_ints(int* p, long long n, hipStream_t stream);
 
 hipError_t launch_combine(const float* cMA, const float* cm, const float* ce, float* MA, float* m,
                           float* e, long long n, int chunks, int D, hipStream_t stream);

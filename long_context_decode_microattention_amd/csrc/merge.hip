@@ -164,10 +164,21 @@ __global__ void queue_reset_kernel(int* queue) {
   if (threadIdx.x == 0) *queue = 0;
 }
 
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_queue_reset(int* queue, hipStream_t stream) {
   hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, stream, queue);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_ints(int* p, long long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 
