@@ -67,8 +67,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C4", help="headline workload (C1..C5)")
-    ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8,C1,C2,C3",
-                    help="comma list reported beside it ('_fp8': over 8-bit pages), or ''")
+    ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8,C4_fp4,C5_fp4,C1,C2,C3",
+                    help="comma list reported beside it ('_fp8' / '_fp4': over 8- / 4-bit "
+                         "pages), or ''")
     ap.add_argument("--seed", default="0",
                     help="seed(s) of the synthetic inputs, comma list; one record per (workload, seed)")
     ap.add_argument("--settle", type=float, default=1.0,
@@ -112,9 +113,10 @@ def _median(x):
 
 
 def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
-    """Times the decode step of workload `key`; a "_fp8" suffix runs it over
-    8-bit pages made from the workload's bf16 pools by da_quantize_rows
-    (quantization is untimed: it belongs to the cache write).  With
+    """Times the decode step of workload `key`; a "_fp8" / "_fp4" suffix runs
+    it over 8- / 4-bit pages made from the workload's bf16 pools by
+    da_quantize_rows / da_quantize_rows_fp4 (quantization is untimed: it
+    belongs to the cache write).  With
     flush_mib > 0 a buffer of that size is overwritten before every timed
     step (outside the events) and the step time is the median; otherwise the
     steps run back to back and the step time is their mean."""
@@ -123,7 +125,8 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     from long_context_decode_microattention_amd import _lib
     from long_context_decode_microattention_amd import workloads as wl
 
-    fp8 = key.endswith("_fp8")
+    bits = 8 if key.endswith("_fp8") else 4 if key.endswith("_fp4") else 16
+    fp8 = bits < 16
     base = key[:-4] if fp8 else key
     spec = wl.CONFIGS[base].replace(layout=wl.PREFERRED_LAYOUT.get(base, "page"))
     t0 = time.time()
@@ -133,13 +136,15 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
     kept = int(b.kept_tokens().sum())
     if fp8:
-        kc, ks = _lib.quantize_rows(b.k_pages)
-        vc, vs = _lib.quantize_rows(b.v_pages)
+        quant = _lib.quantize_rows if bits == 8 else _lib.quantize_rows_fp4
+        kc, ks = quant(b.k_pages)
+        vc, vs = quant(b.v_pages)
         torch.cuda.synchronize()
         b.k_pages = b.v_pages = None  # the bf16 pools are not needed any more
         torch.cuda.empty_cache()
-        kv_bytes = kept * 2 * (D + 4)  # an 8-bit row of D codes plus its fp32 scale, K and V
-        micro = _lib.micro_attention_fp8
+        # a row of D codes of `bits` bits plus its fp32 scale, K and V
+        kv_bytes = kept * 2 * (D * bits // 8 + 4)
+        micro = _lib.micro_attention_fp8 if bits == 8 else _lib.micro_attention_fp4
         args = (b.q, kc, ks, vc, vs, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
     else:
         kv_bytes = b.kv_bytes()
@@ -193,7 +198,7 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     assert torch.isfinite(out).all(), "non-finite output"
 
     # the same step in one launch (da_attention / da_attention_fp8), beside it
-    fused = _lib.attention_fp8 if fp8 else _lib.attention
+    fused = {8: _lib.attention_fp8, 4: _lib.attention_fp4, 16: _lib.attention}[bits]
     out_f = torch.empty_like(out)
 
     def step_fused():
@@ -225,7 +230,7 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
                 else f"mean of {steps} back-to-back steps"),
         GBps=kv_bytes / (ms_step * 1e-3) / 1e9, micro_GBps=kv_bytes / (avg_micro * 1e-3) / 1e9,
         shape=dict(S=S, Hq=Hq, Hkv=spec.Hkv, D=D, P=spec.P, splits=B,
-                   kv_dtype="fp8_e4m3+f32 row scale" if fp8 else spec.dtype,
+                   kv_dtype={8: "fp8_e4m3+f32 row scale", 4: "fp4_e2m1+f32 row scale"}.get(bits, spec.dtype),
                    pool_layout="[Hkv, NP, P, D]" if spec.layout == "head" else "[NP, Hkv, P, D]",
                    max_len=spec.max_len, block_mask=spec.mask is not None),
         kept_tokens=kept,
@@ -705,7 +710,7 @@ def run(a, seeds):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if kv == "bf16" else ("f32" if kv == "f32" else "fp8"),
+        "dtype": kv if kv in ("bf16", "f32") else kv.split("_")[0],
         "data": "synthetic",
         "config": {"workload": head["workload"], **head["shape"], "accum_dtype": "f32",
                    "seed": seeds[0], "kv_bytes_per_step": head["kv_bytes"]},

@@ -60,9 +60,12 @@ typedef enum da_status {
 typedef enum da_dtype {
   DA_F32 = 0,     /* IEEE binary32                                     */
   DA_BF16 = 1,    /* bfloat16: the upper 16 bits of an IEEE binary32  */
-  DA_FP8_E4M3 = 2 /* 8-bit pages: OCP FP8 E4M3 codes with one fp32     */
-                  /* scale per (page, KV head, slot) row; q is bf16.   */
-                  /* Used by da_micro_attention_fp8 only.              */
+  DA_FP8_E4M3 = 2, /* 8-bit pages: OCP FP8 E4M3 codes with one fp32    */
+                   /* scale per (page, KV head, slot) row; q is bf16.  */
+                   /* Used by the *_fp8 entry points only.             */
+  DA_FP4_E2M1 = 3  /* 4-bit pages: OCP FP4 E2M1 codes, two per byte,   */
+                   /* with one fp32 scale per row; q is bf16.  Used by */
+                   /* the *_fp4 entry points only.                     */
 } da_dtype;
 
 /* Order of the dimensions of the K / V pools.  Page-major: [NP, Hkv, P, D]
@@ -218,6 +221,46 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
                            float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
                            const uint8_t* select_heads, void* stats, hipStream_t stream);
+
+/*
+ * 4-bit KV pages (LServe blog page, section 3.2.1: the streaming-head cache
+ * is stored in 4 bits, the retrieval-head cache with 2-8 bits).  Format:
+ * OCP FP4 E2M1 codes (1 sign bit, 2 exponent bits with bias 1, 1 mantissa
+ * bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN), two per
+ * byte, element 2i of a row in the low nibble of byte i; one fp32 scale per
+ * row, s = amax / 6 (fp32 division), code = the E2M1 value nearest to x / s
+ * (fp32 division; |x / s| clamped to 6; ties to the code with mantissa bit
+ * 0; the sign kept when the magnitude rounds to zero); an all-zero row has
+ * s = 0 and codes 0.  A key or value stands for value(code) * s.
+ *
+ * da_quantize_rows_fp4: as da_quantize_rows with codes [rows, D / 2] uint8
+ *   (4-byte aligned) in this format.
+ * da_append_kv_fp4: as da_append_kv_fp8, writing 4-bit code rows of D / 2
+ *   bytes (pools [NP, Hkv, P, D / 2], 4-byte aligned) and their scales.
+ * da_micro_attention_fp4, da_attention_fp4: as the _fp8 entry points with
+ *   sh->dtype = DA_FP4_E2M1 and code pools [NP, Hkv, P, D / 2] uint8
+ *   (16-byte aligned; head-major [Hkv, NP, P, D / 2] with
+ *   DA_POOL_HEAD_MAJOR).  Supported: D 64 or 128 (D = 64 with one query
+ *   head per KV head needs P >= 32), G in {1, 2, 4, 8}; workspace sizes
+ *   from the same queries as the other pages.
+ */
+da_status da_quantize_rows_fp4(int32_t dtype, int64_t rows, int32_t D, const void* x,
+                               uint8_t* codes, float* scales, hipStream_t stream);
+da_status da_append_kv_fp4(const da_shape* sh, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
+                           float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
+                           const uint8_t* select_heads, void* stats, hipStream_t stream);
+da_status da_micro_attention_fp4(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                                 const float* k_scales, const uint8_t* v_codes,
+                                 const float* v_scales, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* split_bounds,
+                                 const uint8_t* block_mask, float* MA, float* m, float* e,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+da_status da_attention_fp4(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                           const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Aggregate b partials per (request, query head) into attention output.

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libda.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "da.h")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_HIP = 0, 1, 2, 3
-DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
+DA_F32, DA_BF16, DA_FP8_E4M3, DA_FP4_E2M1 = 0, 1, 2, 3
 STATUS_NAMES = {0: "DA_OK", 1: "DA_ERR_INVALID_ARG", 2: "DA_ERR_UNSUPPORTED", 3: "DA_ERR_HIP"}
 
 
@@ -95,12 +95,16 @@ def load() -> ctypes.CDLL:
     lib.da_micro_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.da_micro_attention_fp8.restype = ctypes.c_int
+    lib.da_micro_attention_fp4.argtypes = lib.da_micro_attention_fp8.argtypes
+    lib.da_micro_attention_fp4.restype = ctypes.c_int
     lib.da_attention.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                  _VP]
     lib.da_attention.restype = ctypes.c_int
     lib.da_attention_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]
     lib.da_attention_fp8.restype = ctypes.c_int
+    lib.da_attention_fp4.argtypes = lib.da_attention_fp8.argtypes
+    lib.da_attention_fp4.restype = ctypes.c_int
     lib.da_attention_noalloc.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.da_attention_noalloc.restype = ctypes.c_int
     lib.da_attention_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t),
@@ -109,9 +113,13 @@ def load() -> ctypes.CDLL:
     lib.da_quantize_rows.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP,
                                      _VP]
     lib.da_quantize_rows.restype = ctypes.c_int
+    lib.da_quantize_rows_fp4.argtypes = lib.da_quantize_rows.argtypes
+    lib.da_quantize_rows_fp4.restype = ctypes.c_int
     lib.da_append_kv_fp8.argtypes = [sp, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32,
                                      _VP, _VP, _VP]
     lib.da_append_kv_fp8.restype = ctypes.c_int
+    lib.da_append_kv_fp4.argtypes = lib.da_append_kv_fp8.argtypes
+    lib.da_append_kv_fp4.restype = ctypes.c_int
     lib.da_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
     lib.da_stream_read.restype = ctypes.c_int
     lib.da_stream_read_sink_words.argtypes = []
@@ -157,9 +165,11 @@ POOL_LAYOUTS = {"page": 0, "head": 1}
 
 
 def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = None,
-             chunks: int = 0, schedule: int = 0, pool_layout: str = "page") -> DaShape:
+             chunks: int = 0, schedule: int = 0, pool_layout: str = "page",
+             codes_per_byte: int = 1) -> DaShape:
     """da_shape of a call; pool_layout "page" = pools [NP, Hkv, P, D],
-    "head" = [Hkv, NP, P, D]."""
+    "head" = [Hkv, NP, P, D] (4-bit code pools: D / 2 bytes per row,
+    codes_per_byte = 2)."""
     S, Hq, D = q.shape
     if pool_layout not in POOL_LAYOUTS:
         raise ValueError(f"pool_layout must be one of {sorted(POOL_LAYOUTS)}")
@@ -167,6 +177,7 @@ def shape_of(q, k_pages, block_table, split_bounds, scale: Optional[float] = Non
         Hkv, NP, P, D2 = k_pages.shape
     else:
         NP, Hkv, P, D2 = k_pages.shape
+    D2 *= codes_per_byte
     if D2 != D:
         raise ValueError(f"head dim of q ({D}) and k_pages ({D2}) differ")
     nbh = split_bounds.shape[1]
@@ -208,7 +219,7 @@ def _cached_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tenso
 
 
 def _paged_args(q, k, v, block_table, seq_lens, split_bounds, block_mask, scale, chunks, schedule,
-                pool_layout, k_scales=None, v_scales=None) -> DaShape:
+                pool_layout, k_scales=None, v_scales=None, bits: int = 8) -> DaShape:
     """Checks the arguments every attention entry point shares and returns
     the call's da_shape: bf16 / fp32 pools (k, v as q's dtype), or 8-bit
     pools (k, v uint8 codes with k_scales / v_scales, q bf16)."""
@@ -229,9 +240,10 @@ def _paged_args(q, k, v, block_table, seq_lens, split_bounds, block_mask, scale,
     _need(split_bounds, "split_bounds", torch.int32, dev, 3)
     if block_mask is not None:
         _need(block_mask, "block_mask", torch.uint8, dev, 3)
-    sh = shape_of(q, k, block_table, split_bounds, scale, chunks, schedule, pool_layout)
+    sh = shape_of(q, k, block_table, split_bounds, scale, chunks, schedule, pool_layout,
+                  2 if fp8 and bits == 4 else 1)
     if fp8:
-        sh.dtype = DA_FP8_E4M3
+        sh.dtype = DA_FP8_E4M3 if bits == 8 else DA_FP4_E2M1
     if block_table.shape[0] != sh.S or seq_lens.shape[0] != sh.S or split_bounds.shape[0] != sh.S:
         raise ValueError("block_table, seq_lens and split_bounds must have S rows")
     if block_mask is not None and tuple(block_mask.shape) != (sh.S, sh.Hkv, sh.max_pages):
@@ -314,6 +326,52 @@ def quantize_rows(x, *, out=None):
     _check(load().da_quantize_rows(_dtype_code(x), rows, D, _ptr(x), _ptr(codes), _ptr(scales),
                                    _stream(dev)))
     return codes, scales
+
+
+def quantize_rows_fp4(x, *, out=None):
+    """4-bit rows via da_quantize_rows_fp4: x [..., D] (bf16 or float32) ->
+    (codes uint8 [..., D / 2], two OCP FP4 E2M1 codes per byte, element 2i in
+    the low nibble; scales float32 [...], amax / 6 per row)."""
+    dev = x.device
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    D = x.shape[-1]
+    if D % 2:
+        raise ValueError("D must be even")
+    rows = x.numel() // D
+    cshape = tuple(x.shape[:-1]) + (D // 2,)
+    if out is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    else:
+        codes, scales = out
+        _need(codes, "codes", torch.uint8, dev, x.dim())
+        _need(scales, "scales", torch.float32, dev, x.dim() - 1)
+        if tuple(codes.shape) != cshape or scales.shape != x.shape[:-1]:
+            raise ValueError("codes must be x with D / 2 in its last dim, scales x without it")
+    _check(load().da_quantize_rows_fp4(_dtype_code(x), rows, D, _ptr(x), _ptr(codes), _ptr(scales),
+                                       _stream(dev)))
+    return codes, scales
+
+
+def micro_attention_fp4(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens,
+                        split_bounds, block_mask=None, *, scale: Optional[float] = None, out=None,
+                        chunks: int = 0, workspace: Optional[torch.Tensor] = None,
+                        schedule: int = 0, pool_layout: str = "page"):
+    """MicroAttention partials over 4-bit pages via da_micro_attention_fp4:
+    q [S, Hq, D] bf16; k_codes / v_codes [NP, Hkv, P, D / 2] uint8 (two E2M1
+    codes per byte); scales as micro_attention_fp8."""
+    dev = q.device
+    sh = _paged_args(q, k_codes, v_codes, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout, k_scales, v_scales, bits=4)
+    MA, m, e = _partials_out(sh, out, dev)
+    workspace = _micro_workspace(sh, workspace, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().da_micro_attention_fp4(
+        ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(block_table), _ptr(seq_lens), _ptr(split_bounds), _ptr(block_mask), _ptr(MA), _ptr(m),
+        _ptr(e), _ptr(workspace), ws_bytes, _stream(dev)))
+    return MA, m, e
 
 
 def micro_attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens,
@@ -486,6 +544,25 @@ def attention_fp8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens
     return out
 
 
+def attention_fp4(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, split_bounds,
+                  block_mask=None, *, scale: Optional[float] = None, out=None, chunks: int = 0,
+                  schedule: int = 0, workspace: Optional[torch.Tensor] = None,
+                  pool_layout: str = "page", fuse: int = 0):
+    """One decode step over 4-bit pages via da_attention_fp4 (inputs as
+    micro_attention_fp4, output, workspace and fuse as attention)."""
+    dev = q.device
+    sh = _paged_args(q, k_codes, v_codes, block_table, seq_lens, split_bounds, block_mask, scale,
+                     chunks, schedule, pool_layout, k_scales, v_scales, bits=4)
+    sh.fuse = int(fuse)
+    out = _step_out(sh, out, dev)
+    ws = _fused_workspace(dev, sh, workspace)
+    _check(load().da_attention_fp4(
+        ctypes.byref(sh), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+        _ptr(block_table), _ptr(seq_lens), _ptr(split_bounds), _ptr(block_mask), _ptr(out),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DA_F32
@@ -633,12 +710,27 @@ def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_code
     pools in place via da_append_kv_fp8, keeping ``stats`` (head-major
     statistics in the rows' dtype, or None) current from the full-precision
     key rows.  seq_lens is not advanced."""
+    _append_quantized(8, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales,
+                      stats, logical, select_heads, pool_layout)
+
+
+def append_kv_fp4(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales, *,
+                  stats=None, logical: int = 16, select_heads=None, pool_layout: str = "page"):
+    """append_kv_fp8 for 4-bit pools (codes [NP, Hkv, P, D / 2]) via
+    da_append_kv_fp4."""
+    _append_quantized(4, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes, v_scales,
+                      stats, logical, select_heads, pool_layout)
+
+
+def _append_quantized(bits, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes,
+                      v_scales, stats, logical, select_heads, pool_layout):
     dev = k_codes.device
     _need(k_codes, "k_codes", torch.uint8, dev, 4)
     _need(v_codes, "v_codes", torch.uint8, dev, 4)
     if v_codes.shape != k_codes.shape:
         raise ValueError("k_codes and v_codes differ in shape")
     NP, Hkv, P, D = _pool_dims(k_codes, pool_layout)
+    D *= 8 // bits  # 4-bit pools hold two codes per byte
     for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
         _need(t, name, torch.float32, dev, 3)
         if tuple(t.shape) != tuple(k_codes.shape[:3]):
@@ -658,10 +750,10 @@ def append_kv_fp8(k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_code
         _need(select_heads, "select_heads", torch.uint8, dev, 1)
     sh = _selector_shape(S, Hkv, Hkv, D, P, NP, block_table.shape[1], _dtype_code(k_new),
                          pool_layout)
-    _check(load().da_append_kv_fp8(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table),
-                                   _ptr(seq_lens), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
-                                   _ptr(v_scales), int(logical), _ptr(select_heads), _ptr(stats),
-                                   _stream(dev)))
+    fn = load().da_append_kv_fp8 if bits == 8 else load().da_append_kv_fp4
+    _check(fn(ctypes.byref(sh), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(seq_lens),
+              _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), int(logical),
+              _ptr(select_heads), _ptr(stats), _stream(dev)))
 
 
 def split_bounds(block_mask, seq_lens, *, P: int, b: int, horizon: int = 0, Hkv=None,

@@ -41,11 +41,12 @@ COMMON_FLAGS = [
 # loads an unread slot (those rows are zero-filled), so no NaN reaches its
 # arithmetic: with NaNs ruled out and IEEE mode off, max/min results on
 # finite and infinite values are bit-identical and the steps fold.
-# Infinities are still honoured (the kernel relies on -inf).  Only the 8-bit
-# instances take the flags: they run 3-5% faster; the bf16 ones gain nothing
-# on G = 4 and spill more registers on G = 8.
+# Infinities are still honoured (the kernel relies on -inf).  Only the 8- and
+# 4-bit instances take the flags: the 8-bit ones run 3-5% faster; the bf16
+# ones gain nothing on G = 4 and spill more registers on G = 8.
 FILE_FLAGS = {
     "micro_attention_mfma_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "micro_attention_mfma_fp4.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

@@ -34,9 +34,9 @@ da_status fail(da_status st, const char* fmt, ...) {
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 // Shape checks shared by the entry points that read the paged cache.  The
-// 8-bit page type is accepted only where fp8 is true (its own entry point
-// and the workspace query).
-da_status check_shape(const da_shape* sh, bool fp8 = false) {
+// quantized page types (8- and 4-bit) are accepted only where quant is true
+// (their own entry points and the workspace queries).
+da_status check_shape(const da_shape* sh, bool quant = false) {
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 ||
       sh->max_splits < 1 || sh->NP < 1)
@@ -48,9 +48,10 @@ da_status check_shape(const da_shape* sh, bool fp8 = false) {
     return fail(DA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", sh->Hq, sh->Hkv);
   if (sh->bounds_per_head != 0 && sh->bounds_per_head != 1)
     return fail(DA_ERR_INVALID_ARG, "bounds_per_head must be 0 or 1 (got %d)", sh->bounds_per_head);
-  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16 && !(fp8 && sh->dtype == DA_FP8_E4M3))
+  const bool quantized = sh->dtype == DA_FP8_E4M3 || sh->dtype == DA_FP4_E2M1;
+  if (sh->dtype != DA_F32 && sh->dtype != DA_BF16 && !(quant && quantized))
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not a da_dtype%s", sh->dtype,
-                sh->dtype == DA_FP8_E4M3 ? " for this entry point (8-bit pages: da_micro_attention_fp8)" : "");
+                quantized ? " for this entry point (quantized pages: da_micro_attention_fp8 / _fp4)" : "");
   if (!(sh->scale > 0.f) || !isfinite(sh->scale))
     return fail(DA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if ((long long)sh->max_pages * sh->P > (long long)INT_MAX - sh->P)
@@ -106,8 +107,10 @@ int resolve_chunks(const da_shape* sh) {
   const int G = sh->Hq / sh->Hkv;
   const long long items = (long long)sh->S * sh->Hkv * sh->max_splits;
   const long long pages_per_split = sh->max_pages / sh->max_splits;  // typical split size
-  const long long row = sh->dtype == DA_F32 ? 4LL * sh->D : sh->dtype == DA_BF16 ? 2LL * sh->D
-                                                                                 : sh->D + 4LL;
+  const long long row = sh->dtype == DA_F32    ? 4LL * sh->D
+                        : sh->dtype == DA_BF16   ? 2LL * sh->D
+                        : sh->dtype == DA_FP8_E4M3 ? sh->D + 4LL
+                                                   : sh->D / 2 + 4LL;  // codes plus the row scale
   const long long item_bytes = pages_per_split * sh->P * 2 * row;  // K and V of a typical split
   const long long fill = device_cus() * (da::micro_mfma_supported(sh->dtype, sh->D, G) ? 2 : 1);
   long long c = (fill + items - 1) / items;
@@ -222,6 +225,8 @@ da_status check_micro_built(const da_shape* sh) {
   const int G = sh->Hq / sh->Hkv;
   if (!da::micro_supported(sh->dtype, sh->D, G))
     return fail(DA_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", G);
+  if (sh->dtype == DA_FP4_E2M1 && sh->D == 64 && sh->P < 32 && G == 1)
+    return fail(DA_ERR_UNSUPPORTED, "4-bit pages with D = 64 need P >= 32 (a wave load is 32 rows)");
   return DA_OK;
 }
 
@@ -342,23 +347,56 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
                               workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared body of the quantized-page entry points: the shape must name the
+// entry point's page type; out == null gives partials, else the step.
+da_status quantized_step(const char* name, int32_t want, const da_shape* sh, const void* q,
+                         const uint8_t* k_codes, const float* k_scales, const uint8_t* v_codes,
+                         const float* v_scales, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* split_bounds,
+                         const uint8_t* block_mask, float* MA, float* m, float* e, float* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const da_status st = check_shape(sh, true);
+  if (st != DA_OK) return st;
+  if (sh->dtype != want)
+    return fail(DA_ERR_INVALID_ARG, "%s needs dtype %s (got %d)", name,
+                want == DA_FP8_E4M3 ? "DA_FP8_E4M3" : "DA_FP4_E2M1", sh->dtype);
+  if (!k_scales || !v_scales || (MA == nullptr && !out))
+    return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
+  return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
+                              split_bounds, block_mask, MA, m, e, out, workspace, workspace_bytes,
+                              stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_codes,
                                  const float* k_scales, const uint8_t* v_codes,
                                  const float* v_scales, const int32_t* block_table,
                                  const int32_t* seq_lens, const int32_t* split_bounds,
                                  const uint8_t* block_mask, float* MA, float* m, float* e,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const da_status st = check_shape(sh, true);
-  if (st != DA_OK) return st;
-  if (sh->dtype != DA_FP8_E4M3)
-    return fail(DA_ERR_INVALID_ARG, "da_micro_attention_fp8 needs dtype DA_FP8_E4M3 (got %d)",
-                sh->dtype);
-  if (!k_scales || !v_scales) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
-    return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
-  return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
-                              split_bounds, block_mask, MA, m, e, nullptr, workspace,
-                              workspace_bytes, stream);
+  return quantized_step("da_micro_attention_fp8", DA_FP8_E4M3, sh, q, k_codes, k_scales, v_codes,
+                        v_scales, block_table, seq_lens, split_bounds, block_mask, MA, m, e,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+da_status da_micro_attention_fp4(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                                 const float* k_scales, const uint8_t* v_codes,
+                                 const float* v_scales, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* split_bounds,
+                                 const uint8_t* block_mask, float* MA, float* m, float* e,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return quantized_step("da_micro_attention_fp4", DA_FP4_E2M1, sh, q, k_codes, k_scales, v_codes,
+                        v_scales, block_table, seq_lens, split_bounds, block_mask, MA, m, e,
+                        nullptr, workspace, workspace_bytes, stream);
 }
 
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
@@ -388,16 +426,21 @@ da_status da_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_c
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* split_bounds, const uint8_t* block_mask, float* out,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const da_status st = check_shape(sh, true);
-  if (st != DA_OK) return st;
-  if (sh->dtype != DA_FP8_E4M3)
-    return fail(DA_ERR_INVALID_ARG, "da_attention_fp8 needs dtype DA_FP8_E4M3 (got %d)", sh->dtype);
-  if (!k_scales || !v_scales || !out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
-    return fail(DA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
-  return micro_attention_impl(sh, q, k_codes, v_codes, k_scales, v_scales, block_table, seq_lens,
-                              split_bounds, block_mask, nullptr, nullptr, nullptr, out, workspace,
-                              workspace_bytes, stream);
+  if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  return quantized_step("da_attention_fp8", DA_FP8_E4M3, sh, q, k_codes, k_scales, v_codes,
+                        v_scales, block_table, seq_lens, split_bounds, block_mask, nullptr,
+                        nullptr, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+da_status da_attention_fp4(const da_shape* sh, const void* q, const uint8_t* k_codes,
+                           const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* split_bounds, const uint8_t* block_mask, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
+  return quantized_step("da_attention_fp4", DA_FP4_E2M1, sh, q, k_codes, k_scales, v_codes,
+                        v_scales, block_table, seq_lens, split_bounds, block_mask, nullptr,
+                        nullptr, nullptr, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -666,7 +709,12 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
   return DA_OK;
 }
 
-da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
+}  // extern "C"
+
+namespace {
+
+// Shared body of da_append_kv_fp8 (bits 8) and da_append_kv_fp4 (bits 4).
+da_status append_quantized(int bits, const da_shape* sh, const void* k_new, const void* v_new,
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
                            float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
                            const uint8_t* select_heads, void* stats, hipStream_t stream) {
@@ -683,18 +731,20 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
   if ((long long)sh->S * sh->Hkv > INT_MAX)
     return fail(DA_ERR_INVALID_ARG, "S * Hkv exceeds the launch range");
   if (!da::quantize_supported(sh->dtype, sh->D))
-    return fail(DA_ERR_UNSUPPORTED, "8-bit append not built for D=%d (64, 128)", sh->D);
+    return fail(DA_ERR_UNSUPPORTED, "%d-bit append not built for D=%d (64, 128)", bits, sh->D);
   if (stats != nullptr && !da::selector_supported(sh->dtype, sh->D, 1, sh->P, logical))
     return fail(DA_ERR_UNSUPPORTED, "statistics not built for P=%d logical=%d", sh->P, logical);
   if (stats != nullptr && !aligned(stats, 16))
     return fail(DA_ERR_INVALID_ARG, "statistics must be 16-byte aligned");
   if (!k_new || !v_new || !block_table || !seq_lens || !k_codes || !k_scales || !v_codes || !v_scales)
     return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_codes, 8) || !aligned(v_codes, 8))
-    return fail(DA_ERR_INVALID_ARG, "new rows must be 16-byte and code pools 8-byte aligned");
+  const size_t ca = bits == 8 ? 8 : 4;  // a lane writes 8 codes: 8 or 4 bytes
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_codes, ca) || !aligned(v_codes, ca))
+    return fail(DA_ERR_INVALID_ARG, "new rows must be 16-byte and code pools %zu-byte aligned", ca);
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
     return fail(DA_ERR_INVALID_ARG, "int32/float arrays must be 4-byte aligned");
   da::AppendFp8Params p{};
+  p.bits = bits;
   p.k_new = k_new;
   p.v_new = v_new;
   p.table = block_table;
@@ -713,8 +763,29 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
   p.logical = stats != nullptr ? logical : sh->P;
   p.head_major = sh->pool_layout == DA_POOL_HEAD_MAJOR;
   const hipError_t err = da::launch_append_kv_fp8(p, sh->dtype, sh->D, stream);
-  if (err != hipSuccess) return fail(DA_ERR_HIP, "8-bit append launch failed: %s", hipGetErrorString(err));
+  if (err != hipSuccess)
+    return fail(DA_ERR_HIP, "%d-bit append launch failed: %s", bits, hipGetErrorString(err));
   return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
+                           float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
+                           const uint8_t* select_heads, void* stats, hipStream_t stream) {
+  return append_quantized(8, sh, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes,
+                          v_scales, logical, select_heads, stats, stream);
+}
+
+da_status da_append_kv_fp4(const da_shape* sh, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
+                           float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
+                           const uint8_t* select_heads, void* stats, hipStream_t stream) {
+  return append_quantized(4, sh, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes,
+                          v_scales, logical, select_heads, stats, stream);
 }
 
 da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
@@ -746,8 +817,13 @@ da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const i
   return DA_OK;
 }
 
-da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x,
-                           uint8_t* codes, float* scales, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of da_quantize_rows (bits 8) and da_quantize_rows_fp4 (bits 4).
+da_status quantize_rows_impl(int bits, int32_t dtype, int64_t rows, int32_t D, const void* x,
+                             uint8_t* codes, float* scales, hipStream_t stream) {
   if (rows < 0 || D < 1) return fail(DA_ERR_INVALID_ARG, "rows must be >= 0 and D >= 1");
   if (dtype != DA_F32 && dtype != DA_BF16)
     return fail(DA_ERR_INVALID_ARG, "dtype %d is not DA_F32 or DA_BF16", dtype);
@@ -755,13 +831,29 @@ da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x
     return fail(DA_ERR_UNSUPPORTED, "quantization not built for D=%d (64, 128)", D);
   if (rows == 0) return DA_OK;
   if (!x || !codes || !scales) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
-    return fail(DA_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte and scales 4-byte aligned");
+  const size_t ca = bits == 8 ? 8 : 4;  // a lane writes 8 codes: 8 or 4 bytes
+  if (!aligned(x, 16) || !aligned(codes, ca) || !aligned(scales, 4))
+    return fail(DA_ERR_INVALID_ARG, "x must be 16-byte, codes %zu-byte and scales 4-byte aligned",
+                ca);
   if (da::quantize_launch_blocks(D, rows) > UINT_MAX)
     return fail(DA_ERR_INVALID_ARG, "too many rows for one launch");
-  const hipError_t err = da::launch_quantize_rows(dtype, D, x, codes, scales, rows, stream);
+  const hipError_t err = da::launch_quantize_rows(dtype, D, bits, x, codes, scales, rows, stream);
   if (err != hipSuccess) return fail(DA_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(err));
   return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x,
+                           uint8_t* codes, float* scales, hipStream_t stream) {
+  return quantize_rows_impl(8, dtype, rows, D, x, codes, scales, stream);
+}
+
+da_status da_quantize_rows_fp4(int32_t dtype, int64_t rows, int32_t D, const void* x,
+                               uint8_t* codes, float* scales, hipStream_t stream) {
+  return quantize_rows_impl(4, dtype, rows, D, x, codes, scales, stream);
 }
 
 const char* da_last_error(void) { return g_last_error.c_str(); }

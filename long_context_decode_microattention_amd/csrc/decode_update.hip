@@ -100,12 +100,14 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_kernel(AppendP
   }
 }
 
-// One wave per (request, KV head) for 8-bit pages: lanes [0, LPR) quantize
-// the new key row, lanes [LPR, 2 LPR) the value row (each group sits inside
-// one DPP row, so its maximum is a DPP reduction); the other lanes idle.
-template <int DT, int D>
+// One wave per (request, KV head) for 8- or 4-bit pages: lanes [0, LPR)
+// quantize the new key row, lanes [LPR, 2 LPR) the value row (each group sits
+// inside one DPP row, so its maximum is a DPP reduction); the other lanes
+// idle.
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(AppendFp8Params p) {
   constexpr int LPR = D / 8;
+  constexpr int RB = D * BITS / 8;  // code bytes per row
   constexpr int ES = DT == 0 ? 4 : 2;
   const int item = blockIdx.x * kAppendWaves + threadIdx.x / kWave;
   if (item >= p.S * p.Hkv) return;  // wave-uniform
@@ -126,12 +128,16 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void append_kv_fp8_kernel(App
     load8<DT>(static_cast<const char*>(src) + (((size_t)s * p.Hkv + kvh) * D + col * 8) * ES, v);
   }
   float sc;
-  const uint2 c = quantize8<LPR>(v, sc);
+  uint2 c8 = make_uint2(0, 0);
+  uint32_t c4 = 0;
+  if constexpr (BITS == 8) c8 = quantize8<LPR>(v, sc);
+  else c4 = quantize4<LPR>(v, sc);
   if (part < 2) {
     const size_t tile_id = p.head_major ? (size_t)kvh * p.NP + phys : (size_t)phys * p.Hkv + kvh;
     const size_t row = tile_id * p.P + slot;
     uint8_t* codes = part == 0 ? p.k_codes : p.v_codes;
-    *reinterpret_cast<uint2*>(codes + row * D + col * 8) = c;
+    if constexpr (BITS == 8) *reinterpret_cast<uint2*>(codes + row * RB + col * 8) = c8;
+    else *reinterpret_cast<uint32_t*>(codes + row * RB + col * 4) = c4;
     if (col == 0) (part == 0 ? p.k_scales : p.v_scales)[row] = sc;
   }
   // statistics of the logical page, folded from the full-precision key row
@@ -271,10 +277,19 @@ hipError_t launch_append_kv_fp8(const AppendFp8Params& p, int dtype, int D, hipS
   const long long items = (long long)p.S * p.Hkv;
   if (items < 1) return hipSuccess;
   const dim3 g((unsigned)((items + kAppendWaves - 1) / kAppendWaves)), b(kAppendWaves * kWave);
-  if (dtype == 0 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 64>), g, b, 0, stream, p);
-  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 128>), g, b, 0, stream, p);
-  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 64>), g, b, 0, stream, p);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 128>), g, b, 0, stream, p);
+  if (p.bits == 4) {
+    if (dtype == 0 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 64, 4>), g, b, 0, stream, p);
+    else if (dtype == 0 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 128, 4>), g, b, 0, stream, p);
+    else if (dtype == 1 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 64, 4>), g, b, 0, stream, p);
+    else if (dtype == 1 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 128, 4>), g, b, 0, stream, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (p.bits != 8) return hipErrorInvalidValue;
+  if (dtype == 0 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 64, 8>), g, b, 0, stream, p);
+  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<0, 128, 8>), g, b, 0, stream, p);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 64, 8>), g, b, 0, stream, p);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((append_kv_fp8_kernel<1, 128, 8>), g, b, 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -33,16 +33,18 @@ __device__ __forceinline__ float dpp(float x) {
 // branches on it skip code instead of masking it).
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
-// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16 or 32); every
-// lane of the group receives the group total.  After the two quad steps each
+// Sum over aligned groups of N consecutive lanes (N = 2, 4, 8, 16 or 32);
+// every lane of the group receives the group total.  The first quad step
+// sums lane pairs; after the two quad steps each
 // lane holds its quad's sum; the half-row mirror pairs every lane with a lane
 // of the other quad of its 8-lane half, the row mirror with a lane of the
 // other half of its 16-lane row; a 32-lane group finishes with an exchange
 // across rows.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group size");
   x += dpp<kDppQuadXor1>(x);
+  if constexpr (N == 2) return x;
   x += dpp<kDppQuadXor2>(x);
   if constexpr (N == 4) return x;
   x += dpp<kDppHalfMirror>(x);
@@ -96,6 +98,33 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
   out[1] = lo.y;
   out[2] = hi.x;
   out[3] = hi.y;
+}
+
+// Two OCP FP4 E2M1 codes, the low and high nibble of byte B of a word (the
+// row elements 2B and 2B + 1 of the word's eight) -> a bf16 pair in one word,
+// exactly (every E2M1 value is a bf16 value): v_cvt_scalef32_pk_bf16_fp4
+// with scale 1.
+template <int B>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+
+// Eight E2M1 codes packed in a word (element i in bits 4i + 3 .. 4i) ->
+// eight floats, exactly (v_cvt_scalef32_pk_f32_fp4 with scale 1, one byte at
+// a time).
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float* out) {
+  const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a.x;
+  out[1] = a.y;
+  out[2] = b.x;
+  out[3] = b.y;
+  out[4] = c.x;
+  out[5] = c.y;
+  out[6] = d.x;
+  out[7] = d.y;
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));

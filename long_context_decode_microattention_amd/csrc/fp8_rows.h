@@ -1,8 +1,11 @@
-// Quantization of D-wide rows to OCP FP8 E4M3 codes with one fp32 scale per
-// row, shared by the bulk row quantizer and the decode-time append:
-// s = amax / 448 and code(x) = E4M3(x / s), both divisions correctly
-// rounded; y is clamped to +-448 first (v_cvt_pk_fp8_f32 rounds to nearest
-// even in range and gives NaN above 464); an all-zero row has s = 0 and
+// Quantization of D-wide rows to 8-bit OCP FP8 E4M3 or 4-bit OCP FP4 E2M1
+// codes with one fp32 scale per row, shared by the bulk row quantizer and the
+// decode-time append.  8 bits: s = amax / 448 and code(x) = E4M3(x / s),
+// both divisions correctly rounded; y is clamped to +-448 first
+// (v_cvt_pk_fp8_f32 rounds to nearest even in range and gives NaN above
+// 464).  4 bits: s = amax / 6 and code(x) = the E2M1 value nearest to x / s
+// (|y| clamped to 6, ties to mantissa bit 0, the sign of y kept), two codes
+// per byte, element 2i in the low nibble.  An all-zero row has s = 0 and
 // codes 0.  A row is held by D/8 consecutive lanes, 8 elements each.
 #pragma once
 
@@ -70,6 +73,37 @@ __device__ __forceinline__ uint2 quantize8(const float (&v)[8], float& scale) {
   }
   scale = s;
   return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+// Magnitude code (0-7) of the E2M1 value nearest to a >= 0, whose grid is
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6: a compare per midpoint, each tie going to the
+// neighbour with mantissa bit 0 (even code), everything above 5 to 6 (the
+// clamp).
+__device__ __forceinline__ uint32_t e2m1_magnitude(float a) {
+  return a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+       : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.f   ? 6u : 7u;
+}
+
+// This lane's 8 elements as eight E2M1 codes in one word (element i in bits
+// 4i + 3 .. 4i) and the row scale; called like quantize8.
+template <int LPR>
+__device__ __forceinline__ uint32_t quantize4(const float (&v)[8], float& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<LPR>(amax);
+  const float s = __fdiv_rn(amax, 6.f);
+  uint32_t w = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = __fdiv_rn(v[i], s);
+      const uint32_t sign = (__builtin_bit_cast(uint32_t, y) >> 31) << 3;
+      w |= (e2m1_magnitude(fabsf(y)) | sign) << (4 * i);
+    }
+  }
+  scale = s;
+  return w;
 }
 
 }  // namespace da

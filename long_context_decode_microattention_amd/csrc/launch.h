@@ -112,6 +112,7 @@ struct AppendParams {
   int head_major;     // pools [Hkv, NP, P, D] instead of [NP, Hkv, P, D]
 };
 struct AppendFp8Params {
+  int bits;           // 8: FP8 E4M3 code rows of D bytes; 4: FP4 E2M1 rows of D / 2 bytes
   const void* k_new;  // [S, Hkv, D], bf16 or fp32
   const void* v_new;
   const int32_t* table;
@@ -139,8 +140,9 @@ hipError_t launch_split_bounds(const BoundsParams& p, hipStream_t stream);
 
 // 8-bit KV rows (quant.hip).
 bool quantize_supported(int dtype, int D);
-hipError_t launch_quantize_rows(int dtype, int D, const void* x, uint8_t* codes, float* scales,
-                                long long rows, hipStream_t stream);
+// bits 8: codes [rows, D] OCP FP8 E4M3; bits 4: [rows, D / 2] OCP FP4 E2M1, two per byte.
+hipError_t launch_quantize_rows(int dtype, int D, int bits, const void* x, uint8_t* codes,
+                                float* scales, long long rows, hipStream_t stream);
 long long quantize_launch_blocks(int D, long long rows);
 
 int stream_read_grid();

@@ -38,16 +38,18 @@ bool micro_mfma_supported(int dtype, int D, int G);
 
 namespace {
 
-// DT: 0 = fp32, 1 = bf16, 2 = fp8 E4M3 with per-row scales.  SL: tokens per
-// slab (16; 32 for fp8 pages when the page size allows, so a slab moves as
+// DT: 0 = fp32, 1 = bf16, 2 = fp8 E4M3 with per-row scales, 3 = fp4 E2M1
+// with per-row scales (two codes per byte).  SL: tokens per slab (16; for
+// quantized pages as many as the page size allows up to 8 KiB of K + V per
+// slab -- 32 tokens of 8-bit rows, 64 of 4-bit rows -- so a slab moves as
 // many bytes as a 16-token bf16 slab and as many stay in flight).
 template <int DT, int D, int SL>
 struct Layout {
-  static constexpr int ES = DT == 0 ? 4 : (DT == 1 ? 2 : 1);  // bytes per element
-  static constexpr int TOKB = D * ES;          // bytes per token row
+  static constexpr int TOKB = DT == 0 ? 4 * D : DT == 1 ? 2 * D : DT == 2 ? D : D / 2;  // row bytes
   static constexpr int LPT = TOKB / 16;        // lanes per token row
   static constexpr int TPI = kWave / LPT;      // token rows per wave load
-  static constexpr int EPL = 16 / ES;          // elements per lane
+  static constexpr int EPL = DT == 0 ? 4 : DT == 1 ? 8 : DT == 2 ? 16 : 32;  // elements per lane
+  static constexpr int QW = DT >= 2 ? EPL / 8 : 1;  // 16-byte words of the query per lane
   static constexpr int NI = SL / TPI;          // wave loads per slab per tensor
   static_assert(TPI * TOKB == kWave * 16, "wave load covers whole rows");
   static_assert(NI >= 1 && SL % TPI == 0, "slab covers whole wave loads");
@@ -86,20 +88,21 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
     const float c = p.scale * 1.4426950408889634f;  // scale * log2(e)
 
     // Query fragment of every head in the group: the lane's 16-byte column
-    // (for fp8 pages: the lane's 16 dims of the bf16 query, 32 bytes).
-    uint4 qv[G];
-    uint4 qv2[DT == 2 ? G : 1];
+    // (for quantized pages: the lane's EPL dims of the bf16 query, QW words
+    // of 16 bytes).
+    uint4 qv[G][L::QW];
   #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if constexpr (DT == 2) {
-        const uint4* qp = reinterpret_cast<const uint4*>(
-            static_cast<const char*>(p.q) + (size_t)(s * p.Hq + h0 + g) * D * 2 + (size_t)chunk * 32);
-        qv[g] = qp[0];
-        qv2[g] = qp[1];
+      if constexpr (DT >= 2) {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) +
+                                                         (size_t)(s * p.Hq + h0 + g) * D * 2 +
+                                                         (size_t)chunk * (L::EPL * 2));
+  #pragma unroll
+        for (int w = 0; w < L::QW; ++w) qv[g][w] = qp[w];
       } else {
         const char* qp = static_cast<const char*>(p.q) +
                          ((size_t)(s * p.Hq + h0 + g) * L::TOKB) + (size_t)chunk * 16;
-        qv[g] = *reinterpret_cast<const uint4*>(qp);
+        qv[g][0] = *reinterpret_cast<const uint4*>(qp);
       }
     }
 
@@ -126,9 +129,9 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
       const size_t head_row = (size_t)kvh * (p.head_major ? (size_t)p.NP : (size_t)1) * P;
       const char* kbase = static_cast<const char*>(p.k) + head_row * L::TOKB + lane * 16;
       const char* vbase = static_cast<const char*>(p.v) + head_row * L::TOKB + lane * 16;
-      // fp8: the scales of this lane's token rows (no scales for bf16 or fp32)
-      const float* ksb = DT == 2 ? p.ks + head_row + row : nullptr;
-      const float* vsb = DT == 2 ? p.vs + head_row + row : nullptr;
+      // quantized pages: the scales of this lane's token rows (none for bf16 or fp32)
+      const float* ksb = DT >= 2 ? p.ks + head_row + row : nullptr;
+      const float* vsb = DT >= 2 ? p.vs + head_row + row : nullptr;
 
       // resume point of the page scan: without a mask, ordinal = page - pa
       int rlp = it.mrow ? it.pa : it.pa + pc.o0;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
             for (int i = 0; i < L::NI; ++i) {
               f.k[i] = load_stream16(kbase + off + i * 1024);
               f.v[i] = load_stream16(vbase + off + i * 1024);
-              if constexpr (DT == 2) {
+              if constexpr (DT >= 2) {
                 f.ks[i] = ksb[q.row + i * L::TPI];
                 f.vs[i] = vsb[q.row + i * L::TPI];
               }
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
               if (t >= t0 && t < t1) {
                 f.k[i] = load_stream16(kbase + off + i * 1024);
                 f.v[i] = load_stream16(vbase + off + i * 1024);
-                if constexpr (DT == 2) {
+                if constexpr (DT >= 2) {
                   f.ks[i] = ksb[q.row + i * L::TPI];
                   f.vs[i] = vsb[q.row + i * L::TPI];
                 }
@@ -207,11 +210,28 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   #pragma unroll
             for (int g = 0; g < G; ++g) {
               float d;
-              if constexpr (DT == 2) {
+              const uint32_t w4[4] = {f.k[i].x, f.k[i].y, f.k[i].z, f.k[i].w};
+              uint32_t qw[4 * L::QW];
+  #pragma unroll
+              for (int w = 0; w < L::QW; ++w) {
+                qw[4 * w] = qv[g][w].x;
+                qw[4 * w + 1] = qv[g][w].y;
+                qw[4 * w + 2] = qv[g][w].z;
+                qw[4 * w + 3] = qv[g][w].w;
+              }
+              if constexpr (DT == 3) {
+                // codes widened to bf16 pairs (byte b of word w: dims 8w + 2b,
+                // 8w + 2b + 1), then bf16 dot products with q
+                d = 0.f;
+  #pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                  d = dot2_bf16(fp4x2_to_bf16x2<0>(w4[w]), qw[4 * w], d);
+                  d = dot2_bf16(fp4x2_to_bf16x2<1>(w4[w]), qw[4 * w + 1], d);
+                  d = dot2_bf16(fp4x2_to_bf16x2<2>(w4[w]), qw[4 * w + 2], d);
+                  d = dot2_bf16(fp4x2_to_bf16x2<3>(w4[w]), qw[4 * w + 3], d);
+                }
+              } else if constexpr (DT == 2) {
                 // codes widened to bf16 pairs, then bf16 dot products with q
-                const uint32_t w4[4] = {f.k[i].x, f.k[i].y, f.k[i].z, f.k[i].w};
-                const uint32_t qw[8] = {qv[g].x, qv[g].y, qv[g].z, qv[g].w,
-                                        qv2[g].x, qv2[g].y, qv2[g].z, qv2[g].w};
                 d = 0.f;
   #pragma unroll
                 for (int w = 0; w < 4; ++w) {
@@ -219,18 +239,18 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
                   d = dot2_bf16(fp8x2_to_bf16x2<true>(w4[w]), qw[2 * w + 1], d);
                 }
               } else if constexpr (DT == 1) {
-                d = dot2_bf16(f.k[i].x, qv[g].x, 0.f);
-                d = dot2_bf16(f.k[i].y, qv[g].y, d);
-                d = dot2_bf16(f.k[i].z, qv[g].z, d);
-                d = dot2_bf16(f.k[i].w, qv[g].w, d);
+                d = dot2_bf16(w4[0], qw[0], 0.f);
+                d = dot2_bf16(w4[1], qw[1], d);
+                d = dot2_bf16(w4[2], qw[2], d);
+                d = dot2_bf16(w4[3], qw[3], d);
               } else {
-                d = __builtin_bit_cast(float, f.k[i].x) * __builtin_bit_cast(float, qv[g].x);
-                d = fmaf(__builtin_bit_cast(float, f.k[i].y), __builtin_bit_cast(float, qv[g].y), d);
-                d = fmaf(__builtin_bit_cast(float, f.k[i].z), __builtin_bit_cast(float, qv[g].z), d);
-                d = fmaf(__builtin_bit_cast(float, f.k[i].w), __builtin_bit_cast(float, qv[g].w), d);
+                d = __builtin_bit_cast(float, w4[0]) * __builtin_bit_cast(float, qw[0]);
+                d = fmaf(__builtin_bit_cast(float, w4[1]), __builtin_bit_cast(float, qw[1]), d);
+                d = fmaf(__builtin_bit_cast(float, w4[2]), __builtin_bit_cast(float, qw[2]), d);
+                d = fmaf(__builtin_bit_cast(float, w4[3]), __builtin_bit_cast(float, qw[3]), d);
               }
               dot[i][g] = group_sum<L::LPT>(d);
-              if constexpr (DT == 2) dot[i][g] *= f.ks[i];
+              if constexpr (DT >= 2) dot[i][g] *= f.ks[i];
             }
           }
           if (!q.whole) {  // wave-uniform branch
@@ -270,7 +290,11 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   #pragma unroll
           for (int i = 0; i < L::NI; ++i) {
             float vf[L::EPL];
-            if constexpr (DT == 2) {
+            if constexpr (DT == 3) {
+              const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
+  #pragma unroll
+              for (int w = 0; w < 4; ++w) fp4x8_to_f32(w4[w], vf + 8 * w);
+            } else if constexpr (DT == 2) {
               const uint32_t w4[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
   #pragma unroll
               for (int w = 0; w < 4; ++w) fp8x4_to_f32(w4[w], vf + 4 * w);
@@ -289,7 +313,7 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
             }
   #pragma unroll
             for (int g = 0; g < G; ++g) {
-              const float pv = DT == 2 ? pw[i][g] * f.vs[i] : pw[i][g];
+              const float pv = DT >= 2 ? pw[i][g] * f.vs[i] : pw[i][g];
   #pragma unroll
               for (int k = 0; k < L::EPL; ++k) acc[g][k] = fmaf(pv, vf[k], acc[g][k]);
             }
@@ -387,7 +411,7 @@ hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
 
 bool micro_supported(int dtype, int D, int G) {
   if (D != 64 && D != 128) return false;
-  if (dtype == 2) return G == 1 || micro_mfma_supported(dtype, D, G);
+  if (dtype == 2 || dtype == 3) return G == 1 || micro_mfma_supported(dtype, D, G);
   return (dtype == 0 || dtype == 1) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
@@ -405,6 +429,16 @@ hipError_t launch_micro(int dtype, int D, int G, const MicroParams& p, hipStream
     if (p.P % 32 == 0)
       return D == 64 ? launch_one<2, 64, 1, 32>(p, stream) : launch_one<2, 128, 1, 32>(p, stream);
     return D == 64 ? launch_one<2, 64, 1>(p, stream) : launch_one<2, 128, 1>(p, stream);
+  }
+  if (dtype == 3) {  // fp4 pages: slabs of up to 64 tokens (8 KiB of K + V at D = 128)
+    if (D == 64) {  // 32 rows per wave load: pages of 32 tokens or more
+      if (p.P % 64 == 0) return launch_one<3, 64, 1, 64>(p, stream);
+      if (p.P % 32 == 0) return launch_one<3, 64, 1, 32>(p, stream);
+      return hipErrorInvalidValue;
+    }
+    if (p.P % 64 == 0) return launch_one<3, 128, 1, 64>(p, stream);
+    if (p.P % 32 == 0) return launch_one<3, 128, 1, 32>(p, stream);
+    return launch_one<3, 128, 1, 16>(p, stream);
   }
   return D == 64 ? dispatch_g<1, 64>(G, p, stream) : dispatch_g<1, 128>(G, p, stream);
 }

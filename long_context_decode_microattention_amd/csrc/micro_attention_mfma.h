@@ -54,32 +54,45 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// DT: 1 = bf16 pages, 2 = fp8 E4M3 pages with per-row scales.  Either way a
-// value lane holds 8 dims of one token row (LPT lanes per row).  A slab is SL
-// = 16 or 32 tokens: NG score groups of 16 tokens (token 16*g + col of group
-// g in score column col).
+// DT: 1 = bf16 pages, 2 = fp8 E4M3 pages, 3 = fp4 E2M1 pages (two codes per
+// byte), the quantized ones with per-row scales.  Either way a value lane
+// holds 8 dims of one token row (LPT lanes per row).  A slab is SL = 16, 32
+// or 64 tokens: NG score groups of 16 tokens (token 16*g + col of group g in
+// score column col).
 template <int DT, int D, int SL>
 struct MLayout {
-  static constexpr int TOKB = DT == 1 ? D * 2 : D;  // token row bytes
+  static constexpr int TOKB = DT == 1 ? D * 2 : DT == 2 ? D : D / 2;  // token row bytes
   static constexpr int LPT = D / 8;                // value lanes per token row
   static constexpr int TPI = kWave / LPT;          // token rows per value load
   static constexpr int NI = SL / TPI;              // value loads per slab
   static constexpr int NG = SL / 16;               // score groups per slab
   static constexpr int KS = D / 32;                // score k-steps
-  static constexpr int KL = DT == 1 ? KS : KS / 2; // 16-byte key loads per lane
-  static constexpr int VB = 8 * (TOKB / D);        // value bytes per lane per load
+  static constexpr int KL = DT == 1 ? KS : KS / 2; // 16-byte key loads per lane (bf16, fp8)
+  static constexpr int VB = DT == 1 ? 16 : DT == 2 ? 8 : 4;  // value bytes per lane per load
   static constexpr int EPL = 8;                    // elements per lane
 };
 
 template <int DT, int D, int SL>
 struct MFrag {
   using L = MLayout<DT, D, SL>;
-  uint4 k[L::NG][L::KL];
+  uint4 k[DT == 3 ? 1 : L::NG][L::KL];
+  uint32_t k4[DT == 3 ? L::NG : 1][L::KS];  // fp4 keys: 8 codes (one score step) per word
   uint4 v[DT == 1 ? L::NI : 1];   // bf16 values
   uint2 v8[DT == 2 ? L::NI : 1];  // fp8 values
-  float ksc[L::NG];               // fp8: K scale of token 16*g + col
-  float vsc[L::NG];               // fp8: V scale of token 16*g + col
+  uint32_t v4[DT == 3 ? L::NI : 1];  // fp4 values
+  float ksc[L::NG];               // quantized pages: K scale of token 16*g + col
+  float vsc[L::NG];               // quantized pages: V scale of token 16*g + col
 };
+
+// Eight E2M1 codes (one word) -> eight bf16 values (four words), exactly.
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t w) {
+  return make_uint4(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w), fp4x2_to_bf16x2<2>(w),
+                    fp4x2_to_bf16x2<3>(w));
+}
+
+__device__ __forceinline__ uint32_t load_stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
 // Eight E4M3 codes (two words) -> eight bf16 values (four words), exactly.
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
@@ -91,6 +104,23 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(t.x, t.y);
+}
+
+// A lane's KS words of fp4 key codes (4 * KS contiguous bytes).
+template <int KS>
+__device__ __forceinline__ void load_key_words(const char* p, uint32_t (&w)[KS]) {
+  static_assert(KS == 2 || KS == 4, "key steps");
+  if constexpr (KS == 4) {
+    const uint4 t = load_stream16(p);
+    w[0] = t.x;
+    w[1] = t.y;
+    w[2] = t.z;
+    w[3] = t.w;
+  } else {
+    const uint2 t = load_stream8(p);
+    w[0] = t.x;
+    w[1] = t.y;
+  }
 }
 
 __device__ __forceinline__ float row_max16(float x) {
@@ -179,11 +209,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       // key lane: token col; bf16: 16 bytes per step at 64*step + 16*grp;
       // fp8: 8*KS contiguous bytes at 8*KS*grp
       const char* kbase = static_cast<const char*>(p.k) + head_row * L::TOKB +
-                          (size_t)col * L::TOKB + (size_t)grp * (DT == 1 ? 16 : 8 * L::KS);
+                          (size_t)col * L::TOKB +
+                          (size_t)grp * (DT == 1 ? 16 : DT == 2 ? 8 * L::KS : 4 * L::KS);
       const char* vbase = static_cast<const char*>(p.v) + head_row * L::TOKB + lane * L::VB;
       // fp8: the K and V scales of the key lane's token (no scales for bf16)
-      const float* ksb = DT == 2 ? p.ks + head_row + col : nullptr;
-      const float* vsb = DT == 2 ? p.vs + head_row + col : nullptr;
+      const float* ksb = DT >= 2 ? p.ks + head_row + col : nullptr;
+      const float* vsb = DT >= 2 ? p.vs + head_row + col : nullptr;
 
       // resume point of the page scan: without a mask, ordinal = page - pa
       int rlp = it.mrow ? it.pa : it.pa + pc.o0;
@@ -222,10 +253,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
           if (q.whole) {
   #pragma unroll
             for (int g = 0; g < L::NG; ++g) {
+              if constexpr (DT == 3) {
+                load_key_words<L::KS>(kbase + off + g * 16 * L::TOKB, f.k4[g]);
+              } else {
   #pragma unroll
-              for (int j = 0; j < L::KL; ++j)
-                f.k[g][j] = load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE);
-              if constexpr (DT == 2) {
+                for (int j = 0; j < L::KL; ++j)
+                  f.k[g][j] = load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE);
+              }
+              if constexpr (DT >= 2) {
                 f.ksc[g] = ksb[q.row + 16 * g];
                 f.vsc[g] = vsb[q.row + 16 * g];
               }
@@ -234,8 +269,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             for (int i = 0; i < L::NI; ++i) {
               if constexpr (DT == 1) {
                 f.v[i] = load_stream16(vbase + off + i * VSTRIDE);
-              } else {
+              } else if constexpr (DT == 2) {
                 f.v8[i] = load_stream8(vbase + off + i * VSTRIDE);
+              } else {
+                f.v4[i] = load_stream4(vbase + off + i * VSTRIDE);
               }
             }
           } else {  // rows outside the split read as zeros (and zero scales)
@@ -243,11 +280,20 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             for (int g = 0; g < L::NG; ++g) {
               const int tk = q.tb + 16 * g + col;
               const bool kok = tk >= t0 && tk < t1;
+              if constexpr (DT == 3) {
+                if (kok) {
+                  load_key_words<L::KS>(kbase + off + g * 16 * L::TOKB, f.k4[g]);
+                } else {
   #pragma unroll
-              for (int j = 0; j < L::KL; ++j)
-                f.k[g][j] = kok ? load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE)
-                                : make_uint4(0, 0, 0, 0);
-              if constexpr (DT == 2) {
+                  for (int st = 0; st < L::KS; ++st) f.k4[g][st] = 0;
+                }
+              } else {
+  #pragma unroll
+                for (int j = 0; j < L::KL; ++j)
+                  f.k[g][j] = kok ? load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE)
+                                  : make_uint4(0, 0, 0, 0);
+              }
+              if constexpr (DT >= 2) {
                 f.ksc[g] = kok ? ksb[q.row + 16 * g] : 0.f;
                 f.vsc[g] = kok ? vsb[q.row + 16 * g] : 0.f;
               }
@@ -258,8 +304,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
               const bool vok = tv >= t0 && tv < t1;
               if constexpr (DT == 1) {
                 f.v[i] = vok ? load_stream16(vbase + off + i * VSTRIDE) : make_uint4(0, 0, 0, 0);
-              } else {
+              } else if constexpr (DT == 2) {
                 f.v8[i] = vok ? load_stream8(vbase + off + i * VSTRIDE) : make_uint2(0, 0);
+              } else {
+                f.v4[i] = vok ? load_stream4(vbase + off + i * VSTRIDE) : 0u;
               }
             }
           }
@@ -281,15 +329,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
               uint4 kb;
               if constexpr (DT == 1) {
                 kb = f.k[g][st];
-              } else {
+              } else if constexpr (DT == 2) {
                 const uint4& w = f.k[g][st / 2];
                 kb = (st & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+              } else {
+                kb = fp4x8_to_bf16x8(f.k4[g][st]);
               }
               sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
                                                              __builtin_bit_cast(bf16x8_t, kb), sc[g],
                                                              0, 0, 0);
             }
-            if constexpr (DT == 2) sc[g] *= f.ksc[g];
+            if constexpr (DT >= 2) sc[g] *= f.ksc[g];
           }
           if (!q.whole) {  // wave-uniform branch
   #pragma unroll
@@ -354,7 +404,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   #pragma unroll
               for (int i = 0; i < 4; ++i)
                 if (4 * grp + i < G)
-                  sp[(16 * g + col) * G + 4 * grp + i] = DT == 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
+                  sp[(16 * g + col) * G + 4 * grp + i] = DT >= 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
           }
 
           if (wave_any(moved)) {  // scalar branch: skipped, not masked
@@ -383,9 +433,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                 vf[2 * k] = bf16_lo(w4[k]);
                 vf[2 * k + 1] = bf16_hi(w4[k]);
               }
-            } else {
+            } else if constexpr (DT == 2) {
               fp8x4_to_f32(f.v8[j].x, vf);
               fp8x4_to_f32(f.v8[j].y, vf + 4);
+            } else {
+              fp4x8_to_f32(f.v4[j], vf);
             }
   #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -397,10 +449,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         };
 
         constexpr int W = kMicroWaves;
-        if constexpr (DT == 1 || G == 8 || SL == 32) {
-          // 8 KiB slabs (16 bf16 rows or 32 fp8 rows), and 16-row fp8 slabs
-          // with G = 8 (whose accumulators leave no registers for a third
-          // fragment): one slab in flight while the other is computed
+        if constexpr (DT == 1 || G == 8 || SL >= 32) {
+          // 8 KiB slabs (16 bf16 rows, 32 fp8 rows, 64 fp4 rows), 4 KiB slabs
+          // of 32 fp4 rows, and 16-row quantized slabs with G = 8 (whose
+          // accumulators leave no registers for a third fragment): one slab
+          // in flight while the other is computed
           MFrag<DT, D, SL> fa, fb;
           int sl = wave;
           if (sl < nslab) load(sl, fa);
@@ -477,10 +530,17 @@ hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
 
 // bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups
 // under one softmax update, 8 KiB of K + V like a bf16 slab) when the page
-// size allows and G <= 4; otherwise 16-token slabs.
+// size allows and G <= 4; fp4 pages: 64-token slabs (four score groups, 8 KiB
+// at D = 128), else 32; otherwise 16-token slabs.
 template <int DT, int D>
 hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
   if constexpr (DT == 2) {
+    if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
+    if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
+  }
+  if constexpr (DT == 3) {
+    if (p.P % 64 == 0 && G == 2) return launch_one<DT, D, 2, 64>(p, stream);
+    if (p.P % 64 == 0 && G == 4) return launch_one<DT, D, 4, 64>(p, stream);
     if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
     if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
   }
@@ -498,5 +558,8 @@ hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
 // translation unit of its own (micro_attention_mfma_fp8.hip, built with NaNs
 // ruled out and IEEE mode off so that its DPP max steps fold).
 hipError_t launch_micro_mfma_fp8(int D, int G, const MicroParams& p, hipStream_t stream);
+// 4-bit pages: micro_mfma_kernel<3, ...>, likewise in a translation unit of its
+// own (micro_attention_mfma_fp4.hip) with the same flags.
+hipError_t launch_micro_mfma_fp4(int D, int G, const MicroParams& p, hipStream_t stream);
 
 }  // namespace da

@@ -412,3 +412,57 @@ def test_fused_workspace_clean_prefix_bookkeeping():
     assert int(buf[:64].count_nonzero()) == 0 and int((buf[64:] == 3).sum()) == 192
     big = w.get("cpu", 1024, 64)                # too small: a fresh zeroed buffer
     assert big is not buf and big.numel() == 1024 and int(big.count_nonzero()) == 0
+
+
+def _call_quant_step(fn, sh, **ptrs):
+    p = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, table=FAKE, lens=FAKE, bounds=FAKE,
+             MA=FAKE, m=FAKE, e=FAKE)
+    p.update(ptrs)
+    return fn(ctypes.byref(sh), *[_vp(p[k]) for k in ("q", "kc", "ks", "vc", "vs", "table", "lens",
+                                                      "bounds")],
+              None, _vp(p["MA"]), _vp(p["m"]), _vp(p["e"]), None, 0, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=dict(dtype=_lib.DA_BF16)), _lib.DA_ERR_INVALID_ARG),       # needs DA_FP4_E2M1
+    (dict(shape=dict(dtype=_lib.DA_FP8_E4M3)), _lib.DA_ERR_INVALID_ARG),   # the 8-bit type
+    (dict(ptrs=dict(ks=None)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(vs=FAKE + 2)), _lib.DA_ERR_INVALID_ARG),
+    (dict(ptrs=dict(kc=FAKE + 8)), _lib.DA_ERR_INVALID_ARG),                # codes 16-byte aligned
+    (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
+    (dict(shape=dict(D=64, P=16, Hq=2, Hkv=2)), _lib.DA_ERR_UNSUPPORTED),  # D 64, G 1 needs P >= 32
+], ids=lambda x: str(x))
+def test_micro_attention_fp4_rejects(lib, case, status):
+    sh = good_shape(**{"dtype": _lib.DA_FP4_E2M1, **case.get("shape", {})})
+    got = _call_quant_step(lib.da_micro_attention_fp4, sh, **case.get("ptrs", {}))
+    assert got == status, (got, lib.da_last_error())
+
+
+def test_fp8_entry_rejects_fp4_pages(lib):
+    sh = good_shape(dtype=_lib.DA_FP4_E2M1)
+    assert _call_quant_step(lib.da_micro_attention_fp8, sh) == _lib.DA_ERR_INVALID_ARG
+    assert b"DA_FP8_E4M3" in lib.da_last_error()
+    sh = good_shape(dtype=_lib.DA_FP4_E2M1)
+    assert call_micro(lib, sh) == _lib.DA_ERR_INVALID_ARG  # the bf16 / fp32 entry point
+
+
+def test_quantize_rows_fp4_rejects(lib):
+    assert lib.da_quantize_rows_fp4(_lib.DA_BF16, 4, 96, _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                    None) == _lib.DA_ERR_UNSUPPORTED
+    assert lib.da_quantize_rows_fp4(7, 4, 128, _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                    None) == _lib.DA_ERR_INVALID_ARG
+    # 4-bit codes only need 4-byte alignment (a lane writes one word), not 8
+    assert lib.da_quantize_rows_fp4(_lib.DA_BF16, 4, 128, _vp(FAKE), _vp(FAKE + 2), _vp(FAKE),
+                                    None) == _lib.DA_ERR_INVALID_ARG
+    assert lib.da_quantize_rows_fp4(_lib.DA_BF16, 0, 128, None, None, None, None) == _lib.DA_OK
+
+
+def test_fp4_workspace_size_counts_packed_rows(lib):
+    """The chunk heuristic prices a 4-bit row at D / 2 + 4 bytes: the same
+    shape is cut at most as much as over 8-bit pages."""
+    n4, n8 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    sh4 = good_shape(S=8, Hq=32, Hkv=8, max_pages=8193, max_splits=16, P=64, dtype=_lib.DA_FP4_E2M1)
+    sh8 = good_shape(S=8, Hq=32, Hkv=8, max_pages=8193, max_splits=16, P=64, dtype=_lib.DA_FP8_E4M3)
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh4), ctypes.byref(n4)) == _lib.DA_OK
+    assert lib.da_micro_attention_workspace_size(ctypes.byref(sh8), ctypes.byref(n8)) == _lib.DA_OK
+    assert 0 < n4.value <= n8.value

@@ -1,0 +1,345 @@
+"""4-bit (FP4 E2M1) KV pages through the C ABI (da_quantize_rows_fp4,
+da_append_kv_fp4, da_micro_attention_fp4, da_attention_fp4) against the fp64
+oracles on the same seeded inputs.  Needs an MI355X and the built libda.so.
+
+Bars: packed codes and scales are integer / fp32-decided work and are
+compared bit for bit with the oracle's quantization (both take the rounding
+decision in fp32); attention over the quantized pages is compared with the
+oracle's attention over the exactly dequantized values at the bf16 tolerance
+(max-abs 2e-3 on the output; m_j, e_j, MA_j / e_j as for bf16 pages): the GPU
+reads the same codes and scales, widens them exactly and accumulates in
+fp32, so only the accumulation order differs.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.quant4 as oq
+from harness import compare_out, compare_partials
+from long_context_decode_microattention_amd import _lib
+from long_context_decode_microattention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-3
+
+
+def announce(*parts):
+    print("[gpu-case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_rows_fp4_bit_exact(dtype, D):
+    """Random rows at several magnitudes, an all-zero row, a row with one
+    non-zero, rows whose quotients x / s land exactly on the E2M1 midpoints
+    (ties to mantissa 0), tiny and huge magnitudes, negative values that round
+    to zero."""
+    announce("quantize fp4", dtype, D)
+    rng = np.random.default_rng(2 * D + (dtype == "f32"))
+    rows = (rng.standard_normal((300, D)) * rng.choice([1e-20, 1e-3, 1.0, 40.0, 1e20], (300, 1)))
+    rows[0] = 0.0
+    rows[1] = 0.0
+    rows[1, 5] = -3.0
+    ties = np.zeros(D)
+    # s = 1: y = 6 (max), then every midpoint of the grid, both signs, and -1e-3
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    ties[0] = 6.0
+    ties[1:1 + len(mids)] = mids
+    ties[1 + len(mids):1 + 2 * len(mids)] = [-x for x in mids]
+    ties[1 + 2 * len(mids)] = -1e-3
+    rows[2] = ties
+    rows[3] = np.linspace(-1, 1, D)
+    x = torch.from_numpy(rows.astype(np.float32))
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    x = x.to(DEV)
+    codes, scales = _lib.quantize_rows_fp4(x)
+    torch.cuda.synchronize()
+    want_c, want_s = oq.quantize_rows(wl.host(x))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), "scales"
+    bad = np.argwhere(codes.cpu().numpy() != want_c)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()}"
+
+
+# Reduced workloads with bf16 queries: the head shapes, page sizes, split
+# rules and structure of the full ones, and every slab length the 4-bit
+# kernels take (16, 32 and 64 tokens; vector kernel for one query head per KV
+# head, matrix cores for groups).
+CASES = {
+    "C1_bf16_P32": wl.CONFIGS["C1"].replace(dtype=wl.BF16, P=32),
+    "C2": wl.CONFIGS["C2"].replace(S=2),
+    "C3": wl.CONFIGS["C3"].replace(S=6, Hq=8, Hkv=8),
+    "C4": wl.CONFIGS["C4"].replace(Hq=8, Hkv=8, lens=("fixed", 32768 + 21)),
+    "C4_P32_D64": wl.CONFIGS["C4"].replace(Hq=4, Hkv=4, D=64, P=32, lens=("fixed", 8192 + 9)),
+    "C4_P256": wl.CONFIGS["C4"].replace(Hq=4, Hkv=4, P=256, lens=("fixed", 256 * 20 + 77),
+                                        splits=("equal", 5)),
+    "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 32768)),
+    "C5_G2_D64": wl.CONFIGS["C5"].replace(S=2, Hq=16, D=64, lens=("fixed", 8192 + 7)),
+    "C5_G8": wl.CONFIGS["C5"].replace(S=1, Hq=64, lens=("fixed", 8192 + 50)),
+    "C5_P32": wl.CONFIGS["C5"].replace(S=2, P=32, lens=("fixed", 16384 + 13)),
+    "C5_P16_G4": wl.CONFIGS["C5"].replace(S=2, P=16, lens=("fixed", 8192 + 5)),
+    "C5_P128_G2": wl.CONFIGS["C5"].replace(S=2, Hq=16, P=128, lens=("fixed", 16384 + 77)),
+    "C4_G4_P32_mid": wl.CONFIGS["C4"].replace(Hq=8, Hkv=2, P=32, lens=("fixed", 8192 + 21),
+                                               splits=("equal", 7)),
+}
+
+
+def _quantized(b):
+    """GPU quantization of the batch's pools, checked bit for bit against
+    the oracle's; returns the device codes / scales and the host dequantized
+    pools (float64) for the oracle's attention."""
+    kc, ks = _lib.quantize_rows_fp4(b.k_pages)
+    vc, vs = _lib.quantize_rows_fp4(b.v_pages)
+    torch.cuda.synchronize()
+    okc, oks = oq.quantize_rows(wl.host(b.k_pages))
+    ovc, ovs = oq.quantize_rows(wl.host(b.v_pages))
+    assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(vc.cpu().numpy(), ovc)
+    assert np.array_equal(ks.cpu().numpy(), oks) and np.array_equal(vs.cpu().numpy(), ovs)
+    return (kc, ks, vc, vs), (oq.dequantize(okc, oks), oq.dequantize(ovc, ovs))
+
+
+def _run(b, dev_q, chunks=0, workspace=None):
+    kc, ks, vc, vs = dev_q
+    MA, m, e = _lib.micro_attention_fp4(b.q, kc, ks, vc, vs, b.block_table, b.seq_lens,
+                                        b.split_bounds, b.block_mask, scale=b.scale, chunks=chunks,
+                                        workspace=workspace, pool_layout=b.layout)
+    out = _lib.merge(MA, m, e)
+    torch.cuda.synchronize()
+    return out, MA, m, e
+
+
+def _oracle_out(b, kd, vd):
+    h = wl.host
+    mask = None if b.block_mask is None else h(b.block_mask)
+    return oracle.attention(h(b.q), kd, vd, h(b.block_table), h(b.seq_lens), block_mask=mask,
+                            scale=b.scale)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("cfg", sorted(CASES))
+def test_fp4_attention_parity(cfg, seed):
+    spec = CASES[cfg]
+    announce("fp4 attention", cfg, "seed", seed)
+    b = wl.build(spec, seed, DEV)
+    dev_q, (kd, vd) = _quantized(b)
+    out, MA, m, e = _run(b, dev_q)
+    h = wl.host
+    args = (h(b.q), kd, vd, h(b.block_table), h(b.seq_lens))
+    mask = None if b.block_mask is None else h(b.block_mask)
+    compare_out(out.cpu().numpy(), _oracle_out(b, kd, vd), TOL, f"{cfg}/{seed} out")
+    oMA, om, oe = oracle.micro_attention(*args, h(b.split_bounds), block_mask=mask, scale=b.scale)
+    compare_partials(MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy(), oMA, om, oe, TOL,
+                     f"{cfg}/{seed} partials")
+
+
+@pytest.mark.parametrize("chunks", [1, 3, 7])
+@pytest.mark.parametrize("cfg", ["C4", "C5"])
+def test_fp4_forced_chunks(cfg, chunks):
+    spec = CASES[cfg]
+    announce("fp4 chunks", cfg, chunks)
+    b = wl.build(spec, 2, DEV)
+    dev_q, (kd, vd) = _quantized(b)
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)
+    out, *_ = _run(b, dev_q, chunks=chunks, workspace=ws)
+    compare_out(out.cpu().numpy(), _oracle_out(b, kd, vd), TOL, f"{cfg} chunks={chunks}")
+
+
+@pytest.mark.parametrize("cfg", ["C4", "C5", "C5_G2_D64", "C2"])
+def test_fp4_unread_slots_poisoned(cfg):
+    """Arbitrary codes and NaN scales in every slot no split reads (past L_s
+    in the last page, masked pages, pages no table names): the output must
+    not change."""
+    spec = CASES[cfg].replace(extra_pages=3, table="shuffled")
+    announce("fp4 poison", cfg)
+    b = wl.build(spec, 3, DEV)
+    (kc, ks, vc, vs), (kd, vd) = _quantized(b)
+    h = wl.host
+    table, lens = h(b.block_table), h(b.seq_lens)
+    mask = None if b.block_mask is None else h(b.block_mask)
+    P = spec.P
+    read = np.zeros(ks.shape, dtype=bool)  # [NP, Hkv, P]
+    for s in range(spec.S):
+        L = int(lens[s])
+        for lp in range(-(-L // P)):
+            for kvh in range(spec.Hkv):
+                if mask is not None and not mask[s, kvh, lp]:
+                    continue
+                n = min(P, L - lp * P)
+                read[table[s, lp], kvh, :n] = True
+    unread = torch.from_numpy(~read).to(DEV)
+    for c in (kc, vc):
+        c[unread] = 0x77  # the largest code in both nibbles
+    for sc in (ks, vs):
+        sc[unread] = float("nan")
+    out, *_ = _run(b, (kc, ks, vc, vs))
+    want = oracle.attention(h(b.q), kd, vd, table, lens, block_mask=mask, scale=b.scale)
+    compare_out(out.cpu().numpy(), want, TOL, f"{cfg} poisoned")
+
+
+@pytest.mark.parametrize("fuse", [1, 2])
+@pytest.mark.parametrize("cfg", ["C2", "C4", "C5", "C5_G8"])
+def test_fp4_one_launch(cfg, fuse):
+    """da_attention_fp4 in both forms against da_micro_attention_fp4 +
+    da_merge (1e-5) and the oracle."""
+    spec = CASES[cfg]
+    announce("fp4 one launch", cfg, fuse)
+    b = wl.build(spec, 6, DEV)
+    (kc, ks, vc, vs), (kd, vd) = _quantized(b)
+    args = (b.q, kc, ks, vc, vs, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
+    out = _lib.attention_fp4(*args, scale=b.scale, pool_layout=b.layout, fuse=fuse)
+    ref, *_ = _run(b, (kc, ks, vc, vs))
+    assert float((out - ref).abs().max()) <= 1e-5
+    compare_out(out.cpu().numpy(), _oracle_out(b, kd, vd), TOL, f"fp4 one launch {cfg}")
+
+
+def test_fp4_head_major_pools_bitwise():
+    """Head-major code and scale pools give the page-major pools' partials
+    bit for bit (only addresses change)."""
+    spec = CASES["C5"]
+    announce("fp4 head-major")
+    b = wl.build(spec, 8, DEV)
+    (kc, ks, vc, vs), _ = _quantized(b)
+    MA, m, e = _lib.micro_attention_fp4(b.q, kc, ks, vc, vs, b.block_table, b.seq_lens,
+                                        b.split_bounds, b.block_mask, scale=b.scale)
+    hm = [t.transpose(0, 1).contiguous() for t in (kc, ks, vc, vs)]
+    MA2, m2, e2 = _lib.micro_attention_fp4(b.q, *hm, b.block_table, b.seq_lens, b.split_bounds,
+                                           b.block_mask, scale=b.scale, pool_layout="head")
+    torch.cuda.synchronize()
+    assert torch.equal(MA.nan_to_num(), MA2.nan_to_num()) and torch.equal(m, m2) and torch.equal(e, e2)
+
+
+def _host_append_fp4(codes, scales, table, lens, new_rows):
+    """Oracle of a 4-bit append: quantize the new rows, then write packed
+    codes and scales through the table (scales as one-element rows)."""
+    import oracle.decode as odec
+    c_new, s_new = oq.quantize_rows(new_rows)
+    c2, s2 = odec.append_kv(codes, scales[..., None], table, lens, c_new, s_new[..., None])
+    return c2, s2[..., 0]
+
+
+@pytest.mark.parametrize("cfg", ["C4", "C5", "C5_G2_D64"])
+def test_append_fp4_matches_oracle(cfg):
+    """Consecutive 4-bit appends across a page boundary: after every step the
+    packed code and scale pools equal the oracle's (quantize the new rows,
+    write them through the table) bit for bit; the statistics kept from the
+    bf16 key rows equal the oracle's statistics of the bf16 cache with the
+    same rows appended."""
+    import oracle.decode as odec
+    import oracle.selector as osel
+    spec = CASES[cfg].replace(reserve=24, table="shuffled", extra_pages=2)
+    announce("fp4 append", cfg)
+    b = wl.build(spec, 4, DEV)
+    (kc, ks, vc, vs), _ = _quantized(b)
+    h = wl.host
+    table = h(b.block_table)
+    okc, oks, ovc, ovs = h(kc), h(ks), h(vc), h(vs)
+    ok_bf16 = h(b.k_pages)
+    lens = b.seq_lens.clone()
+    logical = 16
+    flags = np.array([1 if i >= spec.Hkv // 2 else 0 for i in range(spec.Hkv)], dtype=np.uint8)
+    sel_t = torch.from_numpy(flags).to(DEV)
+    stats = _lib.page_stats(b.k_pages, b.block_table, lens, logical=logical, select_heads=sel_t)
+    on = flags.astype(bool)
+    for step in range(20):
+        kn, vn = wl.new_tokens(spec, 4, step, DEV)
+        _lib.append_kv_fp4(kn, vn, b.block_table, lens, kc, ks, vc, vs, stats=stats,
+                           logical=logical, select_heads=sel_t)
+        L = h(lens)
+        okc, oks = _host_append_fp4(okc, oks, table, L, h(kn))
+        ovc, ovs = _host_append_fp4(ovc, ovs, table, L, h(vn))
+        ok_bf16, _ = odec.append_kv(ok_bf16, ok_bf16, table, L, h(kn), h(kn))
+        lens += 1
+        torch.cuda.synchronize()
+        assert np.array_equal(h(kc), okc) and np.array_equal(h(vc), ovc), f"{cfg} step {step}: codes"
+        assert np.array_equal(h(ks), oks) and np.array_equal(h(vs), ovs), f"{cfg} step {step}: scales"
+        if step % 7 == 6 or step == 19:
+            want = osel.page_stats(ok_bf16, table, h(lens), logical=logical)
+            got = oracle.to_f64(h(stats.transpose(0, 1).contiguous()))
+            assert np.array_equal(got[:, on], want[:, on]), f"{cfg} step {step}: statistics"
+
+
+def test_fp4_decode_chunk():
+    """16 decode steps over 4-bit pages with a reused mask: split bounds once
+    (horizon 16), then per step a 4-bit append and the attention step; every
+    step's output matches the oracle's attention over the oracle's pools."""
+    chunk = 16
+    spec = CASES["C5"].replace(lens=("fixed", 64 * 40 + 57), reserve=chunk)
+    announce("fp4 decode chunk")
+    b = wl.build(spec, 5, DEV)
+    (kc, ks, vc, vs), _ = _quantized(b)
+    h = wl.host
+    table = h(b.block_table)
+    mask = b.block_mask.clone()
+    L0 = int(b.seq_lens[0].item())
+    mask[:, :, L0 // spec.P:-(-(L0 + chunk) // spec.P)] = 1
+    lens = b.seq_lens.clone()
+    bounds = _lib.split_bounds(mask, lens, P=spec.P, b=8, horizon=chunk)
+    okc, oks, ovc, ovs = h(kc), h(ks), h(vc), h(vs)
+    mask_h = h(mask)
+    for step in range(chunk):
+        kn, vn = wl.new_tokens(spec, 5, step, DEV)
+        _lib.append_kv_fp4(kn, vn, b.block_table, lens, kc, ks, vc, vs)
+        okc, oks = _host_append_fp4(okc, oks, table, h(lens), h(kn))
+        ovc, ovs = _host_append_fp4(ovc, ovs, table, h(lens), h(vn))
+        lens += 1
+        MA, m, e = _lib.micro_attention_fp4(b.q, kc, ks, vc, vs, b.block_table, lens, bounds, mask,
+                                            scale=b.scale)
+        out = _lib.merge(MA, m, e)
+        torch.cuda.synchronize()
+        want = oracle.attention(h(b.q), oq.dequantize(okc, oks), oq.dequantize(ovc, ovs), table,
+                                h(lens), block_mask=mask_h, scale=b.scale)
+        compare_out(out.cpu().numpy(), want, TOL, f"fp4 chunk step {step}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["C4", "C5"])
+def test_fp4_full_size_sampled(cfg):
+    """Full-size workload quantized on the GPU and run in the launch
+    configuration the benchmark times; sampled (request, KV head) units
+    against the oracle on those units alone."""
+    spec = wl.CONFIGS[cfg].replace(layout=wl.PREFERRED_LAYOUT.get(cfg, "page"))
+    announce("fp4 full", cfg, spec.layout)
+    b = wl.build(spec, 0, DEV)
+    kc, ks = _lib.quantize_rows_fp4(b.k_pages)
+    vc, vs = _lib.quantize_rows_fp4(b.v_pages)
+    out, *_ = _run(b, (kc, ks, vc, vs))
+    if b.layout == "head":  # page-major views for the host-side selection below
+        kc, ks, vc, vs = (t.transpose(0, 1) for t in (kc, ks, vc, vs))
+    h = wl.host
+    G, P = spec.G, spec.P
+    units = [(0, 0), (0, spec.Hkv - 1)] if spec.S == 1 else [(0, 5), (spec.S - 1, 2)]
+    for s, kvh in units:
+        announce("unit", s, kvh)
+        L = int(b.seq_lens[s].item())
+        n = -(-L // P)
+        pages = b.block_table[s, :n].long()
+        sub = lambda t: h(t[:, kvh:kvh + 1].index_select(0, pages).contiguous())  # noqa: E731
+        kc_u, vc_u = sub(kc), sub(vc)
+        ks_u, vs_u = sub(ks), sub(vs)
+        okc, oks = oq.quantize_rows(sub(b.k_pm))
+        assert np.array_equal(kc_u, okc) and np.array_equal(ks_u, oks), f"unit ({s},{kvh}) codes"
+        q = h(b.q[s:s + 1, kvh * G:(kvh + 1) * G].contiguous())
+        mask = None
+        if b.block_mask is not None:
+            mask = h(b.block_mask[s:s + 1, kvh:kvh + 1, :n].contiguous())
+        want = oracle.attention(q, oq.dequantize(kc_u, ks_u), oq.dequantize(vc_u, vs_u),
+                                np.arange(n, dtype=np.int32)[None], np.array([L], dtype=np.int32),
+                                block_mask=mask, scale=b.scale)
+        got = out[s:s + 1, kvh * G:(kvh + 1) * G].cpu().numpy()
+        compare_out(got, want, TOL, f"unit ({s},{kvh})")

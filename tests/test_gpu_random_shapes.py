@@ -3,7 +3,7 @@ draws the request count, head counts (G in {1, 2, 4, 8}), head dim, page
 size, dtype, length mix, block table, mask, split rule, chunk count,
 schedule and pool layout, then checks the two-call step (partials and
 output), the one-launch step and, for bf16 cases, the same pools quantized
-to 8 bits.  The draws come from a fixed seed, so every run checks the same
+to 8 and to 4 bits.  The draws come from a fixed seed, so every run checks the same
 cases; sizes keep the oracle at a fraction of a second per case.  Needs an
 MI355X and the built libda.so.
 """
@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import oracle.quant as oq
+import oracle.quant4 as oq4
 from harness import TOL_OUT, compare_out, compare_partials, host_inputs, oracle_micro, oracle_out
 from long_context_decode_microattention_amd import _lib
 from long_context_decode_microattention_amd import workloads as wl
@@ -106,3 +107,20 @@ def test_random_shape(i):
     want8 = oracle.attention(inp["q"], kd, vd, inp["block_table"], inp["seq_lens"],
                              block_mask=inp["block_mask"], scale=b.scale)
     compare_out(out8.cpu().numpy(), want8, tol, f"case {i} 8-bit out")
+    # and in 4 bits (D = 64 with one query head per KV head needs pages of 32
+    # tokens or more)
+    if spec.D == 64 and spec.G == 1 and spec.P < 32:
+        return
+    kc4, ks4 = _lib.quantize_rows_fp4(b.k_pages)
+    vc4, vs4 = _lib.quantize_rows_fp4(b.v_pages)
+    args4 = (b.q, kc4, ks4, vc4, vs4, b.block_table, b.seq_lens, b.split_bounds, b.block_mask)
+    MA4, m4, e4 = _lib.micro_attention_fp4(*args4, scale=b.scale, chunks=chunks,
+                                           schedule=schedule, workspace=ws, pool_layout=b.layout)
+    out4 = _lib.merge(MA4, m4, e4)
+    torch.cuda.synchronize()
+    if b.layout == "head":
+        kc4, ks4, vc4, vs4 = (t.transpose(0, 1).contiguous() for t in (kc4, ks4, vc4, vs4))
+    want4 = oracle.attention(inp["q"], oq4.dequantize(h(kc4), h(ks4)),
+                             oq4.dequantize(h(vc4), h(vs4)), inp["block_table"], inp["seq_lens"],
+                             block_mask=inp["block_mask"], scale=b.scale)
+    compare_out(out4.cpu().numpy(), want4, tol, f"case {i} 4-bit out")
