@@ -1,8 +1,8 @@
-// MicroAttention on the matrix cores, for bf16 or FP8 K/V with G = 2, 4 or 8
-// query heads per KV head (grouped-query attention).  Same per-item result as the
-// vector kernel -- m_j, e_j and MA_j of the MicroAttention equations
-// (Infinite-LLM page, section 方法细节) for every query head of the group --
-// with the page list, slabs and block-mask skipping of that kernel.
+// MicroAttention on the matrix cores, for bf16, FP8 or FP4 K/V with G = 2, 4
+// or 8 query heads per KV head (grouped-query attention).  Same per-item
+// result as the vector kernel -- m_j, e_j and MA_j of the MicroAttention
+// equations (Infinite-LLM page, section 方法细节) for every query head of the
+// group -- with the page list, slabs and block-mask skipping of that kernel.
 //
 // With G query heads per KV head the scores and the value sums are small
 // dense contractions, and on the vector ALUs they cost about 3 instructions
@@ -20,7 +20,8 @@
 //            row, read out as wave-uniform values; the running maximum is
 //            per wave, so the value accumulators are rescaled only when a
 //            head's maximum rises (wave-uniform branch).
-//   values   on v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4x4, K = 1): block
+//   values   (bf16 pages, and any page type at D = 64) on
+//            v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4x4, K = 1): block
 //            b = l/4 takes A = p of heads 0..3 from lanes 4b..4b+3 and B = one
 //            value element from each of its 4 lanes, so the values are used
 //            in the coalesced layout of the vector kernel (lane l holds 8
@@ -29,21 +30,25 @@
 //            probabilities move from the score layout to that operand
 //            layout through an SL x G float scratch in LDS per wave.
 //
-// fp8 (E4M3) pages with per-row scales take the same path: a lane's key codes
-// (8 dims per score step, the steps of a lane now contiguous: dims
-// grp*D/4 + 8*step, q in the same order) are widened exactly to bf16 for the
-// score MFMA and the score column is multiplied by its token's K scale; the
-// value codes (8 per lane, 8-byte loads in the same row layout) are widened
-// exactly to fp32.  A token's V scale multiplies its probabilities in the
+// fp8 (E4M3) and fp4 (E2M1) pages with per-row scales take the same score
+// path: a lane's key codes (8 dims per score step, the steps of a lane now
+// contiguous: dims grp*D/4 + 8*step, q in the same order) are widened exactly
+// to bf16 for the score MFMA and the score column is multiplied by its
+// token's K scale.  A token's V scale multiplies its probabilities in the
 // score layout (where the lane of token `col` loads it next to the K scale),
 // so the value operand arrives in LDS already scaled; the exp-sums take the
-// unscaled probabilities.  With pages of 32 tokens or more (and G <= 4) an
-// 8-bit slab is 32 tokens, two score groups of 16 under one running-max
-// update and one LDS round trip: 8 KiB of K + V, like a bf16 slab.
+// unscaled probabilities.  Their value sums at D = 128 run on the dense bf16
+// MFMA instead (dense_values below): with 4 or 8 times fewer bytes per token
+// than bf16 pages, the 4x4x1 value product took 20-30% of every SIMD's
+// cycles on the matrix pipe.  An 8-bit slab is 32 tokens with pages of 32
+// tokens or more (G <= 4), two score groups of 16 under one running-max
+// update and one LDS round trip (8 KiB of K + V, like a bf16 slab); a 4-bit
+// slab is 64 tokens (four score groups) likewise.
 //
 // The kernel template lives in this header; micro_attention_mfma.hip launches
-// the bf16 instances and micro_attention_mfma_fp8.hip the 8-bit ones, which
-// are built with different floating-point flags.
+// the bf16 instances, micro_attention_mfma_fp8.hip the 8-bit ones and
+// micro_attention_mfma_fp4.hip the 4-bit ones, the last two built with
+// different floating-point flags.
 #pragma once
 
 #include "micro_common.h"
@@ -135,6 +140,131 @@ __device__ __forceinline__ float lane_value(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
 }
 
+// Value product of the quantized pages (D = 128) on the dense bf16 MFMA.
+//
+// A lane's value loads already hold what a B operand wants: load i gives lane
+// l the 8 dims 8*(l%16) .. +7 of token 4i + l/16, so over a block of KB = 32
+// (or 16) tokens the lane holds, for each of its dims, KB/4 tokens.  Taking
+// column n = l%16 as dim 8n + e, v_mfma_f32_16x16x32_bf16 number e (e = 0..7)
+// sums the block for dims 8n + e: its B operand is element e of the lane's 8
+// loads, gathered into bf16 pairs (codes of two tokens side by side by a byte
+// or nibble permutation, then one exact widening each), and its A operand is
+// the probabilities of the same tokens, read from the per-wave LDS buffer
+// where they are stored head-major with each block's tokens ordered by
+// (token % 4, token / 4), so that a lane's KB/4 values are contiguous.
+//
+// The probabilities are fp32 (with the token's V scale folded in).  Each is
+// split into a bf16 high part and the bf16 rounding of the remainder (the
+// pair carries 16 significant bits, relative error <= 2^-17); with G query
+// heads the high parts fill A rows 0 .. G-1 and the low parts rows G ..
+// 2G-1 of the same instruction (16 rows, G <= 8), so the split costs no extra
+// matrix work: output row r accumulates head r % G, and the two rows of a
+// head are added once per item.  Per 32 tokens: 8 MFMA (128 busy cycles)
+// instead of 64 v_mfma_f32_4x4x1f32 (512).
+template <int DT, int D>
+inline constexpr bool kDenseValues = DT >= 2 && D == 128;
+
+template <int DT, int D, int G, int SL>
+__device__ __forceinline__ void dense_values(const float* sp, const MFrag<DT, D, SL>& f,
+                                             f32x4_t (&acc)[8]) {
+  static_assert(kDenseValues<DT, D>, "dense value product: quantized pages, D = 128");
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  constexpr int KB = SL < 32 ? SL : 32;  // tokens per block
+  constexpr int KK = KB / 4;             // operand elements per lane
+  constexpr int KW = KK / 2;             // operand words per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = lane & 15;
+  const float* src = sp + (row % G) * SL + KK * (lane >> 4);
+#pragma unroll
+  for (int b = 0; b < SL / KB; ++b) {
+    // A: probabilities of head row % G, tokens KB*b + 4*kk + lane/16
+    float x[KK];
+#pragma unroll
+    for (int q = 0; q < KK / 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4*>(src + KB * b + 4 * q);
+      x[4 * q] = t.x;
+      x[4 * q + 1] = t.y;
+      x[4 * q + 2] = t.z;
+      x[4 * q + 3] = t.w;
+    }
+    uint32_t a[KW];
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const f32x2_t v = {x[2 * j], x[2 * j + 1]};
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+      const f32x2_t rest = {x[2 * j] - bf16_lo(hi), x[2 * j + 1] - bf16_hi(hi)};
+      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));
+      a[j] = row < G ? hi : (row < 2 * G ? lo : 0u);
+    }
+    // B of instruction e: element e of loads KK*b + 2j and KK*b + 2j + 1 in
+    // word j.  The codes of each load pair are first interleaved (pk[.][j]),
+    // then widened one instruction's operand at a time, so that few operand
+    // words are live at once.
+    auto mfma = [&](int e, const uint32_t (&bw)[KW]) {
+      if constexpr (KB == 32) {
+        const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+        const uint4 bq = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, bq), acc[e], 0,
+                                                        0, 0);
+      } else {
+        const uint2 av = make_uint2(a[0], a[1]);
+        const uint2 bq = make_uint2(bw[0], bw[1]);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, av),
+                                                          __builtin_bit_cast(s16x4_t, bq), acc[e],
+                                                          0, 0, 0);
+      }
+    };
+    if constexpr (DT == 2) {
+      // word w of each load: bytes (a_q, c_q) side by side -> dims 4w + q
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        uint32_t pk[2][KW];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          const int i0 = KK * b + 2 * j;
+          const uint32_t wa = w ? f.v8[i0].y : f.v8[i0].x;
+          const uint32_t wc = w ? f.v8[i0 + 1].y : f.v8[i0 + 1].x;
+          pk[0][j] = __builtin_amdgcn_perm(wc, wa, 0x05010400u);  // a0 c0 a1 c1
+          pk[1][j] = __builtin_amdgcn_perm(wc, wa, 0x07030602u);  // a2 c2 a3 c3
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t bw[KW];
+#pragma unroll
+          for (int j = 0; j < KW; ++j)
+            bw[j] = (q & 1) ? fp8x2_to_bf16x2<true>(pk[q >> 1][j]) : fp8x2_to_bf16x2<false>(pk[q >> 1][j]);
+          mfma(4 * w + q, bw);
+        }
+      }
+    } else {
+      // byte q: the (a, c) codes of element 2q (even word) or 2q + 1 (odd word)
+      uint32_t pk[2][KW];
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        const uint32_t wa = f.v4[KK * b + 2 * j], wc = f.v4[KK * b + 2 * j + 1];
+        pk[0][j] = (wa & 0x0F0F0F0Fu) | ((wc & 0x0F0F0F0Fu) << 4);
+        pk[1][j] = ((wa >> 4) & 0x0F0F0F0Fu) | (wc & 0xF0F0F0F0u);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t bw[KW];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          const uint32_t src = pk[e & 1][j];
+          switch (e >> 1) {
+            case 0: bw[j] = fp4x2_to_bf16x2<0>(src); break;
+            case 1: bw[j] = fp4x2_to_bf16x2<1>(src); break;
+            case 2: bw[j] = fp4x2_to_bf16x2<2>(src); break;
+            default: bw[j] = fp4x2_to_bf16x2<3>(src); break;
+          }
+        }
+        mfma(e, bw);
+      }
+    }
+  }
+}
+
 // Two waves per SIMD: the register budget that holds the prefetched slab, the
 // query operand and the accumulators without spilling (measured faster than
 // three waves with spills).
@@ -144,10 +274,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   using L = MLayout<DT, D, SL>;
   constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
   static_assert(G == 2 || G == 4 || G == 8, "group size");
+  constexpr bool kDense = kDenseValues<DT, D>;
+  constexpr int KB = SL < 32 ? SL : 32;  // tokens per dense value block
   __shared__ int s_phys[kPageCap];
   __shared__ int s_lp[kPageCap];
   __shared__ int s_cnt[kMicroWaves];
-  __shared__ float s_p[kMicroWaves][SL * G];
+  __shared__ __align__(16) float s_p[kMicroWaves][SL * G];
   __shared__ FinishLds<G, D> s_fin;
 
   const int tid = threadIdx.x;
@@ -184,13 +316,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 
     float m_h[G];        // running raw-dot maximum per head (wave-uniform)
     float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
-    f32x4_t acc[HS][8];  // value sums: block layout, register i = head 4*hs + i
+    // value sums.  4x4 blocks: acc[hs][k] register i = head 4*hs + i, dim k
+    // of the lane's 8.  Dense form: acc[0][e] = the 16 x 16 output tile of
+    // dims 8n + e (column n = lane % 16); register i holds row 4*(lane/16) + i
+    // (rows < G: the high parts of the probabilities, G .. 2G - 1: the low
+    // parts, the rest zero)
+    f32x4_t acc[kDense ? 1 : HS][8];
   #pragma unroll
     for (int h = 0; h < G; ++h) m_h[h] = neg_inf();
   #pragma unroll
     for (int i = 0; i < 4; ++i) e_l[i] = 0.f;
   #pragma unroll
-    for (int hs = 0; hs < HS; ++hs)
+    for (int hs = 0; hs < (kDense ? 1 : HS); ++hs)
   #pragma unroll
       for (int k = 0; k < 8; ++k) acc[hs][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -403,20 +540,50 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             for (int g = 0; g < L::NG; ++g)
   #pragma unroll
               for (int i = 0; i < 4; ++i)
-                if (4 * grp + i < G)
-                  sp[(16 * g + col) * G + 4 * grp + i] = DT >= 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
+                if (4 * grp + i < G) {
+                  const float pv = DT >= 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
+                  if constexpr (kDense) {
+                    // head-major, each value block's tokens ordered by
+                    // (token % 4, token / 4) so that a lane's operand is
+                    // contiguous
+                    const int t = 16 * g + col;
+                    const int tb = t % KB;
+                    sp[(4 * grp + i) * SL + (t - tb) + (KB / 4) * (tb & 3) + (tb >> 2)] = pv;
+                  } else {
+                    sp[(16 * g + col) * G + 4 * grp + i] = pv;
+                  }
+                }
           }
 
           if (wave_any(moved)) {  // scalar branch: skipped, not masked
+            if constexpr (kDense) {
+              // row 4*(lane/16) + i belongs to head (row % G)
+              float al[4];
   #pragma unroll
-            for (int hs = 0; hs < HS; ++hs)
+              for (int i = 0; i < 4; ++i) {
+                al[i] = alpha_h[i % G];
+                if constexpr (G > 4) {
+                  if (grp & 1) al[i] = alpha_h[4 + i];
+                }
+              }
   #pragma unroll
               for (int k = 0; k < 8; ++k)
   #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
+                for (int i = 0; i < 4; ++i) acc[0][k][i] *= al[i];
+            } else {
+  #pragma unroll
+              for (int hs = 0; hs < HS; ++hs)
+  #pragma unroll
+                for (int k = 0; k < 8; ++k)
+  #pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    if (4 * hs + i < G) acc[hs][k][i] *= alpha_h[4 * hs + i];
+            }
           }
 
+          if constexpr (kDense) {
+            dense_values<DT, D, G, SL>(sp, f, acc[0]);
+          } else {
           // value sums: acc[hs][k] += p[4hs + i][token] * v[token][dim k of this lane]
   #pragma unroll
           for (int j = 0; j < L::NI; ++j) {
@@ -445,6 +612,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
               for (int hs = 0; hs < HS; ++hs)
                 acc[hs][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hs], vf[k], acc[hs][k], 0, 0, 0);
             }
+          }
           }
         };
 
@@ -504,10 +672,26 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       we[h] = lane_value(x, 16 * (h >> 2));
     }
     float accg[G][8];
+    if constexpr (kDense) {
+      // each head's high and low rows, summed over the lanes of a column below
   #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
   #pragma unroll
-      for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
+        for (int k = 0; k < 8; ++k) {
+          if constexpr (G == 2) {
+            accg[h][k] = acc[0][k][h] + acc[0][k][h + 2];
+          } else if constexpr (G == 4) {
+            accg[h][k] = acc[0][k][h];
+          } else {
+            accg[h][k] = ((grp & 1) == (h >> 2)) ? acc[0][k][h & 3] : 0.f;
+          }
+        }
+    } else {
+  #pragma unroll
+      for (int h = 0; h < G; ++h)
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) accg[h][k] = acc[h >> 2][k][h & 3];
+    }
   #pragma unroll
     for (int off = L::LPT; off < kWave; off <<= 1)
   #pragma unroll
