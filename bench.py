@@ -69,7 +69,8 @@ def parse():
     ap.add_argument("--workload", default="C4", help="headline workload (C1..C5)")
     ap.add_argument("--secondary", default="C5,C4_fp8,C5_fp8,C4_fp4,C5_fp4,C1,C2,C3",
                     help="comma list reported beside it ('_fp8' / '_fp4': over 8- / 4-bit "
-                         "pages), or ''")
+                         "pages; ':dense' / ':masked': only the dense or only the masked KV "
+                         "heads of C5), or ''")
     ap.add_argument("--seed", default="0",
                     help="seed(s) of the synthetic inputs, comma list; one record per (workload, seed)")
     ap.add_argument("--settle", type=float, default=1.0,
@@ -116,7 +117,11 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     """Times the decode step of workload `key`; a "_fp8" / "_fp4" suffix runs
     it over 8- / 4-bit pages made from the workload's bf16 pools by
     da_quantize_rows / da_quantize_rows_fp4 (quantization is untimed: it
-    belongs to the cache write).  With
+    belongs to the cache write).  A ":dense" / ":masked" suffix keeps only
+    the KV heads a block-masked workload leaves dense, or only those it masks
+    (the others' mask rows are cleared, so their items hold no pages and
+    their bytes are not counted): the two halves of the step, measured
+    apart.  With
     flush_mib > 0 a buffer of that size is overwritten before every timed
     step (outside the events) and the step time is the median; otherwise the
     steps run back to back and the step time is their mean."""
@@ -125,15 +130,25 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     from long_context_decode_microattention_amd import _lib
     from long_context_decode_microattention_amd import workloads as wl
 
-    bits = 8 if key.endswith("_fp8") else 4 if key.endswith("_fp4") else 16
+    name, _, heads = key.partition(":")
+    bits = 8 if name.endswith("_fp8") else 4 if name.endswith("_fp4") else 16
     fp8 = bits < 16
-    base = key[:-4] if fp8 else key
+    base = name[:-4] if fp8 else name
     spec = wl.CONFIGS[base].replace(layout=wl.PREFERRED_LAYOUT.get(base, "page"))
     t0 = time.time()
     b = wl.build(spec, seed, dev)
     torch.cuda.synchronize()
     log(f"[bench] built {key} seed {seed} in {time.time() - t0:.1f}s: NP={b.k_pm.shape[0]}")
     S, Hq, D, B = spec.S, spec.Hq, spec.D, b.max_splits
+    if heads:
+        if spec.mask is None or heads not in ("dense", "masked"):
+            raise ValueError(f"{key}: ':dense' / ':masked' need a block-masked workload")
+        masked = [h >= spec.Hkv // 2 for h in range(spec.Hkv)]  # the mask covers the upper half
+        for h in range(spec.Hkv):
+            if masked[h] != (heads == "masked"):
+                b.block_mask[:, h, :] = 0
+                for s in range(S):
+                    b.kept_pages[s * spec.Hkv + h] = b.kept_pages[s * spec.Hkv + h][:0]
     kept = int(b.kept_tokens().sum())
     if fp8:
         quant = _lib.quantize_rows if bits == 8 else _lib.quantize_rows_fp4
@@ -222,7 +237,8 @@ def time_workload(key, steps, warmup, dev, seed=0, settle=1.0, flush_mib=0):
     fused_diff = float((out_f - out).abs().max())
     assert fused_diff <= 1e-4, f"one-launch step differs from the two calls by {fused_diff}"
     res = dict(
-        workload=spec.name, key=key, seed=seed, kv_bytes=kv_bytes, ms_per_step=ms_step,
+        workload=spec.name + (f" ({heads} KV heads only)" if heads else ""), key=key, seed=seed,
+        kv_bytes=kv_bytes, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, us_micro=avg_micro * 1e3, us_merge=avg_merge * 1e3,
         us_per_step_median=_median(step_ms) * 1e3,
         us_micro_min=min(micro_ms) * 1e3, merge_share=avg_merge / (avg_micro + avg_merge),
@@ -305,16 +321,19 @@ def time_selector(b, steps, warmup, dev, logical=16):
         select()
         topk()
     torch.cuda.synchronize()
-    evs = [ev() for _ in range(3 * steps)]
-    for i in range(steps):
-        evs[3 * i].record()
+    # each kernel timed over `steps` launches back to back (idempotent calls),
+    # so the figure is its own rate, not that of one launch between two events
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record()
+    for _ in range(steps):
         select()
-        evs[3 * i + 1].record()
+    e1.record()
+    for _ in range(steps):
         topk()
-        evs[3 * i + 2].record()
+    e2.record()
     torch.cuda.synchronize()
-    us_scores = sum(evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(steps)) * 1e3 / steps
-    us_topk = sum(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(steps)) * 1e3 / steps
+    us_scores = e0.elapsed_time(e1) * 1e3 / steps
+    us_topk = e1.elapsed_time(e2) * 1e3 / steps
     # bytes the score kernel must move: the statistics of the selected KV
     # heads' pages below L_s, plus one fp32 score per (request, KV head, page)
     score_bytes = sp.S * n_sel * npg * NL * 2 * D * esize + sp.S * Hkv * max_pages * 4
@@ -654,13 +673,14 @@ def run(a, seeds):
     check = not a.no_cpu_baseline
 
     def flush_for(key):
-        return a.flush_mib if key.split("_")[0] in FLUSHED else 0
+        return a.flush_mib if key.split(":")[0].split("_")[0] in FLUSHED else 0
 
     head, cpu, ceiling, head_selector = None, None, None, None
     records = []
     for seed in seeds:
         b, r = time_workload(a.workload, a.steps, a.warmup, dev, seed, a.settle, flush_for(a.workload))
-        bf16_pools = b.k_pages is not None  # an "_fp8" headline keeps only the 8-bit pools
+        # an "_fp8" headline keeps only the 8-bit pools; a half (":dense") is not checked
+        bf16_pools = b.k_pages is not None and ":" not in a.workload
         if check and bf16_pools:
             oc = oracle_check(b, f"{a.workload}/{seed}", one_core_units=2)
             r["oracle_check"] = oc
@@ -685,14 +705,15 @@ def run(a, seeds):
         for seed in seeds:
             b2, r2 = time_workload(key, a.steps, a.warmup, dev, seed, a.settle, flush_for(key))
             r2["traffic"] = measured_traffic(key) if seed == 0 else None
-            if check and b2.k_pages is not None:
+            if check and b2.k_pages is not None and ":" not in key:
                 base = key.split("_")[0]
                 r2["oracle_check"] = oracle_check(b2, f"{key}/{seed}",
                                                   one_core_units=(10**9 if base in ("C1", "C2") else 0))
             records.append(r2)
             if seed == seeds[0]:
                 secondary[key] = r2
-                if b2.spec.mask is not None and not a.no_selector and b2.k_pages is not None:
+                if b2.spec.mask is not None and not a.no_selector and b2.k_pages is not None \
+                        and ":" not in key:
                     secondary[key + "_selector"] = time_selector(b2, a.steps, a.warmup, dev)
                     secondary[key + "_selector"]["decode_loop"] = time_decode_chunks(b2, a.chunks, dev)
             del b2
