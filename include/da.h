@@ -98,8 +98,8 @@ typedef struct da_shape {
                            /* this many page ranges, processed independently   */
                            /* and folded back (needs a workspace)              */
   int32_t schedule;        /* 0: library choice; 1: one workgroup per item;     */
-                           /* 2: persistent workgroups claiming items from a   */
-                           /* work queue in the workspace                      */
+                           /* 2: persistent workgroups claiming items from     */
+                           /* work queues in the workspace                     */
   int32_t pool_layout;     /* da_pool_layout of the K / V pools (and fp8 scale  */
                            /* arrays); read by every call that takes them      */
   int32_t fuse;            /* read by da_attention* only: 0 library choice;    */
@@ -140,10 +140,10 @@ typedef struct da_shape {
  *                scaled score.  An empty split (no kept token) is written as
  *                MA = 0, m = -inf, e = 0.
  * Workspace (device, caller-owned, 16-byte aligned, contents irrelevant):
- *   da_micro_attention_workspace_size() bytes.  It holds a work-queue
- *   counter (reset on `stream` by the call itself) used when the grid of
- *   (request, KV head, split) items is far larger than the GPU can hold at
- *   once, and the partials of page-range chunks that every split is cut
+ *   da_micro_attention_workspace_size() bytes.  It holds work-queue
+ *   counters (512 bytes, reset on `stream` by the call itself) used when
+ *   the grid of (request, KV head, split) items is far larger than the GPU
+ *   can hold at once, and the partials of page-range chunks that every split is cut
  *   into and folded back afterwards: with sh->chunks == 0, when there are
  *   fewer items than the GPU runs at once, or when splits are long (4 MiB
  *   of K and V or more) and cutting them balances the launch.
@@ -305,7 +305,7 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
  *              after using the buffer for anything else, or before a call
  *              whose S * Hkv exceeds every earlier one (the new counters
  *              then cover bytes that held partials).  The rest holds the
- *              partials and a work-queue counter.  Concurrent calls must not
+ *              partials and the work-queue counters.  Concurrent calls must not
  *              share a workspace.  A workspace too small is
  *              DA_ERR_INVALID_ARG (with sh->chunks == 0 the call first falls
  *              back to unchunked splits if those fit).

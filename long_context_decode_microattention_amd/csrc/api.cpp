@@ -137,8 +137,8 @@ int piece_pages(const da_shape* sh, int chunks) {
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Workspace layout: the work-queue counter of the persistent launch
-// (16 bytes), then, when splits are cut into chunks, chunk MA
+// Workspace layout: the work-queue counters of the persistent launch
+// (da::kQueueBytes), then, when splits are cut into chunks, chunk MA
 // [n, chunks, D] and chunk m and e [n, chunks], n = S * Hq * max_splits,
 // each part 16-byte aligned.
 struct WsLayout {
@@ -146,10 +146,11 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const da_shape* sh, int chunks) {
-  WsLayout w{0, 16, 16, 16, 16};
+  constexpr size_t Q = da::kQueueBytes;
+  WsLayout w{0, Q, Q, Q, Q};
   if (chunks <= 1) return w;
   const size_t n = (size_t)sh->S * sh->Hq * sh->max_splits * chunks;
-  w.ma = 16;
+  w.ma = Q;
   w.m = w.ma + align16(n * sh->D * sizeof(float));
   w.e = w.m + align16(n * sizeof(float));
   w.total = w.e + align16(n * sizeof(float));
@@ -158,13 +159,13 @@ WsLayout ws_layout(const da_shape* sh, int chunks) {
 
 // Workspace of the fused entry points: the group counters [S * Hkv] int32
 // first (zero before the first call, left zero by every call), the work-queue
-// counter, then the partials MA [n, D], m [n], e [n] with
+// counters, then the partials MA [n, D], m [n], e [n] with
 // n = S * Hq * max_splits * chunks, each part 16-byte aligned.
 WsLayout ws_fused_layout(const da_shape* sh, int chunks, size_t* counters) {
   *counters = align16((size_t)sh->S * sh->Hkv * sizeof(int32_t));
   WsLayout w{};
   w.queue = *counters;
-  w.ma = w.queue + 16;
+  w.ma = w.queue + da::kQueueBytes;
   const size_t n = (size_t)sh->S * sh->Hq * sh->max_splits * chunks;
   w.m = w.ma + align16(n * sh->D * sizeof(float));
   w.e = w.m + align16(n * sizeof(float));
@@ -301,7 +302,6 @@ da_status micro_attention_impl(const da_shape* sh, const void* q, const void* k_
   p.chunks = chunks;
   p.piece_pages = piece_pages(sh, chunks);
   p.n_items = sh->S * sh->Hkv * sh->max_splits * chunks;
-  p.grab = 1;
   p.schedule = sh->schedule;
   p.queue = persistent ? reinterpret_cast<int*>(wsb + ws.queue) : nullptr;
   p.S = sh->S;

@@ -27,13 +27,14 @@ struct MicroParams {
   float scale;
   long long NP;     // pages in the pools
   int head_major;   // 0: pools [NP, Hkv, P, D] (scales [NP, Hkv, P]); 1: [Hkv, NP, P, D] ([Hkv, NP, P])
-  // Persistent launch: `queue` is a device counter that is zero when the
-  // kernel starts; each workgroup claims `grab` consecutive items at a time
-  // until all n_items = S*Hkv*max_splits*chunks are taken.  queue == null:
-  // one workgroup per item (grid = n_items).
+  // Persistent launch: `queue` holds kQueues counters, kQueueStride ints
+  // apart, all zero when the kernel starts (kQueueBytes of workspace);
+  // counter q hands out, one at a time, the items of the splits j with
+  // j % kQueues == q, and a workgroup takes from the queue of its own XCD
+  // first (for_each_item) until all n_items = S*Hkv*max_splits*chunks are
+  // taken.  queue == null: one workgroup per item (grid = n_items).
   int* queue;
   int n_items;
-  int grab;
   int schedule;  // 0: launcher's choice, 1: one workgroup per item, 2: persistent
   // Fused merge: group_count [S * Hkv] counters, zero when the kernel starts
   // and left zero by it; the item completing the last partial of its
@@ -58,6 +59,11 @@ bool micro_mfma_supported(int dtype, int D, int G);  // the GQA matrix-core kern
 // cMA [n, chunks, D], cm/ce [n, chunks] -> MA [n, D], m/e [n], n = S*Hq*max_splits.
 // Zeroes the persistent-launch counter (a one-lane kernel, not a memset, so
 // it can be captured in a graph).
+// The persistent launch's work queues: one counter per XCD, each in its own
+// 64-byte line.
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 16;  // ints
+constexpr size_t kQueueBytes = (size_t)kQueues * kQueueStride * sizeof(int);
 hipError_t launch_queue_reset(int* queue, hipStream_t stream);
 // Zeroes n ints with a fill kernel (capturable in a graph, unlike a memset node).
 hipError_t launch_zero_ints(int* p, long long n, hipStream_t stream);

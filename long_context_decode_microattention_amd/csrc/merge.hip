@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const float* __restrict_
 }
 
 __global__ void queue_reset_kernel(int* queue) {
-  if (threadIdx.x == 0) *queue = 0;
+  if (threadIdx.x < kQueues) queue[threadIdx.x * kQueueStride] = 0;
 }
 
 __global__ __launch_bounds__(256) void zero_ints_kernel(int* p, long long n) {

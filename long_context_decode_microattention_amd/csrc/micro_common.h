@@ -122,13 +122,31 @@ struct FusedArgs {
 };
 static __shared__ FusedArgs s_fused;
 
+// Item number of the k-th item of work queue q: queue q holds the splits j
+// with j % kQueues == q, ordered (piece, request, split, KV head) with the KV
+// head fastest, so that the workgroups of one XCD read the tiles of all KV
+// heads of one page range close together in time (a page-major pool keeps
+// a page's heads side by side).  Items are numbered as in plan_item.
+__device__ __forceinline__ int queue_item(const MicroParams& p, int q, int nj, int k) {
+  const int kvh = k % p.Hkv;
+  int r = k / p.Hkv;
+  const int jj = r % nj;
+  r /= nj;
+  const int s = r % p.S;
+  const int c = r / p.S;
+  return (c * p.S + s) * p.Hkv * p.max_splits + kvh * p.max_splits + q + kQueues * jj;
+}
+
 // Runs body(x) for every work item x this workgroup owns (kFused: the
-// kernel instance with the fused merge): item blockIdx.x
-// for a one-per-item launch, or, for a persistent launch, items claimed from
-// p.queue `grab` at a time in increasing order until none are left.  The
-// next claim is issued before the current items are processed, so its
-// latency is hidden.  body may use LDS and barriers; every lane calls it with
-// the same x.
+// kernel instance with the fused merge): item blockIdx.x for a one-per-item
+// launch, or, for a persistent launch, items claimed one at a time from the
+// work queues of p.queue.  The dispatcher places workgroup b on XCD
+// b % kQueues, so a workgroup drains queue b % kQueues first (its XCD's
+// share: each XCD then serves the same splits of every KV head, as a
+// one-per-item launch of those shapes does), then the other queues in turn.
+// The next claim is issued before the current item is processed, so its
+// latency is hidden.  body may use LDS and barriers; every lane calls it
+// with the same x.
 template <bool kFused, class Body>
 __device__ __forceinline__ void for_each_item(const MicroParams& p, int* s_claim, Body&& body) {
   if constexpr (kFused) {
@@ -139,20 +157,32 @@ __device__ __forceinline__ void for_each_item(const MicroParams& p, int* s_claim
     return;
   }
   const int tid = threadIdx.x;
-  if (tid == 0) *s_claim = atomicAdd(p.queue, p.grab);
+  const int home = (int)(blockIdx.x % kQueues);
+  const int per_split_set = p.chunks * p.S * p.Hkv;  // items per split index
+  int qi = 0, q = home;
+  auto splits_of = [&](int qq) { return qq < p.max_splits ? (p.max_splits - 1 - qq) / kQueues + 1 : 0; };
+  int nj = splits_of(q);
+  if (tid == 0) *s_claim = atomicAdd(p.queue + q * kQueueStride, 1);
   __syncthreads();
-  int x0 = __builtin_amdgcn_readfirstlane(*s_claim);
-  while (x0 >= 0 && x0 < p.n_items) {  // a counter not reset to 0 ends the loop
-    int next = 0;
-    if (tid == 0) next = atomicAdd(p.queue, p.grab);
-    const int x1 = min(x0 + p.grab, p.n_items);
-    for (int x = x0; x < x1; ++x) {
-      body(x);
-      __syncthreads();  // the item's LDS (page list, combine) is free again
+  int k = __builtin_amdgcn_readfirstlane(*s_claim);
+  for (;;) {
+    // a drained queue (or a counter not reset to 0): the next queue
+    while (k < 0 || k >= per_split_set * nj) {
+      if (++qi == kQueues) return;
+      q = (home + qi) % kQueues;
+      nj = splits_of(q);
+      __syncthreads();  // every lane has read s_claim
+      if (tid == 0) *s_claim = atomicAdd(p.queue + q * kQueueStride, 1);
+      __syncthreads();
+      k = __builtin_amdgcn_readfirstlane(*s_claim);
     }
+    int next = 0;
+    if (tid == 0) next = atomicAdd(p.queue + q * kQueueStride, 1);
+    body(queue_item(p, q, nj, k));
+    __syncthreads();  // the item's LDS (page list, combine) is free again
     if (tid == 0) *s_claim = next;
     __syncthreads();
-    x0 = __builtin_amdgcn_readfirstlane(*s_claim);
+    k = __builtin_amdgcn_readfirstlane(*s_claim);
   }
 }
 
@@ -536,11 +566,6 @@ hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipS
       const hipError_t err = launch_queue_reset(p.queue, stream);
       if (err != hipSuccess) return err;
       grid = slots;
-      // One item per claim: with the next claim issued before the current
-      // item runs, the counter's latency is hidden, and single claims balance
-      // the tail best (larger claims measured 3-7% slower on the
-      // log-uniform batch, equal on the rest).
-      p.grab = 1;
     } else {
       p.queue = nullptr;
     }

@@ -90,7 +90,7 @@ int main(void) {
   s = good();
   expect("null q", micro(&s, NULL, NULL, 0), DA_ERR_INVALID_ARG);
   expect("misaligned q", micro(&s, (char*)FAKE + 2, NULL, 0), DA_ERR_INVALID_ARG);
-  expect("misaligned workspace", micro(&s, FAKE, (char*)FAKE + 4, 64), DA_ERR_INVALID_ARG);
+  expect("misaligned workspace", micro(&s, FAKE, (char*)FAKE + 4, 4096), DA_ERR_INVALID_ARG);
   s = good(); s.D = 96;
   expect("D unsupported", micro(&s, FAKE, NULL, 0), DA_ERR_UNSUPPORTED);
   s = good(); s.P = 48;

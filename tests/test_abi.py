@@ -65,7 +65,7 @@ def call_micro(lib, sh, **ptrs):
     (dict(shape=dict(chunks=65)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(chunks=4)), _lib.DA_ERR_INVALID_ARG),  # forced chunks, no workspace
     (dict(shape=dict(chunks=4), ptrs=dict(ws=FAKE, ws_bytes=16)), _lib.DA_ERR_INVALID_ARG),
-    (dict(ptrs=dict(ws=FAKE + 4, ws_bytes=64)), _lib.DA_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(ptrs=dict(ws=FAKE + 4, ws_bytes=4096)), _lib.DA_ERR_INVALID_ARG),  # misaligned workspace
     (dict(shape=dict(schedule=3)), _lib.DA_ERR_INVALID_ARG),
     (dict(shape=dict(schedule=2)), _lib.DA_ERR_INVALID_ARG),  # persistent, no workspace
     (dict(shape=dict(D=96)), _lib.DA_ERR_UNSUPPORTED),
@@ -155,16 +155,16 @@ def test_workspace_size(lib):
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
     chunks = 2  # 128 items -> 2048 / 128 = 16 chunks (capped at 16)
     assert n.value > 0
-    # many items: no chunks; only the 16-byte work-queue counter
+    # many items: no chunks; only the work-queue counters (8 x 64 bytes)
     sh = good_shape(S=64, Hq=40, Hkv=40, max_pages=2048, max_splits=16, P=16)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
-    assert n.value == 16
+    assert n.value == 512
     # forced chunks: the counter and the three chunk arrays, 16-byte aligned each
     sh = good_shape(S=2, Hq=8, Hkv=2, D=128, max_splits=3, chunks=5)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), ctypes.byref(n)) == _lib.DA_OK
     rows = 2 * 8 * 3 * 5
     align = lambda x: (x + 15) // 16 * 16
-    assert n.value == 16 + align(rows * 128 * 4) + 2 * align(rows * 4)
+    assert n.value == 512 + align(rows * 128 * 4) + 2 * align(rows * 4)
     assert lib.da_micro_attention_workspace_size(ctypes.byref(sh), None) == _lib.DA_ERR_INVALID_ARG
     del chunks
 

@@ -90,6 +90,25 @@ def test_persistent_schedule_parity(cfg, chunks):
                      f"{cfg} persistent partials")
 
 
+@pytest.mark.parametrize("chunks", [0, 3])
+@pytest.mark.parametrize("cfg,splits", [("C2", ("equal", 5)), ("C2", ("equal", 13)),
+                                        ("C3", ("chunk", 3000)), ("C1", ("equal", 1))])
+def test_persistent_queues_any_split_count(cfg, splits, chunks):
+    """The persistent launch's per-XCD queues split the items by split index
+    modulo 8: split counts that leave queues empty or uneven (1, 5, 11, 13
+    splits) still hand out every item exactly once."""
+    spec = REDUCED[cfg].replace(splits=splits)
+    announce("persistent queues", cfg, splits, chunks)
+    b = wl.build(spec, 12, DEV)
+    out, MA, m, e = run_gpu(b, chunks=chunks, schedule=2)
+    inp = host_inputs(b)
+    tol = TOL_OUT[spec.dtype]
+    compare_out(out.cpu().numpy(), oracle_out(inp, b.scale), tol, f"{cfg} {splits} persistent")
+    oMA, om, oe = oracle_micro(inp, b.scale)
+    compare_partials(MA.cpu().numpy(), m.cpu().numpy(), e.cpu().numpy(), oMA, om, oe, tol,
+                     f"{cfg} {splits} persistent partials")
+
+
 @pytest.mark.parametrize("cfg", sorted(REDUCED))
 def test_one_workgroup_per_item_parity(cfg):
     """Without a workspace the launch is one workgroup per item (no work
