@@ -109,8 +109,11 @@ CONFIGS = {
 # Pool layout each full-size workload is measured with: head-major pools
 # read 2.7% faster on the GQA block-sparse workload (its dense heads stream
 # contiguous runs and its masked heads read ascending tiles of one head's
-# run) and equally fast on the 1M-token one.
-PREFERRED_LAYOUT = {"C5": "head"}
+# run) and 0.7% faster on the 1M-token one (2426 against 2443 us in one
+# process), where each split then reads one contiguous run instead of
+# 16 KiB tiles 512 KiB apart; on the 16-token-page batches (a random
+# table) the two layouts measured equal.
+PREFERRED_LAYOUT = {"C5": "head", "C4": "head"}
 
 
 @dataclass
