@@ -506,8 +506,8 @@ constexpr long long kPersistentFactor = 8;
 // than the resident slots (many small or empty items, as in ragged batches)
 // and p.queue provides a counter, the in-order, XCD-round-robin dispatch
 // itself becomes the bottleneck; then the launch is persistent: one
-// workgroup per resident slot, each claiming items from the counter in
-// batches small enough that the tail stays short.
+// workgroup per resident slot, each claiming items one at a time from the
+// per-XCD work queues (for_each_item).
 template <class Kernel>
 hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipStream_t stream);
 
@@ -518,11 +518,14 @@ hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipS
 // head) -- the same aggregation rule, associative, so the pieces need no
 // separate combine.  The fused merge saves a launch and the partials' round
 // trip but makes every item count its group up, and the group's last item
-// merge alone; measured (HIP-graph replays) it wins where the grid is one
-// round of workgroups, on the persistent work queue (many short items), and
-// for grouped query heads with few partials per group, and loses on long
-// grids of short single-head items (C2: 190 vs 171 us) and on groups of
-// hundreds of partials.  fuse = 1 or 2 forces a form.
+// merge alone.  Measured with both forms timed in one process, it wins
+// where the grid is one round of workgroups (C1: 23.4 against 24.1 us) and
+// on the persistent work queue (C3: 908 against 917 us), and loses on long
+// grids of short single-head items (C2: 194 against 169 us) and on the
+// grouped-query batch (C5: 1614 against 1584 us over bf16 pages, 876
+// against 859 over 8-bit, 513 against 500 over 4-bit), where the merge's
+// tail on the last item of each group outweighs the saved launch.
+// fuse = 1 or 2 forces a form.
 template <int D, class KPlain, class KFused>
 hipError_t launch_micro_step(KPlain plain, KFused fused, int wg_per_cu, MicroParams p,
                              hipStream_t stream) {
@@ -534,8 +537,7 @@ hipError_t launch_micro_step(KPlain plain, KFused fused, int wg_per_cu, MicroPar
     const bool persistent = p.queue != nullptr && slots > 0 &&
                             (p.schedule == 2 ||
                              (p.schedule == 0 && p.n_items > kPersistentFactor * slots));
-    const long long per_group = (long long)p.max_splits * p.chunks;
-    one = persistent || p.n_items <= slots || (p.Hq > p.Hkv && per_group <= 128);
+    one = persistent || p.n_items <= slots;
     // a fused instance that spills registers (the merge's code on top of the
     // largest slab loops: 4-bit pages with 64-token slabs, G = 8) runs its
     // slab loop through scratch memory; measured on the GQA batch over 4-bit
