@@ -386,14 +386,39 @@ __global__ __launch_bounds__(kMicroThreads) void micro_kernel(MicroParams p) {
   });
 }
 
-// Resident workgroups per CU (0: as many as registers allow).  A cap of two
-// measured 15% slower on 16-token 8-bit pages and no faster on C4.
-constexpr int kValuWorkgroupsPerCU = 0;
+// Pieces of at least this many bytes of K and V run one workgroup per CU.
+constexpr long long kLongPieceBytes = 4LL << 20;
 
+// Resident workgroups per CU, chosen per launch (0: as many as registers
+// allow, three for the bf16 instances).  Fewer, deeper streams read HBM
+// faster once a CU's workgroups need not hide each other's per-item fixed
+// cost: one per CU for long pieces of bf16, fp32 or 8-bit rows (C4: 2390
+// against 2435 us, over 8-bit pages 1229 against 1256), two on the
+// persistent work queues (C3: 887-896 against 904-911 us), as many as fit
+// for short pieces (C2: 165 us, 197 with one per CU) and for 4-bit rows,
+// whose arithmetic per byte one workgroup per CU cannot cover (C4 over
+// 4-bit pages: 741 us with one, 668 with three).  The schedule is settled
+// first, with the uncapped slots, so the cap does not move a launch between
+// the two schedules.
 template <int DT, int D, int G, int SL = kSlab>
-hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
-  return launch_micro_step<D>(micro_kernel<DT, D, G, SL, false>, micro_kernel<DT, D, G, SL, true>,
-                              kValuWorkgroupsPerCU, p, stream);
+hipError_t launch_one(const MicroParams& p0, hipStream_t stream) {
+  using L = Layout<DT, D, SL>;
+  const auto plain = micro_kernel<DT, D, G, SL, false>;
+  MicroParams p = p0;
+  int cap = 0;
+  const int slots = resident_slots(reinterpret_cast<const void*>(plain), 0);
+  const bool persistent = p.queue != nullptr && slots > 0 &&
+                          (p.schedule == 2 ||
+                           (p.schedule == 0 && p.n_items > kPersistentFactor * slots));
+  if (persistent) {
+    cap = 2;
+    p.schedule = 2;
+  } else {
+    const long long row = 2LL * L::TOKB + (DT >= 2 ? 8 : 0);  // K and V (and their scales)
+    if (DT <= 2 && (long long)p.piece_pages * p.P * row >= kLongPieceBytes) cap = 1;
+    if (p.schedule == 0) p.schedule = 1;
+  }
+  return launch_micro_step<D>(plain, micro_kernel<DT, D, G, SL, true>, cap, p, stream);
 }
 
 template <int DT, int D>
