@@ -285,11 +285,10 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
  * KV head) instead of by a second kernel.  sh->fuse picks the form: 1 that
  * one launch; 2 two launches (the partials of every piece into the
  * workspace, then the merge kernel over them); 0 the library's choice per
- * shape: one launch when the grid is one round of workgroups or when it
- * runs persistently on the work queues, two launches otherwise (the shapes
- * where each was measured faster); also two when the one-launch kernel
- * instance would spill registers.  Either form gives the same result within
- * fp32 rounding.
+ * shape: one launch when the grid is one round of workgroups, two launches
+ * otherwise (the shapes where each was measured faster); also two when the
+ * one-launch kernel instance would spill registers.  Either form gives the
+ * same result within fp32 rounding.
  *
  *   Inputs as for da_micro_attention (da_attention_fp8: as for
  *   da_micro_attention_fp8).

@@ -519,9 +519,9 @@ hipError_t launch_micro_kernel(Kernel kernel, int wg_per_cu, MicroParams p, hipS
 // separate combine.  The fused merge saves a launch and the partials' round
 // trip but makes every item count its group up, and the group's last item
 // merge alone.  Measured with both forms timed in one process, it wins
-// where the grid is one round of workgroups (C1: 23.4 against 24.1 us) and
-// on the persistent work queue (C3: 908 against 917 us), and loses on long
-// grids of short single-head items (C2: 194 against 169 us) and on the
+// where the grid is one round of workgroups (C1: 20.8 against 24.4 us) and
+// loses on long grids of short single-head items (C2: 193 against 170 us),
+// on the persistent work queues (C3: 913 against 901 us) and on the
 // grouped-query batch (C5: 1614 against 1584 us over bf16 pages, 876
 // against 859 over 8-bit, 513 against 500 over 4-bit), where the merge's
 // tail on the last item of each group outweighs the saved launch.
@@ -534,10 +534,7 @@ hipError_t launch_micro_step(KPlain plain, KFused fused, int wg_per_cu, MicroPar
   if (p.fuse == 0) {
     const void* fn = reinterpret_cast<const void*>(plain);
     const int slots = resident_slots(fn, occupancy_lds(fn, wg_per_cu));
-    const bool persistent = p.queue != nullptr && slots > 0 &&
-                            (p.schedule == 2 ||
-                             (p.schedule == 0 && p.n_items > kPersistentFactor * slots));
-    one = persistent || p.n_items <= slots;
+    one = p.n_items <= slots;
     // a fused instance that spills registers (the merge's code on top of the
     // largest slab loops: 4-bit pages with 64-token slabs, G = 8) runs its
     // slab loop through scratch memory; measured on the GQA batch over 4-bit
