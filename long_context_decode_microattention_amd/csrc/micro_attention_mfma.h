@@ -85,8 +85,9 @@ struct MFrag {
   uint4 v[DT == 1 ? L::NI : 1];   // bf16 values
   uint2 v8[DT == 2 ? L::NI : 1];  // fp8 values
   uint32_t v4[DT == 3 ? L::NI : 1];  // fp4 values
-  float ksc[L::NG];               // quantized pages: K scale of token 16*g + col
-  float vsc[L::NG];               // quantized pages: V scale of token 16*g + col
+  float ksc[L::NG];               // quantized pages: K scale of token 16*g + col (packed
+                                  // softmax: ksc[0] holds token `lane`'s)
+  float vsc[L::NG];               // quantized pages: V scale, likewise
 };
 
 // Eight E2M1 codes (one word) -> eight bf16 values (four words), exactly.
@@ -275,6 +276,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
   static_assert(G == 2 || G == 4 || G == 8, "group size");
   constexpr bool kDense = kDenseValues<DT, D>;
+  // softmax on the scores packed one token per lane (at most 4 heads, 2 or 4
+  // score groups per slab)
+  constexpr bool kPacked = kDense && G <= 4 && L::NG >= 2;
   constexpr int KB = SL < 32 ? SL : 32;  // tokens per dense value block
   __shared__ int s_phys[kPageCap];
   __shared__ int s_lp[kPageCap];
@@ -315,7 +319,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
     }
 
     float m_h[G];        // running raw-dot maximum per head (wave-uniform)
-    float e_l[4];        // per-lane exp-sum of token column `col`, heads 4*grp + i
+    float e_l[4];        // per-lane exp-sums: token column `col`, heads 4*grp + i (packed:
+                         // token `lane` of each slab, head i)
     // value sums.  4x4 blocks: acc[hs][k] register i = head 4*hs + i, dim k
     // of the lane's 8.  Dense form: acc[0][e] = the 16 x 16 output tile of
     // dims 8n + e (column n = lane % 16); register i holds row 4*(lane/16) + i
@@ -352,6 +357,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       // fp8: the K and V scales of the key lane's token (no scales for bf16)
       const float* ksb = DT >= 2 ? p.ks + head_row + col : nullptr;
       const float* vsb = DT >= 2 ? p.vs + head_row + col : nullptr;
+      // packed softmax: lane l takes token l of the slab (the last one past SL)
+      const int tl = lane < SL ? lane : SL - 1;
+      const float* ksp = DT >= 2 ? p.ks + head_row + tl : nullptr;
+      const float* vsp = DT >= 2 ? p.vs + head_row + tl : nullptr;
 
       // resume point of the page scan: without a mask, ordinal = page - pa
       int rlp = it.mrow ? it.pa : it.pa + pc.o0;
@@ -397,10 +406,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                 for (int j = 0; j < L::KL; ++j)
                   f.k[g][j] = load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE);
               }
-              if constexpr (DT >= 2) {
+              if constexpr (DT >= 2 && !kPacked) {
                 f.ksc[g] = ksb[q.row + 16 * g];
                 f.vsc[g] = vsb[q.row + 16 * g];
               }
+            }
+            if constexpr (kPacked) {  // the scales of token `lane` of the slab
+              f.ksc[0] = ksp[q.row];
+              f.vsc[0] = vsp[q.row];
             }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
@@ -430,10 +443,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                   f.k[g][j] = kok ? load_stream16(kbase + off + g * 16 * L::TOKB + j * KSTRIDE)
                                   : make_uint4(0, 0, 0, 0);
               }
-              if constexpr (DT >= 2) {
+              if constexpr (DT >= 2 && !kPacked) {
                 f.ksc[g] = kok ? ksb[q.row + 16 * g] : 0.f;
                 f.vsc[g] = kok ? vsb[q.row + 16 * g] : 0.f;
               }
+            }
+            if constexpr (kPacked) {
+              const int tk = q.tb + lane;
+              const bool kok = lane < SL && tk >= t0 && tk < t1;
+              f.ksc[0] = kok ? ksp[q.row] : 0.f;
+              f.vsc[0] = kok ? vsp[q.row] : 0.f;
             }
   #pragma unroll
             for (int i = 0; i < L::NI; ++i) {
@@ -476,83 +495,137 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
                                                              __builtin_bit_cast(bf16x8_t, kb), sc[g],
                                                              0, 0, 0);
             }
-            if constexpr (DT >= 2) sc[g] *= f.ksc[g];
-          }
-          if (!q.whole) {  // wave-uniform branch
-  #pragma unroll
-            for (int g = 0; g < L::NG; ++g) {
-              const int tk = q.tb + 16 * g + col;
-              const bool kvalid = tk >= t0 && tk < t1;
-  #pragma unroll
-              for (int i = 0; i < 4; ++i) sc[g][i] = kvalid ? sc[g][i] : neg_inf();
-            }
-          }
-
-          // slab maxima per head, then the running maxima (wave-uniform)
-          float rm[4];
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sc[0][i];
-  #pragma unroll
-            for (int g = 1; g < L::NG; ++g) x = fmaxf(x, sc[g][i]);
-            rm[i] = row_max16(x);
+            if constexpr (DT >= 2 && !kPacked) sc[g] *= f.ksc[g];
           }
           float alpha_h[G], nmc_h[G];
           bool moved = false;
+          float* sp = s_p[wave];
+          if constexpr (kPacked) {
+            // The score tile of group g holds heads 0..3 in lanes 0..15 (rows
+            // 4..15 of the A operand are empty); one lane shuffle per group
+            // and register gathers the groups so that lane l holds token l of
+            // the slab (group l / 16, column l % 16), register i head i.  The
+            // K scale, split mask, exponentials, exp-sums, V scale and the
+            // store for the value product then run once per token, every lane
+            // busy, instead of once per (group, row); the per-head maxima
+            // reduce over the whole wave.
+            float X[4];
   #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
-            const float mn = fmaxf(m_h[h], mx);
-            const float ms = mn != neg_inf() ? mn : 0.f;
-            alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
-            nmc_h[h] = -ms * c;
-            moved |= mn != m_h[h];
-            m_h[h] = mn;
-          }
-
-          // probabilities in the score layout (0 for rows scored -inf);
-          // exp-sums per token column
-          float pw[L::NG][4];
+            for (int i = 0; i < 4; ++i) {
+              // row k of lanes takes row 0 of group k's tile
+              float x = sc[0][i];
   #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int hi = (i < G) ? i : 0;
-            float nmc = nmc_h[hi], al = alpha_h[hi];
-            if constexpr (G > 4) {
-              if (grp == 1) {
-                nmc = nmc_h[4 + i];
-                al = alpha_h[4 + i];
+              for (int g = 1; g < L::NG; ++g) {
+                const float y = __shfl(sc[g][i], lane - 16 * g, kWave);
+                x = grp == g ? y : x;
+              }
+              X[i] = x;
+            }
+            const int t = lane;                          // the lane's token in the slab
+            const bool has_tok = L::NG == 4 || grp < 2;  // with two groups, lanes 32..63 hold none
+            // K and V scales of token t
+            const float ks = f.ksc[0], vs = f.vsc[0];
+            bool valid = has_tok;
+            if (!q.whole) valid = valid && q.tb + t >= t0 && q.tb + t < t1;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) X[i] = valid ? X[i] * ks : neg_inf();
+  #pragma unroll
+            for (int h = 0; h < G; ++h) {
+              // the rows' maxima combined across the rows
+              float r = row_max16(X[h]);
+              r = fmaxf(r, __shfl_xor(r, 16, kWave));
+              if constexpr (L::NG == 4) r = fmaxf(r, __shfl_xor(r, 32, kWave));
+              const float mx = __builtin_bit_cast(
+                  float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r)));
+              const float mn = fmaxf(m_h[h], mx);
+              const float ms = mn != neg_inf() ? mn : 0.f;
+              alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
+              nmc_h[h] = -ms * c;
+              moved |= mn != m_h[h];
+              m_h[h] = mn;
+            }
+            const int tb = t % KB;
+            const int slot = (t - tb) + (KB / 4) * (tb & 3) + (tb >> 2);
+  #pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float pv = fast_exp2(fmaf(X[h], c, nmc_h[h]));
+              e_l[h] = fmaf(e_l[h], alpha_h[h], pv);
+              if (has_tok) sp[h * SL + slot] = pv * vs;
+            }
+          } else {
+            if (!q.whole) {  // wave-uniform branch
+  #pragma unroll
+              for (int g = 0; g < L::NG; ++g) {
+                const int tk = q.tb + 16 * g + col;
+                const bool kvalid = tk >= t0 && tk < t1;
+  #pragma unroll
+                for (int i = 0; i < 4; ++i) sc[g][i] = kvalid ? sc[g][i] : neg_inf();
               }
             }
-            float sum = 0.f;
-  #pragma unroll
-            for (int g = 0; g < L::NG; ++g) {
-              pw[g][i] = fast_exp2(fmaf(sc[g][i], c, nmc));
-              sum += pw[g][i];
-            }
-            e_l[i] = fmaf(e_l[i], al, sum);
-          }
 
-          // probabilities to the value-product operand layout (per-wave LDS);
-          // over 8-bit pages each carries its token's V scale
-          float* sp = s_p[wave];
-          if (grp < HS) {
+            // slab maxima per head, then the running maxima (wave-uniform)
+            float rm[4];
   #pragma unroll
-            for (int g = 0; g < L::NG; ++g)
+            for (int i = 0; i < 4; ++i) {
+              float x = sc[0][i];
   #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (4 * grp + i < G) {
-                  const float pv = DT >= 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
-                  if constexpr (kDense) {
-                    // head-major, each value block's tokens ordered by
-                    // (token % 4, token / 4) so that a lane's operand is
-                    // contiguous
-                    const int t = 16 * g + col;
-                    const int tb = t % KB;
-                    sp[(4 * grp + i) * SL + (t - tb) + (KB / 4) * (tb & 3) + (tb >> 2)] = pv;
-                  } else {
-                    sp[(16 * g + col) * G + 4 * grp + i] = pv;
-                  }
+              for (int g = 1; g < L::NG; ++g) x = fmaxf(x, sc[g][i]);
+              rm[i] = row_max16(x);
+            }
+  #pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float mx = lane_value(rm[h & 3], 16 * (h >> 2));
+              const float mn = fmaxf(m_h[h], mx);
+              const float ms = mn != neg_inf() ? mn : 0.f;
+              alpha_h[h] = fast_exp2((m_h[h] - ms) * c);
+              nmc_h[h] = -ms * c;
+              moved |= mn != m_h[h];
+              m_h[h] = mn;
+            }
+
+            // probabilities in the score layout (0 for rows scored -inf);
+            // exp-sums per token column
+            float pw[L::NG][4];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int hi = (i < G) ? i : 0;
+              float nmc = nmc_h[hi], al = alpha_h[hi];
+              if constexpr (G > 4) {
+                if (grp == 1) {
+                  nmc = nmc_h[4 + i];
+                  al = alpha_h[4 + i];
                 }
+              }
+              float sum = 0.f;
+  #pragma unroll
+              for (int g = 0; g < L::NG; ++g) {
+                pw[g][i] = fast_exp2(fmaf(sc[g][i], c, nmc));
+                sum += pw[g][i];
+              }
+              e_l[i] = fmaf(e_l[i], al, sum);
+            }
+
+            // probabilities to the value-product operand layout (per-wave LDS);
+            // over 8-bit pages each carries its token's V scale
+            if (grp < HS) {
+  #pragma unroll
+              for (int g = 0; g < L::NG; ++g)
+  #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (4 * grp + i < G) {
+                    const float pv = DT >= 2 ? pw[g][i] * f.vsc[g] : pw[g][i];
+                    if constexpr (kDense) {
+                      // head-major, each value block's tokens ordered by
+                      // (token % 4, token / 4) so that a lane's operand is
+                      // contiguous
+                      const int t = 16 * g + col;
+                      const int tb = t % KB;
+                      sp[(4 * grp + i) * SL + (t - tb) + (KB / 4) * (tb & 3) + (tb >> 2)] = pv;
+                    } else {
+                      sp[(16 * g + col) * G + 4 * grp + i] = pv;
+                    }
+                  }
+            }
           }
 
           if (wave_any(moved)) {  // scalar branch: skipped, not masked
@@ -669,7 +742,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
       x = x + dpp<kDppQuadXor2>(x);
       x = x + dpp<kDppHalfMirror>(x);
       x = x + dpp<kDppRowMirror>(x);
-      we[h] = lane_value(x, 16 * (h >> 2));
+      if constexpr (kPacked) {  // one token per lane: every row holds part of the sum
+        we[h] = (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+      } else {
+        we[h] = lane_value(x, 16 * (h >> 2));
+      }
     }
     float accg[G][8];
     if constexpr (kDense) {
