@@ -503,8 +503,9 @@ da_status da_attention_noalloc(const da_shape* sh, const void* q, const void* k_
                                const int32_t* seq_lens, const int32_t* split_bounds,
                                const uint8_t* block_mask, float* out, hipStream_t stream);
 
-/* Message for the last non-OK status returned on the calling thread
- * (thread-local; never NULL; empty if none). */
+/* Message for the status of the calling thread's most recent da_* call that
+ * returns a da_status: empty when that call returned DA_OK (every such entry
+ * point clears it first).  Thread-local; never NULL. */
 const char* da_last_error(void);
 
 /*

@@ -340,6 +340,7 @@ da_status da_micro_attention(const da_shape* sh, const void* q, const void* k_pa
                              const int32_t* seq_lens, const int32_t* split_bounds,
                              const uint8_t* block_mask, float* MA, float* m, float* e,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   const da_status st = check_shape(sh);
   if (st != DA_OK) return st;
   return micro_attention_impl(sh, q, k_pages, v_pages, nullptr, nullptr, block_table, seq_lens,
@@ -383,6 +384,7 @@ da_status da_micro_attention_fp8(const da_shape* sh, const void* q, const uint8_
                                  const int32_t* seq_lens, const int32_t* split_bounds,
                                  const uint8_t* block_mask, float* MA, float* m, float* e,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   return quantized_step("da_micro_attention_fp8", DA_FP8_E4M3, sh, q, k_codes, k_scales, v_codes,
                         v_scales, block_table, seq_lens, split_bounds, block_mask, MA, m, e,
                         nullptr, workspace, workspace_bytes, stream);
@@ -394,12 +396,14 @@ da_status da_micro_attention_fp4(const da_shape* sh, const void* q, const uint8_
                                  const int32_t* seq_lens, const int32_t* split_bounds,
                                  const uint8_t* block_mask, float* MA, float* m, float* e,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   return quantized_step("da_micro_attention_fp4", DA_FP4_E2M1, sh, q, k_codes, k_scales, v_codes,
                         v_scales, block_table, seq_lens, split_bounds, block_mask, MA, m, e,
                         nullptr, workspace, workspace_bytes, stream);
 }
 
 da_status da_micro_attention_workspace_size(const da_shape* sh, size_t* bytes) {
+  g_last_error.clear();
   if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
   da_status st = check_shape(sh, true);
   if (st != DA_OK) return st;
@@ -413,6 +417,7 @@ da_status da_attention(const da_shape* sh, const void* q, const void* k_pages, c
                        const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* split_bounds, const uint8_t* block_mask, float* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   const da_status st = check_shape(sh);
   if (st != DA_OK) return st;
   if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -426,6 +431,7 @@ da_status da_attention_fp8(const da_shape* sh, const void* q, const uint8_t* k_c
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* split_bounds, const uint8_t* block_mask, float* out,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   return quantized_step("da_attention_fp8", DA_FP8_E4M3, sh, q, k_codes, k_scales, v_codes,
                         v_scales, block_table, seq_lens, split_bounds, block_mask, nullptr,
@@ -437,6 +443,7 @@ da_status da_attention_fp4(const da_shape* sh, const void* q, const uint8_t* k_c
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* split_bounds, const uint8_t* block_mask, float* out,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
   if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   return quantized_step("da_attention_fp4", DA_FP4_E2M1, sh, q, k_codes, k_scales, v_codes,
                         v_scales, block_table, seq_lens, split_bounds, block_mask, nullptr,
@@ -486,6 +493,7 @@ da_status da_attention_noalloc(const da_shape* sh, const void* q, const void* k_
                                const void* v_pages, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* split_bounds,
                                const uint8_t* block_mask, float* out, hipStream_t stream) {
+  g_last_error.clear();
   da_status st = check_shape(sh);
   if (st != DA_OK) return st;
   if (!out) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -514,6 +522,7 @@ da_status da_attention_noalloc(const da_shape* sh, const void* q, const void* k_
 }
 
 da_status da_attention_workspace_size(const da_shape* sh, size_t* bytes, size_t* counter_bytes) {
+  g_last_error.clear();
   if (bytes == nullptr) return fail(DA_ERR_INVALID_ARG, "bytes is NULL");
   da_status st = check_shape(sh, true);
   if (st != DA_OK) return st;
@@ -527,6 +536,7 @@ da_status da_attention_workspace_size(const da_shape* sh, size_t* bytes, size_t*
 
 da_status da_merge(const da_shape* sh, const float* MA, const float* m, const float* e,
                    float* out, hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hq < 1 || sh->D < 1 || sh->max_splits < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hq=%d D=%d max_splits=%d)", sh->S,
@@ -545,6 +555,7 @@ da_status da_merge(const da_shape* sh, const float* MA, const float* m, const fl
 da_status da_merge_partials(const da_shape* sh, const float* MA, const float* m, const float* e,
                             int32_t out_splits, int32_t out_slot, float* MA_out, float* m_out,
                             float* e_out, hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hq < 1 || sh->D < 1 || sh->max_splits < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hq=%d D=%d max_splits=%d)", sh->S,
@@ -569,6 +580,7 @@ da_status da_merge_partials(const da_shape* sh, const float* MA, const float* m,
 
 da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
                           const int32_t* seq_lens, int32_t* err, hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1");
@@ -586,6 +598,7 @@ da_status da_check_inputs(const da_shape* sh, const int32_t* block_table,
 da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* block_table,
                         const int32_t* seq_lens, int32_t logical, const uint8_t* select_heads,
                         void* stats, hipStream_t stream) {
+  g_last_error.clear();
   da_status st = check_selector(sh, logical);
   if (st != DA_OK) return st;
   if (!k_pages || !block_table || !seq_lens || !stats)
@@ -608,6 +621,7 @@ da_status da_page_stats(const da_shape* sh, const void* k_pages, const int32_t* 
 da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t logical,
                          const uint8_t* select_heads, float* scores, hipStream_t stream) {
+  g_last_error.clear();
   da_status st = check_selector(sh, logical);
   if (st != DA_OK) return st;
   if (!q || !stats || !block_table || !seq_lens || !scores)
@@ -631,6 +645,7 @@ da_status da_page_scores(const da_shape* sh, const void* q, const void* stats,
 da_status da_select_pages(const da_shape* sh, const float* scores, const int32_t* seq_lens,
                           int32_t budget, int32_t keep_first, int32_t keep_last, int32_t horizon,
                           const uint8_t* select_heads, uint8_t* block_mask, hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d)", sh->S,
@@ -665,6 +680,7 @@ da_status da_append_kv(const da_shape* sh, const void* k_new, const void* v_new,
                        const int32_t* block_table, const int32_t* seq_lens, void* k_pages,
                        void* v_pages, int32_t logical, const uint8_t* select_heads, void* stats,
                        hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hkv < 1 || sh->D < 1 || sh->P < 1 || sh->max_pages < 1 || sh->NP < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d D=%d P=%d max_pages=%d NP=%lld)",
@@ -776,6 +792,7 @@ da_status da_append_kv_fp8(const da_shape* sh, const void* k_new, const void* v_
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
                            float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
                            const uint8_t* select_heads, void* stats, hipStream_t stream) {
+  g_last_error.clear();
   return append_quantized(8, sh, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes,
                           v_scales, logical, select_heads, stats, stream);
 }
@@ -784,12 +801,14 @@ da_status da_append_kv_fp4(const da_shape* sh, const void* k_new, const void* v_
                            const int32_t* block_table, const int32_t* seq_lens, uint8_t* k_codes,
                            float* k_scales, uint8_t* v_codes, float* v_scales, int32_t logical,
                            const uint8_t* select_heads, void* stats, hipStream_t stream) {
+  g_last_error.clear();
   return append_quantized(4, sh, k_new, v_new, block_table, seq_lens, k_codes, k_scales, v_codes,
                           v_scales, logical, select_heads, stats, stream);
 }
 
 da_status da_split_bounds(const da_shape* sh, const uint8_t* block_mask, const int32_t* seq_lens,
                           int32_t horizon, int32_t* split_bounds, hipStream_t stream) {
+  g_last_error.clear();
   if (sh == nullptr) return fail(DA_ERR_INVALID_ARG, "shape is NULL");
   if (sh->S < 1 || sh->Hkv < 1 || sh->P < 1 || sh->max_pages < 1 || sh->max_splits < 1)
     return fail(DA_ERR_INVALID_ARG, "sizes must be >= 1 (S=%d Hkv=%d P=%d max_pages=%d max_splits=%d)",
@@ -848,17 +867,20 @@ extern "C" {
 
 da_status da_quantize_rows(int32_t dtype, int64_t rows, int32_t D, const void* x,
                            uint8_t* codes, float* scales, hipStream_t stream) {
+  g_last_error.clear();
   return quantize_rows_impl(8, dtype, rows, D, x, codes, scales, stream);
 }
 
 da_status da_quantize_rows_fp4(int32_t dtype, int64_t rows, int32_t D, const void* x,
                                uint8_t* codes, float* scales, hipStream_t stream) {
+  g_last_error.clear();
   return quantize_rows_impl(4, dtype, rows, D, x, codes, scales, stream);
 }
 
 const char* da_last_error(void) { return g_last_error.c_str(); }
 
 da_status da_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  g_last_error.clear();
   if (!src || !sink) return fail(DA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(src, 16) || bytes % 16 != 0 || bytes == 0)
     return fail(DA_ERR_INVALID_ARG, "src must be 16-byte aligned and bytes a positive multiple of 16");

@@ -360,6 +360,18 @@ def test_quantize_rows_rejects(lib, args, status):
     assert got == status, _lib.load().da_last_error()
 
 
+def test_last_error_is_cleared_by_a_successful_call(lib):
+    """da_last_error() describes the most recent call: a failure sets it, the
+    next call that returns DA_OK leaves it empty (host-side calls only)."""
+    lib.da_last_error.restype = ctypes.c_char_p
+    assert lib.da_quantize_rows(_lib.DA_BF16, -1, 128, _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                None) == _lib.DA_ERR_INVALID_ARG
+    assert len(lib.da_last_error()) > 0
+    assert lib.da_quantize_rows(_lib.DA_BF16, 0, 128, _vp(FAKE), _vp(FAKE), _vp(FAKE),
+                                None) == _lib.DA_OK
+    assert lib.da_last_error() == b""
+
+
 def test_quantize_rows_misaligned(lib):
     got = lib.da_quantize_rows(_lib.DA_BF16, 4, 128, _vp(FAKE + 8), _vp(FAKE), _vp(FAKE), None)
     assert got == _lib.DA_ERR_INVALID_ARG
