@@ -43,7 +43,11 @@
 // cycles on the matrix pipe.  An 8-bit slab is 32 tokens with pages of 32
 // tokens or more (G <= 4), two score groups of 16 under one running-max
 // update and one LDS round trip (8 KiB of K + V, like a bf16 slab); a 4-bit
-// slab is 64 tokens (four score groups) likewise.
+// slab is 64 tokens (four score groups) likewise.  With G <= 4 such a slab's
+// softmax runs on its scores packed one token per lane (lane shuffles gather
+// the groups, whose heads fill one row of lanes each), so the scales, mask,
+// exponentials and the probability store cost one pass per token; each lane
+// then loads its own token's K and V scales.
 //
 // The kernel template lives in this header; micro_attention_mfma.hip launches
 // the bf16 instances, micro_attention_mfma_fp8.hip the 8-bit ones and
@@ -690,11 +694,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         };
 
         constexpr int W = kMicroWaves;
-        if constexpr (DT == 1 || G == 8 || SL >= 32) {
-          // 8 KiB slabs (16 bf16 rows, 32 fp8 rows, 64 fp4 rows), 4 KiB slabs
-          // of 32 fp4 rows, and 16-row quantized slabs with G = 8 (whose
-          // accumulators leave no registers for a third fragment): one slab
-          // in flight while the other is computed
+        // Two slabs in flight while one is computed (three fragments taking
+        // turns) wherever the registers hold them: 16-token slabs and the
+        // plain instances' 32-token 8-bit slabs; one where they do not: G = 8
+        // (its accumulators), 4-bit 32- and 64-token slabs, and the bf16 and
+        // 32-token 8-bit slabs of the fused instances (the merge's code).
+        constexpr bool kTwoInFlight =
+            G != 8 && (SL == 16 ? (DT != 1 || !kFused) : (DT == 2 && SL == 32 && !kFused));
+        if constexpr (!kTwoInFlight) {
           MFrag<DT, D, SL> fa, fb;
           int sl = wave;
           if (sl < nslab) load(sl, fa);
@@ -708,9 +715,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
             sl += W;
           }
         } else {
-          // 16-row fp8 slabs (pages of 16 tokens) carry half the bytes, so two
-          // are kept in flight; the three fragments take turns (no register
-          // copies, which would have to wait for the loads in flight)
+          // the three fragments take turns (no register copies, which would
+          // have to wait for the loads in flight)
           MFrag<DT, D, SL> f0, f1, f2;
           int sl = wave;
           if (sl < nslab) load(sl, f0);
