@@ -20,7 +20,7 @@
 //            row, read out as wave-uniform values; the running maximum is
 //            per wave, so the value accumulators are rescaled only when a
 //            head's maximum rises (wave-uniform branch).
-//   values   (bf16 pages, and any page type at D = 64) on
+//   values   (bf16 pages with G <= 4, and any page type at D = 64) on
 //            v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4x4, K = 1): block
 //            b = l/4 takes A = p of heads 0..3 from lanes 4b..4b+3 and B = one
 //            value element from each of its 4 lanes, so the values are used
@@ -145,15 +145,18 @@ __device__ __forceinline__ float lane_value(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
 }
 
-// Value product of the quantized pages (D = 128) on the dense bf16 MFMA.
+// Value product at D = 128 on the dense bf16 MFMA: over quantized pages, and
+// over bf16 pages with G = 8 (whose 4x4x1 accumulators, 64 registers, left
+// too few for the slabs in flight).
 //
 // A lane's value loads already hold what a B operand wants: load i gives lane
 // l the 8 dims 8*(l%16) .. +7 of token 4i + l/16, so over a block of KB = 32
 // (or 16) tokens the lane holds, for each of its dims, KB/4 tokens.  Taking
 // column n = l%16 as dim 8n + e, v_mfma_f32_16x16x32_bf16 number e (e = 0..7)
 // sums the block for dims 8n + e: its B operand is element e of the lane's 8
-// loads, gathered into bf16 pairs (codes of two tokens side by side by a byte
-// or nibble permutation, then one exact widening each), and its A operand is
+// loads, gathered into bf16 pairs (bf16 values by a half-word permutation;
+// codes of two tokens side by side by a byte or nibble permutation, then one
+// exact widening each), and its A operand is
 // the probabilities of the same tokens, read from the per-wave LDS buffer
 // where they are stored head-major with each block's tokens ordered by
 // (token % 4, token / 4), so that a lane's KB/4 values are contiguous.
@@ -166,13 +169,13 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // matrix work: output row r accumulates head r % G, and the two rows of a
 // head are added once per item.  Per 32 tokens: 8 MFMA (128 busy cycles)
 // instead of 64 v_mfma_f32_4x4x1f32 (512).
-template <int DT, int D>
-inline constexpr bool kDenseValues = DT >= 2 && D == 128;
+template <int DT, int D, int G>
+inline constexpr bool kDenseValues = D == 128 && (DT >= 2 || G == 8);
 
 template <int DT, int D, int G, int SL>
 __device__ __forceinline__ void dense_values(const float* sp, const MFrag<DT, D, SL>& f,
                                              f32x4_t (&acc)[8]) {
-  static_assert(kDenseValues<DT, D>, "dense value product: quantized pages, D = 128");
+  static_assert(kDenseValues<DT, D, G>, "dense value product: D = 128, quantized pages or G = 8");
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
   constexpr int KB = SL < 32 ? SL : 32;  // tokens per block
   constexpr int KK = KB / 4;             // operand elements per lane
@@ -220,7 +223,24 @@ __device__ __forceinline__ void dense_values(const float* sp, const MFrag<DT, D,
                                                           0, 0, 0);
       }
     };
-    if constexpr (DT == 2) {
+    if constexpr (DT == 1) {
+      // element e of each bf16 load: half e % 2 of word e / 2; the two loads'
+      // halves side by side
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t bw[KW];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          const uint4& va = f.v[KK * b + 2 * j];
+          const uint4& vc = f.v[KK * b + 2 * j + 1];
+          const int w = e >> 1;
+          const uint32_t wa = w == 0 ? va.x : (w == 1 ? va.y : (w == 2 ? va.z : va.w));
+          const uint32_t wc = w == 0 ? vc.x : (w == 1 ? vc.y : (w == 2 ? vc.z : vc.w));
+          bw[j] = __builtin_amdgcn_perm(wc, wa, (e & 1) ? 0x07060302u : 0x05040100u);
+        }
+        mfma(e, bw);
+      }
+    } else if constexpr (DT == 2) {
       // word w of each load: bytes (a_q, c_q) side by side -> dims 4w + q
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
@@ -279,7 +299,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
   using L = MLayout<DT, D, SL>;
   constexpr int HS = (G + 3) / 4;  // groups of 4 heads (score rows / value head sets)
   static_assert(G == 2 || G == 4 || G == 8, "group size");
-  constexpr bool kDense = kDenseValues<DT, D>;
+  constexpr bool kDense = kDenseValues<DT, D, G>;
   // softmax on the scores packed one token per lane (at most 4 heads, 2 or 4
   // score groups per slab)
   constexpr bool kPacked = kDense && G <= 4 && L::NG >= 2;
@@ -695,12 +715,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
 
         constexpr int W = kMicroWaves;
         // Two slabs in flight while one is computed (three fragments taking
-        // turns) wherever the registers hold them: 16-token slabs and the
-        // plain instances' 32-token 8-bit slabs; one where they do not: G = 8
-        // (its accumulators), 4-bit 32- and 64-token slabs, and the bf16 and
-        // 32-token 8-bit slabs of the fused instances (the merge's code).
+        // turns) wherever the registers hold them: 16-token slabs (with G = 8
+        // only under the dense value product) and the plain instances'
+        // 32-token 8-bit slabs with G <= 4; one where they do not: 4-bit 32-
+        // and 64-token slabs, 8-bit 32-token slabs with G = 8, G = 8 at D = 64,
+        // and the bf16 and 32-token 8-bit slabs of the fused instances (the
+        // merge's code).
         constexpr bool kTwoInFlight =
-            G != 8 && (SL == 16 ? (DT != 1 || !kFused) : (DT == 2 && SL == 32 && !kFused));
+            (G != 8 || kDense) && (SL == 16 ? (DT != 1 || !kFused) : (DT == 2 && SL == 32 && G != 8 && !kFused));
         if constexpr (!kTwoInFlight) {
           MFrag<DT, D, SL> fa, fb;
           int sl = wave;
@@ -797,19 +819,27 @@ hipError_t launch_one(const MicroParams& p, hipStream_t stream) {
 
 // bf16 pages: 16-token slabs.  fp8 pages: 32-token slabs (two score groups
 // under one softmax update, 8 KiB of K + V like a bf16 slab) when the page
-// size allows and G <= 4; fp4 pages: 64-token slabs (four score groups, 8 KiB
-// at D = 128), else 32; otherwise 16-token slabs.
+// size allows (G = 8: at D = 128 only); fp4 pages: 64-token slabs (four score
+// groups, 8 KiB at D = 128), else 32 (G = 8: both at D = 128 only);
+// otherwise 16-token slabs.  G = 8 over 16-token quantized slabs measured 9%
+// (8-bit) and 33% (4-bit) slower on the grouped-query batch.
 template <int DT, int D>
 hipError_t dispatch_g(int G, const MicroParams& p, hipStream_t stream) {
   if constexpr (DT == 2) {
     if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
     if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
+    if constexpr (D == 128)
+      if (p.P % 32 == 0 && G == 8) return launch_one<DT, D, 8, 32>(p, stream);
   }
   if constexpr (DT == 3) {
     if (p.P % 64 == 0 && G == 2) return launch_one<DT, D, 2, 64>(p, stream);
     if (p.P % 64 == 0 && G == 4) return launch_one<DT, D, 4, 64>(p, stream);
+    if constexpr (D == 128)
+      if (p.P % 64 == 0 && G == 8) return launch_one<DT, D, 8, 64>(p, stream);
     if (p.P % 32 == 0 && G == 2) return launch_one<DT, D, 2, 32>(p, stream);
     if (p.P % 32 == 0 && G == 4) return launch_one<DT, D, 4, 32>(p, stream);
+    if constexpr (D == 128)
+      if (p.P % 32 == 0 && G == 8) return launch_one<DT, D, 8, 32>(p, stream);
   }
   switch (G) {
     case 2: return launch_one<DT, D, 2, 16>(p, stream);

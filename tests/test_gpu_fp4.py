@@ -92,6 +92,7 @@ CASES = {
     "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 32768)),
     "C5_G2_D64": wl.CONFIGS["C5"].replace(S=2, Hq=16, D=64, lens=("fixed", 8192 + 7)),
     "C5_G8": wl.CONFIGS["C5"].replace(S=1, Hq=64, lens=("fixed", 8192 + 50)),
+    "C5_G8_P32": wl.CONFIGS["C5"].replace(S=1, Hq=64, P=32, lens=("fixed", 8192 + 19)),
     "C5_P32": wl.CONFIGS["C5"].replace(S=2, P=32, lens=("fixed", 16384 + 13)),
     "C5_P16_G4": wl.CONFIGS["C5"].replace(S=2, P=16, lens=("fixed", 8192 + 5)),
     "C5_P128_G2": wl.CONFIGS["C5"].replace(S=2, Hq=16, P=128, lens=("fixed", 16384 + 77)),

@@ -87,6 +87,7 @@ CASES = {
     "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 32768)),
     "C5_G2_D64": wl.CONFIGS["C5"].replace(S=2, Hq=16, D=64, lens=("fixed", 8192 + 7)),
     "C5_G8": wl.CONFIGS["C5"].replace(S=1, Hq=64, lens=("fixed", 8192 + 50)),
+    "C5_G8_P32": wl.CONFIGS["C5"].replace(S=1, Hq=64, P=32, lens=("fixed", 8192 + 19)),
     # pages of 32 and 128 tokens (one and four 32-token slabs per page of the
     # grouped-query kernel), splits cut mid-slab, ragged last page
     "C5_P32": wl.CONFIGS["C5"].replace(S=2, P=32, lens=("fixed", 16384 + 13)),

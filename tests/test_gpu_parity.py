@@ -27,6 +27,8 @@ REDUCED = {
     "C3": wl.CONFIGS["C3"].replace(S=6, Hq=8, Hkv=8),
     "C4": wl.CONFIGS["C4"].replace(Hq=8, Hkv=8, lens=("fixed", 32768)),
     "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 32768)),
+    # eight query heads per KV head: the dense value product over bf16 pages
+    "C5_G8": wl.CONFIGS["C5"].replace(S=1, Hq=64, lens=("fixed", 16384 + 50)),
 }
 
 
