@@ -36,6 +36,8 @@ REDUCED = {
     "C3": wl.CONFIGS["C3"].replace(S=6, Hq=8, Hkv=8),
     "C4": wl.CONFIGS["C4"].replace(Hq=8, Hkv=8, lens=("fixed", 32768)),
     "C5": wl.CONFIGS["C5"].replace(S=2, lens=("fixed", 32768)),
+    # eight query heads per KV head (the dense value product over bf16 pages)
+    "C5_G8": wl.CONFIGS["C5"].replace(S=1, Hq=64, lens=("fixed", 16384 + 50)),
 }
 TOL_SAME = {wl.F32: 1e-6, wl.BF16: 1e-5}
 
@@ -199,7 +201,7 @@ def test_fused_masks_empty_requests_and_poison():
     assert torch.equal(out[0, 4:], torch.zeros_like(out[0, 4:])), "KV head 1 of request 0 is all masked"
 
 
-@pytest.mark.parametrize("cfg", ["C2", "C4", "C5"])
+@pytest.mark.parametrize("cfg", ["C2", "C4", "C5", "C5_G8"])
 def test_fused_fp8_pages(cfg):
     """8-bit pages: the fused step against the oracle over the dequantized
     pools and against da_micro_attention_fp8 + da_merge."""
