@@ -170,7 +170,7 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // head are added once per item.  Per 32 tokens: 8 MFMA (128 busy cycles)
 // instead of 64 v_mfma_f32_4x4x1f32 (512).
 template <int DT, int D, int G>
-inline constexpr bool kDenseValues = D == 128 && (DT >= 2 || G == 8);
+inline constexpr bool kDenseValues = D == 128 && (DT >= 2 || (DT == 1 && G == 8));
 
 template <int DT, int D, int G, int SL>
 __device__ __forceinline__ void dense_values(const float* sp, const MFrag<DT, D, SL>& f,
@@ -722,7 +722,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void micro_mfma_kernel(MicroParams p) {
         // and the bf16 and 32-token 8-bit slabs of the fused instances (the
         // merge's code).
         constexpr bool kTwoInFlight =
-            (G != 8 || kDense) && (SL == 16 ? (DT != 1 || !kFused) : (DT == 2 && SL == 32 && G != 8 && !kFused));
+            (G != 8 || kDense) &&
+            (SL == 16 ? (DT != 1 || !kFused) : (DT == 2 && SL == 32 && G != 8 && !kFused));
         if constexpr (!kTwoInFlight) {
           MFrag<DT, D, SL> fa, fb;
           int sl = wave;
