@@ -98,6 +98,12 @@ CASES = {
     "C5_P128_G2": wl.CONFIGS["C5"].replace(S=2, Hq=16, P=128, lens=("fixed", 16384 + 77)),
     "C4_G4_P32_mid": wl.CONFIGS["C4"].replace(Hq=8, Hkv=2, P=32, lens=("fixed", 8192 + 21),
                                                splits=("equal", 7)),
+    # 64-token pages with splits cut inside a slab (the packed softmax's
+    # partial slabs), four and eight query heads per KV head
+    "C4_G4_P64_mid": wl.CONFIGS["C4"].replace(Hq=8, Hkv=2, P=64, lens=("fixed", 8192 + 37),
+                                               splits=("equal", 7)),
+    "C4_G8_P64_mid": wl.CONFIGS["C4"].replace(Hq=16, Hkv=2, P=64, lens=("fixed", 8192 + 37),
+                                               splits=("equal", 7)),
 }
 
 

@@ -94,6 +94,12 @@ CASES = {
     "C5_P128_G2": wl.CONFIGS["C5"].replace(S=2, Hq=16, P=128, lens=("fixed", 16384 + 77)),
     "C4_G4_P32_mid": wl.CONFIGS["C4"].replace(Hq=8, Hkv=2, P=32, lens=("fixed", 8192 + 21),
                                                splits=("equal", 7)),
+    # 64-token pages with splits cut inside a slab (the packed softmax's
+    # partial slabs), four and eight query heads per KV head
+    "C4_G4_P64_mid": wl.CONFIGS["C4"].replace(Hq=8, Hkv=2, P=64, lens=("fixed", 8192 + 37),
+                                               splits=("equal", 7)),
+    "C4_G8_P64_mid": wl.CONFIGS["C4"].replace(Hq=16, Hkv=2, P=64, lens=("fixed", 8192 + 37),
+                                               splits=("equal", 7)),
     # the largest page size built: 256 tokens (8 slabs of 32 or 16 of 16 per page)
     "C4_P256": wl.CONFIGS["C4"].replace(Hq=4, Hkv=4, P=256, lens=("fixed", 256 * 20 + 77),
                                         splits=("equal", 5)),
